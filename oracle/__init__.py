@@ -1,0 +1,109 @@
+"""Oracle of the fused AdaLN (LayerNorm-Modulate) operator: a plain,
+double-precision CPU implementation written from the AdaptiveLoad technical
+summary pages (gist.science, arXiv 2605.17923), section "Methodology", parts
+A (dual-constraint bucket sizing) and B (fused LayerNorm-Modulate kernels).
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the benchmark's
+CPU-baseline leg may call it; the GPU path never imports it, and it imports
+nothing from the GPU path.  The arithmetic lives in ``adaln_oracle.c``; this
+module marshals arrays through ctypes.
+
+Every function is pinned by ``tests/test_oracle.py`` to facts that do not come
+from the oracle itself (a float64 library LayerNorm with autograd, central
+finite differences, closed forms, hand-evaluated bucket sizes).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import numpy as np
+
+from . import build as _build
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_build.LIB):
+        _build.build()
+    lib = ctypes.CDLL(_build.LIB)
+    i64, f64, vp = ctypes.c_int64, ctypes.c_double, ctypes.c_void_p
+    lib.oracle_bshape.argtypes = [i64, i64, i64, ctypes.c_int32]
+    lib.oracle_bshape.restype = i64
+    lib.oracle_fwd.argtypes = [vp, vp, vp, i64, i64, i64, f64, vp, vp, vp]
+    lib.oracle_fwd.restype = None
+    lib.oracle_bwd.argtypes = [vp, vp, vp, i64, i64, i64, f64, vp, vp, vp]
+    lib.oracle_bwd.restype = None
+    lib.oracle_num_threads.argtypes = []
+    lib.oracle_num_threads.restype = ctypes.c_int
+    lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
+    lib.oracle_set_num_threads.restype = None
+    _lib = lib
+    return lib
+
+
+def _f64(a) -> np.ndarray:
+    """Float64 C-contiguous numpy copy of a numpy array or torch tensor.
+
+    bfloat16, float32 and float64 values convert exactly."""
+    if hasattr(a, "detach"):  # torch tensor
+        import torch
+        a = a.detach().to("cpu", torch.float64).contiguous().numpy()
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data
+
+
+def bshape(S: int, m_mem: int, m_comp: int, p: int) -> int:
+    """max(1, min(M_mem // S, M_comp // S**p)); -1 on invalid arguments."""
+    return int(_load().oracle_bshape(int(S), int(m_mem), int(m_comp), int(p)))
+
+
+def fwd(x, scale, shift, eps: float = 1e-6, want_y: bool = True
+        ) -> Tuple[Optional[np.ndarray], np.ndarray, np.ndarray]:
+    """Forward of AdaLN in float64.
+
+    x: [B, N, D]; scale, shift: [B, D].  Returns (y [B,N,D] or None,
+    mean [B,N], rstd [B,N]) as float64 arrays."""
+    x, scale, shift = _f64(x), _f64(scale), _f64(shift)
+    B, N, D = x.shape
+    assert scale.shape == (B, D) and shift.shape == (B, D)
+    y = np.empty((B, N, D), np.float64) if want_y else None
+    mean = np.empty((B, N), np.float64)
+    rstd = np.empty((B, N), np.float64)
+    _load().oracle_fwd(_ptr(x), _ptr(scale), _ptr(shift), B, N, D,
+                       float(eps), _ptr(y), _ptr(mean), _ptr(rstd))
+    return y, mean, rstd
+
+
+def bwd(dy, x, scale, eps: float = 1e-6, want_dx: bool = True,
+        want_dmod: bool = True):
+    """Backward of AdaLN in float64.
+
+    Returns (dx [B,N,D] or None, dscale [B,D] or None, dshift [B,D] or None).
+    """
+    dy, x, scale = _f64(dy), _f64(x), _f64(scale)
+    B, N, D = x.shape
+    assert dy.shape == (B, N, D) and scale.shape == (B, D)
+    dx = np.empty((B, N, D), np.float64) if want_dx else None
+    dscale = np.empty((B, D), np.float64) if want_dmod else None
+    dshift = np.empty((B, D), np.float64) if want_dmod else None
+    _load().oracle_bwd(_ptr(dy), _ptr(x), _ptr(scale), B, N, D, float(eps),
+                       _ptr(dx), _ptr(dscale), _ptr(dshift))
+    return dx, dscale, dshift
+
+
+def num_threads() -> int:
+    return int(_load().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    _load().oracle_set_num_threads(int(n))
