@@ -1,0 +1,10 @@
+"""Fused AdaLN (LayerNorm-Modulate) forward and backward for AMD Instinct
+MI355X (gfx950), as hand-written HIP kernels behind a C ABI
+(include/adaln.h).  PyTorch supplies device memory and streams only."""
+
+from ._lib import AdalnError, BF16, F32, LIB_PATH, load
+from .ops import (bshape, bwd, bwd_dmod, bwd_dx, bwd_workspace_bytes, fwd,
+                  max_d)
+
+__all__ = ["AdalnError", "BF16", "F32", "LIB_PATH", "load", "bshape", "bwd",
+           "bwd_dmod", "bwd_dx", "bwd_workspace_bytes", "fwd", "max_d"]

@@ -1,0 +1,193 @@
+// Modulation gradients of the fused AdaLN operator through the D-tile
+// coalesced reduction (AdaptiveLoad technical summary, section 2.B, backward
+// pass): dscale[b,d] = sum_n dy * xhat and dshift[b,d] = sum_n dy.
+//
+// Reducing along N row by row would walk memory with a stride of D.  Instead
+// the grid is cut into (d_tile, n_tile) pieces (times the batch): each lane is
+// pinned to the 16 bytes of features it owns and accumulates down the token
+// rows of its n_tile, so every load of a wavefront covers 1 KiB of contiguous
+// memory.  The four wavefronts of a workgroup take interleaved rows of the
+// same n_tile and combine through LDS; each workgroup writes one float32
+// partial per feature, and a second kernel sums the partials of the n_tiles
+// in index order.  No floating-point atomics: the result is reproducible bit
+// for bit.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace adaln {
+
+constexpr int kRowsInFlight = 4;  // rows each wavefront loads before using
+
+template <typename T>
+__global__ __launch_bounds__(kBlock) void dmod_partial_kernel(
+    const T *__restrict__ dy, const T *__restrict__ x,
+    const float *__restrict__ mean, const float *__restrict__ rstd,
+    float *__restrict__ part_scale, float *__restrict__ part_shift,
+    int32_t N, int32_t D, int32_t d_tiles, int32_t n_tile, int32_t n_tiles,
+    int64_t total_tiles) {
+  constexpr int E = Elems<T>::value;
+  constexpr int U = kRowsInFlight;
+  constexpr int kWaves = kBlock / kWave;
+  __shared__ float stage[kWaves - 1][2 * E][kWave];
+  const int lane = lane_id();
+  const int wave = wave_id();
+  const int nvec = D / E;
+
+  for (int64_t tile = blockIdx.x; tile < total_tiles; tile += gridDim.x) {
+    const int dt = (int)(tile % d_tiles);
+    const int64_t rest = tile / d_tiles;
+    const int t = (int)(rest % n_tiles);
+    const int b = (int)(rest / n_tiles);
+    const int j = dt * kWave + lane;  // this lane's vector of the row
+    const bool ok = j < nvec;
+    const int n0 = t * n_tile;
+    const int n1 = min(N, n0 + n_tile);
+    const int64_t row0 = (int64_t)b * N;
+
+    float acc_s[E], acc_h[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc_s[e] = acc_h[e] = 0.f;
+
+    for (int n = n0 + wave; n < n1; n += kWaves * U) {
+      Vec xv[U], gv[U];
+      float mu[U], r[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int nn = n + u * kWaves;
+        const bool live = nn < n1;
+        const int64_t off = (row0 + (live ? nn : n0)) * D + (int64_t)j * E;
+        xv[u] = (live && ok) ? load_vec(x + off) : vzero();
+        gv[u] = (live && ok) ? load_vec(dy + off) : vzero();
+        mu[u] = live ? mean[row0 + nn] : 0.f;
+        r[u] = live ? rstd[row0 + nn] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const float g = elem<T>(gv[u], e);
+          const float xh = (elem<T>(xv[u], e) - mu[u]) * r[u];
+          acc_s[e] = fmaf(g, xh, acc_s[e]);
+          acc_h[e] += g;
+        }
+      }
+    }
+
+    if (wave > 0) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        stage[wave - 1][e][lane] = acc_s[e];
+        stage[wave - 1][E + e][lane] = acc_h[e];
+      }
+    }
+    __syncthreads();
+    if (wave == 0 && ok) {
+#pragma unroll
+      for (int w = 0; w < kWaves - 1; ++w) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          acc_s[e] += stage[w][e][lane];
+          acc_h[e] += stage[w][E + e][lane];
+        }
+      }
+      const int64_t po = ((int64_t)b * n_tiles + t) * D + (int64_t)j * E;
+#pragma unroll
+      for (int q = 0; q < E / 4; ++q) {
+        *reinterpret_cast<float4 *>(part_scale + po + 4 * q) =
+            make_float4(acc_s[4 * q], acc_s[4 * q + 1], acc_s[4 * q + 2],
+                        acc_s[4 * q + 3]);
+        *reinterpret_cast<float4 *>(part_shift + po + 4 * q) =
+            make_float4(acc_h[4 * q], acc_h[4 * q + 1], acc_h[4 * q + 2],
+                        acc_h[4 * q + 3]);
+      }
+    }
+    __syncthreads();  // `stage` is reused by the next tile
+  }
+}
+
+// dscale[b, d] = sum over t = 0 .. n_tiles-1 of part_scale[b, t, d] (and the
+// same for dshift).  Lane l of every wavefront owns 4 features; wavefront w
+// sums tiles w, w+4, w+8, ... in order, and the four wavefront sums are added
+// in wavefront order.  With n_tiles == 0 the outputs are zero.
+__global__ __launch_bounds__(kBlock) void dmod_finish_kernel(
+    const float *__restrict__ part_scale, const float *__restrict__ part_shift,
+    float *__restrict__ dscale, float *__restrict__ dshift, int32_t D,
+    int32_t n_tiles, int32_t col_blocks, int64_t total_blocks) {
+  constexpr int kWaves = kBlock / kWave;
+  __shared__ float4 stage[kWaves - 1][2][kWave];
+  const int lane = lane_id();
+  const int wave = wave_id();
+  const int ncol = D / 4;
+
+  for (int64_t blk = blockIdx.x; blk < total_blocks; blk += gridDim.x) {
+    const int cb = (int)(blk % col_blocks);
+    const int b = (int)(blk / col_blocks);
+    const int c = cb * kWave + lane;
+    const bool ok = c < ncol;
+    float4 as = make_float4(0.f, 0.f, 0.f, 0.f);
+    float4 ah = as;
+    if (ok) {
+      const float4 *ps = reinterpret_cast<const float4 *>(
+          part_scale + (int64_t)b * n_tiles * D) + c;
+      const float4 *ph = reinterpret_cast<const float4 *>(
+          part_shift + (int64_t)b * n_tiles * D) + c;
+#pragma unroll 4
+      for (int t = wave; t < n_tiles; t += kWaves) {
+        const float4 vs = ps[(int64_t)t * ncol];
+        const float4 vh = ph[(int64_t)t * ncol];
+        as.x += vs.x; as.y += vs.y; as.z += vs.z; as.w += vs.w;
+        ah.x += vh.x; ah.y += vh.y; ah.z += vh.z; ah.w += vh.w;
+      }
+    }
+    if (wave > 0) {
+      stage[wave - 1][0][lane] = as;
+      stage[wave - 1][1][lane] = ah;
+    }
+    __syncthreads();
+    if (wave == 0 && ok) {
+#pragma unroll
+      for (int w = 0; w < kWaves - 1; ++w) {
+        const float4 vs = stage[w][0][lane];
+        const float4 vh = stage[w][1][lane];
+        as.x += vs.x; as.y += vs.y; as.z += vs.z; as.w += vs.w;
+        ah.x += vh.x; ah.y += vh.y; ah.z += vh.z; ah.w += vh.w;
+      }
+      reinterpret_cast<float4 *>(dscale + (int64_t)b * D)[c] = as;
+      reinterpret_cast<float4 *>(dshift + (int64_t)b * D)[c] = ah;
+    }
+    __syncthreads();
+  }
+}
+
+
+hipError_t launch_dmod(int dtype, const DmodPlan &plan, const void *dy,
+                       const void *x, const float *mean, const float *rstd,
+                       float *part_scale, float *part_shift, float *dscale,
+                       float *dshift, int32_t B, int32_t N, int32_t D,
+                       hipStream_t stream) {
+  const int64_t total_tiles = (int64_t)plan.d_tiles * plan.n_tiles * B;
+  hipError_t e = hipSuccess;
+  if (total_tiles > 0) {
+    if (dtype == 1)
+      e = launch_kernel(dmod_partial_kernel<bf16>, total_tiles, stream,
+                        (const bf16 *)dy, (const bf16 *)x, mean, rstd,
+                        part_scale, part_shift, N, D, (int32_t)plan.d_tiles,
+                        (int32_t)plan.n_tile, (int32_t)plan.n_tiles,
+                        total_tiles);
+    else
+      e = launch_kernel(dmod_partial_kernel<float>, total_tiles, stream,
+                        (const float *)dy, (const float *)x, mean, rstd,
+                        part_scale, part_shift, N, D, (int32_t)plan.d_tiles,
+                        (int32_t)plan.n_tile, (int32_t)plan.n_tiles,
+                        total_tiles);
+    if (e != hipSuccess) return e;
+  }
+  const int32_t col_blocks = (D / 4 + kWave - 1) / kWave;
+  const int64_t total_blocks = (int64_t)col_blocks * B;
+  return launch_kernel(dmod_finish_kernel, total_blocks, stream,
+                       (const float *)part_scale, (const float *)part_shift,
+                       dscale, dshift, D, (int32_t)plan.n_tiles, col_blocks,
+                       total_blocks);
+}
+
+}  // namespace adaln

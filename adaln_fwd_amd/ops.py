@@ -1,0 +1,199 @@
+"""Python binding of the fused AdaLN C ABI for torch tensors.
+
+Argument marshalling only: shapes, dtypes, devices and contiguity are checked
+here because the C ABI cannot see torch metadata; every step of the operator
+runs in the HIP kernels of ``libadaln.so``.  Outputs that are not passed in
+are allocated with torch on the input's device; work is enqueued on the
+current torch stream of that device unless ``stream`` is given.
+"""
+
+from __future__ import annotations
+
+from typing import Optional, Tuple
+
+import torch
+
+from . import _lib
+
+_DTYPES = {torch.float32: _lib.F32, torch.bfloat16: _lib.BF16}
+
+
+def _code(t: torch.Tensor) -> int:
+    try:
+        return _DTYPES[t.dtype]
+    except KeyError:
+        raise TypeError(f"unsupported dtype {t.dtype}; use float32 or "
+                        "bfloat16") from None
+
+
+def _check(t: torch.Tensor, name: str, shape, dtype, device) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor, got {device}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected "
+                         f"{tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return t.data_ptr() if t is not None and t.numel() > 0 else None
+
+
+def _stream(device: torch.device, stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream(device).cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _shape3(x: torch.Tensor) -> Tuple[int, int, int]:
+    if x.dim() != 3:
+        raise ValueError(f"x must be [B, N, D], got shape {tuple(x.shape)}")
+    return tuple(x.shape)
+
+
+def fwd(x: torch.Tensor, scale: torch.Tensor, shift: torch.Tensor, *,
+        y: Optional[torch.Tensor] = None,
+        mean: Optional[torch.Tensor] = None,
+        rstd: Optional[torch.Tensor] = None, stream=None):
+    """y = LayerNorm(x) * (1 + scale[b]) + shift[b]; returns (y, mean, rstd).
+
+    x: [B, N, D]; scale, shift: [B, D] (same dtype); mean, rstd: [B, N] f32."""
+    B, N, D = _shape3(x)
+    dev, dt = x.device, x.dtype
+    code = _code(x)
+    _check(x, "x", (B, N, D), dt, dev)
+    _check(scale, "scale", (B, D), dt, dev)
+    _check(shift, "shift", (B, D), dt, dev)
+    if y is None:
+        y = torch.empty_like(x)
+    if mean is None:
+        mean = torch.empty(B, N, dtype=torch.float32, device=dev)
+    if rstd is None:
+        rstd = torch.empty(B, N, dtype=torch.float32, device=dev)
+    _check(y, "y", (B, N, D), dt, dev)
+    _check(mean, "mean", (B, N), torch.float32, dev)
+    _check(rstd, "rstd", (B, N), torch.float32, dev)
+    lib = _lib.load()
+    with torch.cuda.device(dev):
+        rc = lib.adaln_fwd(_ptr(x), _ptr(scale), _ptr(shift), _ptr(y),
+                           _ptr(mean), _ptr(rstd), B, N, D, code,
+                           _stream(dev, stream))
+    _lib.check(rc, "adaln_fwd")
+    return y, mean, rstd
+
+
+def bwd_workspace_bytes(B: int, N: int, D: int, dtype: torch.dtype) -> int:
+    code = _DTYPES.get(dtype, -1)
+    return int(_lib.load().adaln_bwd_workspace_bytes(B, N, D, code))
+
+
+def _bwd_common(dy, x, scale, mean, rstd):
+    B, N, D = _shape3(x)
+    dev, dt = x.device, x.dtype
+    _code(x)
+    _check(dy, "dy", (B, N, D), dt, dev)
+    _check(x, "x", (B, N, D), dt, dev)
+    if scale is not None:
+        _check(scale, "scale", (B, D), dt, dev)
+    _check(mean, "mean", (B, N), torch.float32, dev)
+    _check(rstd, "rstd", (B, N), torch.float32, dev)
+    return B, N, D, dev, dt
+
+
+def _workspace(workspace, B, N, D, dt, dev):
+    need = bwd_workspace_bytes(B, N, D, dt)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    if workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on "
+                         f"{dev}")
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def bwd(dy: torch.Tensor, x: torch.Tensor, scale: torch.Tensor,
+        mean: torch.Tensor, rstd: torch.Tensor, *,
+        dx: Optional[torch.Tensor] = None,
+        dscale: Optional[torch.Tensor] = None,
+        dshift: Optional[torch.Tensor] = None,
+        workspace: Optional[torch.Tensor] = None, stream=None):
+    """Backward of :func:`fwd`; returns (dx, dscale, dshift).
+
+    dscale and dshift are float32 [B, D]; the workspace (bytes from
+    :func:`bwd_workspace_bytes`) is allocated if not given."""
+    B, N, D, dev, dt = _bwd_common(dy, x, scale, mean, rstd)
+    if dx is None:
+        dx = torch.empty_like(x)
+    if dscale is None:
+        dscale = torch.empty(B, D, dtype=torch.float32, device=dev)
+    if dshift is None:
+        dshift = torch.empty(B, D, dtype=torch.float32, device=dev)
+    _check(dx, "dx", (B, N, D), dt, dev)
+    _check(dscale, "dscale", (B, D), torch.float32, dev)
+    _check(dshift, "dshift", (B, D), torch.float32, dev)
+    workspace, wbytes = _workspace(workspace, B, N, D, dt, dev)
+    lib = _lib.load()
+    with torch.cuda.device(dev):
+        rc = lib.adaln_bwd(_ptr(dy), _ptr(x), _ptr(scale), _ptr(mean),
+                           _ptr(rstd), _ptr(dx), _ptr(dscale), _ptr(dshift),
+                           _ptr(workspace), wbytes, B, N, D, _code(x),
+                           _stream(dev, stream))
+    _lib.check(rc, "adaln_bwd")
+    return dx, dscale, dshift
+
+
+def bwd_dx(dy, x, scale, mean, rstd, *, dx=None, stream=None):
+    """Input gradient only (one launch); returns dx."""
+    B, N, D, dev, dt = _bwd_common(dy, x, scale, mean, rstd)
+    if dx is None:
+        dx = torch.empty_like(x)
+    _check(dx, "dx", (B, N, D), dt, dev)
+    lib = _lib.load()
+    with torch.cuda.device(dev):
+        rc = lib.adaln_bwd_dx(_ptr(dy), _ptr(x), _ptr(scale), _ptr(mean),
+                              _ptr(rstd), _ptr(dx), B, N, D, _code(x),
+                              _stream(dev, stream))
+    _lib.check(rc, "adaln_bwd_dx")
+    return dx
+
+
+def bwd_dmod(dy, x, mean, rstd, *, dscale=None, dshift=None, workspace=None,
+             stream=None):
+    """Modulation gradients only (D-tile reduction); returns (dscale, dshift)."""
+    B, N, D, dev, dt = _bwd_common(dy, x, None, mean, rstd)
+    if dscale is None:
+        dscale = torch.empty(B, D, dtype=torch.float32, device=dev)
+    if dshift is None:
+        dshift = torch.empty(B, D, dtype=torch.float32, device=dev)
+    _check(dscale, "dscale", (B, D), torch.float32, dev)
+    _check(dshift, "dshift", (B, D), torch.float32, dev)
+    workspace, wbytes = _workspace(workspace, B, N, D, dt, dev)
+    lib = _lib.load()
+    with torch.cuda.device(dev):
+        rc = lib.adaln_bwd_dmod(_ptr(dy), _ptr(x), _ptr(mean), _ptr(rstd),
+                                _ptr(dscale), _ptr(dshift), _ptr(workspace),
+                                wbytes, B, N, D, _code(x),
+                                _stream(dev, stream))
+    _lib.check(rc, "adaln_bwd_dmod")
+    return dscale, dshift
+
+
+def bshape(S: int, m_mem: int, m_comp: int, p: int) -> int:
+    """Dual-constraint bucket batch size (host integer arithmetic in the
+    library); raises on invalid arguments."""
+    v = int(_lib.load().adaln_bshape(int(S), int(m_mem), int(m_comp), int(p)))
+    if v < 1:
+        _lib.check(v, "adaln_bshape")
+    return v
+
+
+def max_d(dtype: torch.dtype) -> int:
+    return int(_lib.load().adaln_max_d(_DTYPES.get(dtype, -1)))

@@ -1,0 +1,156 @@
+/*
+ * adaln.h -- C ABI of the fused AdaLN (LayerNorm-Modulate) library for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The operator is the one the AdaptiveLoad technical summary pages
+ * (gist.science, arXiv 2605.17923) describe in section 2 ("Methodology"),
+ * part B, "fused LayerNorm-Modulate kernels": each token row of x is
+ * normalised over the feature dimension D and then modulated by per-sample
+ * vectors, in one launch; in the backward pass the gradients of the
+ * modulation parameters are reduced along the sequence dimension N over a
+ * (d_tile, n_tile) grid with lanes pinned to features (the D-tile coalesced
+ * reduction).  The formula, which the pages leave implicit, is read as:
+ *
+ *     mean = (1/D) sum_d x          var = (1/D) sum_d (x - mean)^2
+ *     rstd = 1 / sqrt(var + 1e-6)   xhat = (x - mean) * rstd
+ *     y    = xhat * (1 + scale[b]) + shift[b]
+ *
+ *     g      = dy * (1 + scale[b])
+ *     dx     = rstd * (g - mean_d(g) - xhat * mean_d(g * xhat))
+ *     dscale = sum_n dy * xhat      dshift = sum_n dy      (per b and d)
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Layout.  Row-major, contiguous.  x, y, dy, dx are [B, N, D] in `dtype`;
+ *   scale and shift are [B, D] in `dtype`; mean and rstd are [B, N] float32;
+ *   dscale and dshift are [B, D] float32.  Row r = b*N + n.
+ * dtype.  ADALN_F32 or ADALN_BF16.  Arithmetic is float32 in registers;
+ *   bfloat16 outputs are rounded to nearest even.
+ * Pointers.  Device pointers (hipMalloc'd or torch CUDA/HIP tensors), each
+ *   16-byte aligned.  A pointer may be NULL only when its tensor has zero
+ *   elements.  Input and output buffers must not overlap.
+ * Sizes.  B, N >= 0; D > 0 and a multiple of 8 (bf16) or 4 (f32), at most
+ *   adaln_max_d(dtype); B*N < 2^31 rows, B*D < 2^31.
+ * Ownership.  The caller owns every buffer, including the backward
+ *   workspace.  The library allocates no device memory and keeps no state
+ *   between calls, so calls on different streams may run concurrently as long
+ *   as they use distinct output and workspace buffers.
+ * Streams.  `stream` is a hipStream_t passed as void* (NULL = the default
+ *   stream).  Calls enqueue kernels and return without synchronising.
+ * Errors.  Arguments are validated on the host before any HIP call; a failing
+ *   check returns a negative code and enqueues nothing.  A launch failure
+ *   returns ADALN_ERR_HIP.  adaln_strerror() names a code; adaln_last_error()
+ *   gives the calling thread's message for its most recent failing call.
+ */
+#ifndef ADALN_H
+#define ADALN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ADALN_F32 0
+#define ADALN_BF16 1
+
+#define ADALN_OK 0
+#define ADALN_ERR_INVALID (-1)     /* NULL pointer, bad size or exponent */
+#define ADALN_ERR_DTYPE (-2)       /* unknown dtype code */
+#define ADALN_ERR_ALIGN (-3)       /* D not a multiple of the vector width,
+                                      or a pointer not 16-byte aligned */
+#define ADALN_ERR_WORKSPACE (-4)   /* workspace NULL or too small */
+#define ADALN_ERR_HIP (-5)         /* the HIP runtime reported an error */
+#define ADALN_ERR_UNSUPPORTED (-6) /* D above adaln_max_d(dtype) */
+
+/*
+ * Forward pass: mean, rstd and y for every token row, one kernel launch.
+ * Section 2.B, forward pass: the row statistics stay in registers (and LDS
+ * when several wavefronts share a row) and the modulation is applied on the
+ * pass that writes y.
+ *   x      [B,N,D] dtype  in
+ *   scale  [B,D]   dtype  in
+ *   shift  [B,D]   dtype  in
+ *   y      [B,N,D] dtype  out
+ *   mean   [B,N]   f32    out (saved for the backward pass)
+ *   rstd   [B,N]   f32    out (saved for the backward pass)
+ * B*N == 0 is a successful no-op.
+ */
+int adaln_fwd(const void *x, const void *scale, const void *shift, void *y,
+              float *mean, float *rstd, int64_t B, int64_t N, int64_t D,
+              int dtype, void *stream);
+
+/*
+ * Bytes of device workspace adaln_bwd and adaln_bwd_dmod need for this
+ * shape: the per-(sample, n_tile) partial sums of the D-tile reduction.
+ * A pure function of its arguments.  Returns 0 for invalid arguments.
+ */
+size_t adaln_bwd_workspace_bytes(int64_t B, int64_t N, int64_t D, int dtype);
+
+/*
+ * Backward pass: dx, dscale and dshift.  Equivalent to adaln_bwd_dx followed
+ * by adaln_bwd_dmod on the same stream.
+ *   dy        [B,N,D] dtype in   upstream gradient dL/dy
+ *   x         [B,N,D] dtype in   the forward input
+ *   scale     [B,D]   dtype in
+ *   mean,rstd [B,N]   f32   in   as written by adaln_fwd for this x
+ *   dx        [B,N,D] dtype out
+ *   dscale    [B,D]   f32   out  (overwritten, not accumulated)
+ *   dshift    [B,D]   f32   out  (overwritten, not accumulated)
+ *   workspace, workspace_bytes: at least adaln_bwd_workspace_bytes(...)
+ *     bytes of device memory; contents on entry are ignored.
+ * With B*N == 0 and B*D > 0, dscale and dshift are set to zero.
+ */
+int adaln_bwd(const void *dy, const void *x, const void *scale,
+              const float *mean, const float *rstd, void *dx, float *dscale,
+              float *dshift, void *workspace, size_t workspace_bytes,
+              int64_t B, int64_t N, int64_t D, int dtype, void *stream);
+
+/*
+ * Backward, input gradient only: dx from dy, x, scale and the saved
+ * mean/rstd, one kernel launch (arguments as in adaln_bwd).  The pages give
+ * no design for dx; it is the exact gradient of the formula above.
+ */
+int adaln_bwd_dx(const void *dy, const void *x, const void *scale,
+                 const float *mean, const float *rstd, void *dx, int64_t B,
+                 int64_t N, int64_t D, int dtype, void *stream);
+
+/*
+ * Backward, modulation gradients only: dscale and dshift through the D-tile
+ * coalesced reduction of section 2.B (backward pass).  Two launches: a
+ * (d_tile, n_tile, b) grid in which each lane owns 16 bytes of features and
+ * accumulates down the rows of its n_tile in float32, writing per-tile
+ * partial sums to the workspace; then a fixed-order sum over the n_tiles.
+ * No floating-point atomics: results are bitwise reproducible.
+ * Arguments as in adaln_bwd.
+ */
+int adaln_bwd_dmod(const void *dy, const void *x, const float *mean,
+                   const float *rstd, float *dscale, float *dshift,
+                   void *workspace, size_t workspace_bytes, int64_t B,
+                   int64_t N, int64_t D, int dtype, void *stream);
+
+/*
+ * Dual-constraint bucket batch size of section 2.A:
+ *     max(1, min(floor(m_mem / S), floor(m_comp / S^p)))
+ * in exact integer arithmetic.  When S^p exceeds the int64 range the compute
+ * bound is 0 and the result is 1.  Returns ADALN_ERR_INVALID for S <= 0,
+ * negative bounds or a negative exponent.  Host-only; no HIP call.
+ */
+int64_t adaln_bshape(int64_t S, int64_t m_mem, int64_t m_comp, int32_t p);
+
+/* Largest D the row kernels accept for `dtype` (0 for an unknown dtype). */
+int64_t adaln_max_d(int dtype);
+
+/* Static, human-readable name of a return code. */
+const char *adaln_strerror(int code);
+
+/* The calling thread's message for its most recent failing call ("" if
+ * none); valid until that thread's next call into the library. */
+const char *adaln_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ADALN_H */

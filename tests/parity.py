@@ -1,0 +1,178 @@
+"""Parity helpers: run the HIP path and the oracle on the same seeded inputs
+and compare them under the tolerances below.
+
+Tolerances (per element; r = oracle value in float64, g = GPU value):
+
+* float32 outputs (y, dx of float32 inputs): |g - r| <= 1e-5 * max(|r|, rms)
+  where rms is the root mean square of the whole output tensor -- relative
+  1e-5 with a scale floor, since cancellation leaves some entries near 0.
+* bfloat16 outputs (y, dx of bfloat16 inputs), contract bound:
+  |g - r| <= 2e-2 + (2^-8 + 2^-16) * |r|.  2e-2 absolute, widened by the
+  half-ulp of bfloat16 (2^-8 relative) that correct rounding alone costs once
+  |r| >= 8, plus float32 slack.  The count of elements over the plain 2e-2
+  bound is reported.
+* bfloat16 outputs, strict bound (checked too): |g - r| <= 2^-8 * |r| +
+  1e-4 * rms, i.e. the stored value is the correctly rounded bfloat16 of a
+  float32 result that lies within 1e-4 * rms of the exact one.  Without it
+  the 2e-2 bound would be vacuous for dx, whose entries are about 1e-2.
+* dscale, dshift (float32 sums over N): |g - r| <= 1e-3 * max(|r|, rms).
+* mean: |g - r| <= 1e-5 * max(|r|, rms of the row's x);
+  rstd: |g - r| <= 1e-5 * |r|.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Dict, Optional, Sequence
+
+import numpy as np
+import torch
+
+F32_RTOL = 1e-5
+BF16_ATOL = 2e-2
+BF16_RTOL = 2.0 ** -8 + 2.0 ** -16
+STRICT_RTOL = 2.0 ** -8
+STRICT_RMS = 1e-4
+DMOD_RTOL = 1e-3
+STAT_RTOL = 1e-5
+
+
+def _np(t) -> np.ndarray:
+    if isinstance(t, torch.Tensor):
+        return t.detach().to("cpu", torch.float64).numpy()
+    return np.asarray(t, dtype=np.float64)
+
+
+def _rms(r: np.ndarray) -> float:
+    return float(np.sqrt(np.mean(r * r))) if r.size else 0.0
+
+
+@dataclass
+class Report:
+    name: str
+    max_err: float
+    max_ratio: float      # max over elements of err / allowed (<= 1 passes)
+    over_plain: int = 0   # bf16: elements over the plain 2e-2 bound
+    n: int = 0
+
+    def __str__(self):
+        s = (f"{self.name}: n={self.n} max_err={self.max_err:.3e} "
+             f"worst/allowed={self.max_ratio:.3f}")
+        if self.over_plain:
+            s += f" over_2e-2={self.over_plain}"
+        return s
+
+
+def _judge(name, g, r, allowed, over_plain=0) -> Report:
+    err = np.abs(g - r)
+    ratio = np.max(err / allowed) if err.size else 0.0
+    rep = Report(name, float(err.max()) if err.size else 0.0, float(ratio),
+                 over_plain, int(err.size))
+    assert ratio <= 1.0, f"parity failure: {rep}"
+    return rep
+
+
+def check_out(name: str, got, ref, dtype: str) -> Sequence[Report]:
+    """y or dx: float32 or bfloat16 rules."""
+    g, r = _np(got), _np(ref)
+    assert g.shape == r.shape, (name, g.shape, r.shape)
+    assert np.all(np.isfinite(g)), f"{name}: non-finite GPU values"
+    rms = _rms(r)
+    if dtype == "f32":
+        return [_judge(name, g, r, F32_RTOL * np.maximum(np.abs(r), rms))]
+    over = int(np.sum(np.abs(g - r) > BF16_ATOL))
+    a = _judge(name + "[contract]", g, r, BF16_ATOL + BF16_RTOL * np.abs(r),
+               over)
+    b = _judge(name + "[strict]", g, r,
+               STRICT_RTOL * np.abs(r) + STRICT_RMS * rms + 1e-30)
+    return [a, b]
+
+
+def check_dmod(name: str, got, ref) -> Report:
+    g, r = _np(got), _np(ref)
+    assert g.shape == r.shape
+    rms = _rms(r)
+    return _judge(name, g, r, DMOD_RTOL * np.maximum(np.abs(r), rms) + 1e-30)
+
+
+def check_stats(got_mean, got_rstd, ref_mean, ref_rstd, x_rows) -> Sequence[Report]:
+    gm, rm = _np(got_mean), _np(ref_mean)
+    gr, rr = _np(got_rstd), _np(ref_rstd)
+    xr = _np(x_rows)
+    row_rms = np.sqrt(np.mean(xr * xr, axis=-1))
+    a = _judge("mean", gm, rm, STAT_RTOL * np.maximum(np.abs(rm), row_rms)
+               + 1e-30)
+    b = _judge("rstd", gr, rr, STAT_RTOL * np.abs(rr))
+    return [a, b]
+
+
+# ----------------------------------------------------------------- running
+
+def to_device(inp, device="cuda"):
+    return {k: (None if v is None else v.to(device))
+            for k, v in (("x", inp.x), ("scale", inp.scale),
+                         ("shift", inp.shift), ("dy", inp.dy))}
+
+
+def gpu_fwd_bwd(dev: Dict[str, torch.Tensor], stream=None):
+    """The HIP path as a caller runs it: adaln_fwd then adaln_bwd."""
+    import adaln_fwd_amd as A
+    y, mean, rstd = A.fwd(dev["x"], dev["scale"], dev["shift"], stream=stream)
+    dx, dscale, dshift = A.bwd(dev["dy"], dev["x"], dev["scale"], mean, rstd,
+                               stream=stream)
+    return dict(y=y, mean=mean, rstd=rstd, dx=dx, dscale=dscale,
+                dshift=dshift)
+
+
+def oracle_rows(inp, rows: np.ndarray):
+    """Oracle forward and dx for the token rows `rows` (flat b*N + n)."""
+    import oracle
+    B, N, D = inp.x.shape
+    rows = np.asarray(rows, dtype=np.int64)
+    xr = inp.x.reshape(B * N, D)[torch.from_numpy(rows)].unsqueeze(1)
+    gr = inp.dy.reshape(B * N, D)[torch.from_numpy(rows)].unsqueeze(1)
+    bidx = torch.from_numpy(rows // N)
+    s = inp.scale[bidx]
+    h = inp.shift[bidx]
+    y, mean, rstd = oracle.fwd(xr, s, h)
+    dx, _, _ = oracle.bwd(gr, xr, s, want_dmod=False)
+    return dict(y=y[:, 0], mean=mean[:, 0], rstd=rstd[:, 0], dx=dx[:, 0],
+                x=xr[:, 0])
+
+
+def compare_rows(inp, out, rows: np.ndarray, dtype: str):
+    """Compare GPU outputs (CPU copies) on `rows` with the oracle."""
+    B, N, D = inp.x.shape
+    ref = oracle_rows(inp, rows)
+    t = torch.from_numpy(np.asarray(rows, np.int64))
+    reps = []
+    reps += check_out("y", out["y"].reshape(B * N, D)[t], ref["y"], dtype)
+    reps += check_out("dx", out["dx"].reshape(B * N, D)[t], ref["dx"], dtype)
+    reps += check_stats(out["mean"].reshape(-1)[t], out["rstd"].reshape(-1)[t],
+                        ref["mean"], ref["rstd"], ref["x"])
+    return reps
+
+
+def compare_full(inp, out, dtype: str, with_rows: bool = True):
+    """Full element-by-element comparison (sizes the oracle finishes fast)."""
+    import oracle
+    reps = []
+    if with_rows:
+        y, mean, rstd = oracle.fwd(inp.x, inp.scale, inp.shift)
+        dx, ds, dh = oracle.bwd(inp.dy, inp.x, inp.scale)
+        reps += check_out("y", out["y"], y, dtype)
+        reps += check_out("dx", out["dx"], dx, dtype)
+        reps += check_stats(out["mean"], out["rstd"], mean, rstd, inp.x)
+    else:
+        _, ds, dh = oracle.bwd(inp.dy, inp.x, inp.scale, want_dx=False)
+    reps.append(check_dmod("dscale", out["dscale"], ds))
+    reps.append(check_dmod("dshift", out["dshift"], dh))
+    return reps
+
+
+def sample_rows(total: int, k: int, seed: int = 0) -> np.ndarray:
+    """k distinct rows: the first and last 8 plus a seeded random draw."""
+    g = np.random.default_rng(seed)
+    edge = np.r_[np.arange(min(8, total)), np.arange(max(0, total - 8), total)]
+    rnd = g.choice(total, size=min(k, total), replace=False)
+    return np.unique(np.r_[edge, rnd])

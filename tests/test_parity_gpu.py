@@ -1,0 +1,241 @@
+"""GPU parity of the HIP path against the oracle, through the C ABI.
+
+Small and medium shapes are compared element by element; the full-size
+workloads are compared on sampled token rows (y, dx, mean, rstd, which are
+row-local) and in full for dscale/dshift.  Every case prints its name before
+touching the GPU.
+"""
+
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from synth import workloads as W
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(f"[parity] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module")
+def A():
+    import adaln_fwd_amd
+    adaln_fwd_amd.load()
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return adaln_fwd_amd
+
+
+def _run_full(A, wl, seed=0, bucket=0, label=None):
+    _say(f"{label or wl.name} B={wl.B} N={wl.N} D={wl.D} {wl.dtype} seed={seed}")
+    inp = synth.make_inputs(wl, seed=seed, bucket=bucket)
+    dev = P.to_device(inp)
+    out = P.gpu_fwd_bwd(dev)
+    torch.cuda.synchronize()
+    out = {k: v.cpu() for k, v in out.items()}
+    reps = P.compare_full(inp, out, wl.dtype)
+    for r in reps:
+        _say(f"  {r}")
+    return inp, out
+
+
+def test_tiny_f32(A):
+    _run_full(A, synth.TINY_F32)
+
+
+def test_image_bucket_full(A):
+    _run_full(A, synth.IMAGE_BUCKET)
+
+
+def test_video_bucket_full(A):
+    _run_full(A, synth.VIDEO_BUCKET)
+
+
+@pytest.mark.parametrize("B,N,D,dtype,kind", [
+    (1, 1, 1536, "bf16", "offset"),        # a single token
+    (3, 1, 64, "f32", "normal"),           # one token per sample
+    (2, 1000, 1536, "bf16", "offset"),     # ragged n_tiles
+    (5, 77, 3072, "bf16", "offset"),       # several samples, ragged
+    (2, 300, 5120, "bf16", "outliers"),
+    (1, 40, 8, "bf16", "normal"),          # smallest bf16 row
+    (2, 33, 4, "f32", "normal"),           # smallest f32 row
+    (2, 130, 520, "bf16", "normal"),       # partial last vector column
+    (2, 64, 4104, "bf16", "normal"),       # V rounded up (513 vectors)
+    (1, 50, 6144, "bf16", "normal"),
+    (1, 30, 8192, "bf16", "normal"),
+    (1, 20, 12288, "bf16", "normal"),      # two wavefronts per row
+    (1, 9, 32768, "bf16", "normal"),       # four wavefronts per row (max D)
+    (2, 17, 8192, "f32", "normal"),        # two wavefronts per row, f32
+    (1, 5, 16384, "f32", "normal"),        # largest f32 row
+    (3, 257, 1024, "f32", "offset"),
+])
+def test_shapes(A, B, N, D, dtype, kind):
+    wl = W.custom(B, N, D, dtype, x_kind=kind, dy_std=1e-2 if dtype ==
+                  "bf16" else 1.0)
+    _run_full(A, wl, seed=B + N + D)
+
+
+def test_large_model_sampled(A):
+    """D=5120, N=75600 at full size: sampled rows plus full dscale/dshift."""
+    wl = synth.LARGE_MODEL
+    _say(f"{wl.name} full size, sampled rows")
+    inp = synth.make_inputs(wl)
+    dev = P.to_device(inp)
+    out = P.gpu_fwd_bwd(dev)
+    torch.cuda.synchronize()
+    out = {k: v.cpu() for k, v in out.items()}
+    del dev
+    rows = P.sample_rows(wl.rows, 1500)
+    for r in P.compare_rows(inp, out, rows, wl.dtype):
+        _say(f"  {r}")
+    for r in P.compare_full(inp, out, wl.dtype, with_rows=False):
+        _say(f"  {r}")
+    # every output is finite
+    for k in ("y", "dx", "mean", "rstd"):
+        assert torch.isfinite(out[k].float()).all(), k
+
+
+def test_constant_and_extreme_rows(A):
+    B, N, D = 2, 6, 1024
+    x = torch.randn(B, N, D, generator=torch.Generator().manual_seed(3))
+    x[0, 0] = 2.5                 # constant row: var = 0, rstd = 1/sqrt(eps)
+    x[0, 1] = 0.0                 # all-zero row
+    x[1, 2] *= 1e4                # huge row
+    x[1, 3] *= 1e-4               # tiny row (var below eps)
+    x = x.to(torch.bfloat16)
+    g = torch.Generator().manual_seed(4)
+    inp = synth.Inputs(x=x, scale=(0.1 * torch.randn(B, D, generator=g)).to(
+        torch.bfloat16), shift=(0.1 * torch.randn(B, D, generator=g)).to(
+        torch.bfloat16), dy=(0.01 * torch.randn(B, N, D, generator=g)).to(
+        torch.bfloat16), workload=None, seed=0, bucket=0)
+    _say("constant/zero/huge/tiny rows")
+    out = P.gpu_fwd_bwd(P.to_device(inp))
+    torch.cuda.synchronize()
+    out = {k: v.cpu() for k, v in out.items()}
+    for r in P.compare_full(inp, out, "bf16"):
+        _say(f"  {r}")
+
+
+def test_deterministic(A):
+    wl = W.custom(2, 3000, 1536, "bf16", x_kind="offset", dy_std=1e-2)
+    _say("bitwise determinism")
+    dev = P.to_device(synth.make_inputs(wl))
+    a = P.gpu_fwd_bwd(dev)
+    b = P.gpu_fwd_bwd(dev)
+    torch.cuda.synchronize()
+    for k in a:
+        assert torch.equal(a[k], b[k]), k
+
+
+def test_side_stream(A):
+    wl = W.custom(3, 500, 3072, "bf16", x_kind="offset", dy_std=1e-2)
+    _say("non-default stream")
+    inp = synth.make_inputs(wl)
+    dev = P.to_device(inp)
+    ref = P.gpu_fwd_bwd(dev)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        got = P.gpu_fwd_bwd(dev, stream=s)
+    s.synchronize()
+    for k in ref:
+        assert torch.equal(ref[k], got[k]), k
+
+
+def test_guard_bytes_untouched(A):
+    """Outputs written through views into larger buffers leave the bytes
+    before and after them untouched."""
+    B, N, D = 3, 123, 1536
+    wl = W.custom(B, N, D, "bf16", x_kind="offset", dy_std=1e-2)
+    _say("guard bytes around outputs")
+    inp = synth.make_inputs(wl)
+    dev = P.to_device(inp)
+    pad = 4096  # elements, keeps 16-byte alignment
+
+    def guarded(n, dtype):
+        buf = torch.full((n + 2 * pad,), -7.0, dtype=dtype, device="cuda")
+        return buf, buf[pad:pad + n]
+
+    yb, y = guarded(B * N * D, torch.bfloat16)
+    mb, mean = guarded(B * N, torch.float32)
+    rb, rstd = guarded(B * N, torch.float32)
+    xb, dx = guarded(B * N * D, torch.bfloat16)
+    sb, dscale = guarded(B * D, torch.float32)
+    hb, dshift = guarded(B * D, torch.float32)
+    need = A.bwd_workspace_bytes(B, N, D, torch.bfloat16)
+    wb, ws = guarded(need // 4, torch.float32)
+    A.fwd(dev["x"], dev["scale"], dev["shift"], y=y.view(B, N, D),
+          mean=mean.view(B, N), rstd=rstd.view(B, N))
+    A.bwd(dev["dy"], dev["x"], dev["scale"], mean.view(B, N), rstd.view(B, N),
+          dx=dx.view(B, N, D), dscale=dscale.view(B, D),
+          dshift=dshift.view(B, D), workspace=ws)
+    torch.cuda.synchronize()
+    for buf in (yb, mb, rb, xb, sb, hb, wb):
+        assert torch.all(buf[:pad] == -7.0) and torch.all(buf[-pad:] == -7.0)
+    out = dict(y=y.view(B, N, D).cpu(), mean=mean.view(B, N).cpu(),
+               rstd=rstd.view(B, N).cpu(), dx=dx.view(B, N, D).cpu(),
+               dscale=dscale.view(B, D).cpu(), dshift=dshift.view(B, D).cpu())
+    P.compare_full(inp, out, "bf16")
+
+
+def test_split_entry_points_match_bwd(A):
+    """adaln_bwd equals adaln_bwd_dx followed by adaln_bwd_dmod."""
+    wl = W.custom(2, 700, 3072, "bf16", x_kind="offset", dy_std=1e-2)
+    _say("bwd == bwd_dx + bwd_dmod")
+    dev = P.to_device(synth.make_inputs(wl))
+    out = P.gpu_fwd_bwd(dev)
+    dx = A.bwd_dx(dev["dy"], dev["x"], dev["scale"], out["mean"], out["rstd"])
+    ds, dh = A.bwd_dmod(dev["dy"], dev["x"], out["mean"], out["rstd"])
+    torch.cuda.synchronize()
+    assert torch.equal(dx, out["dx"])
+    assert torch.equal(ds, out["dscale"]) and torch.equal(dh, out["dshift"])
+
+
+def test_empty(A):
+    _say("empty inputs")
+    d = "cuda"
+    x = torch.empty(0, 5, 64, dtype=torch.bfloat16, device=d)
+    y, m, r = A.fwd(x, torch.empty(0, 64, dtype=torch.bfloat16, device=d),
+                    torch.empty(0, 64, dtype=torch.bfloat16, device=d))
+    assert y.shape == (0, 5, 64)
+    # N = 0: dscale/dshift are defined (empty sums) and zero
+    x = torch.empty(3, 0, 64, dtype=torch.bfloat16, device=d)
+    s = torch.zeros(3, 64, dtype=torch.bfloat16, device=d)
+    y, m, r = A.fwd(x, s, s)
+    ds = torch.full((3, 64), 5.0, device=d)
+    dh = torch.full((3, 64), 5.0, device=d)
+    A.bwd(x, x, s, m, r, dscale=ds, dshift=dh)
+    torch.cuda.synchronize()
+    assert torch.all(ds == 0) and torch.all(dh == 0)
+
+
+def test_abi_errors_on_device_buffers(A):
+    _say("error codes with device buffers")
+    lib = A.load()
+    # every buffer is large enough for the call it is passed to, so even a
+    # missed check could not write out of bounds
+    B, N, D = 2, 4, 1536
+    x = torch.zeros(B * N * D + 64, dtype=torch.bfloat16, device="cuda")
+    y = torch.zeros(B * N * D, dtype=torch.bfloat16, device="cuda")
+    s = torch.zeros(B, D, dtype=torch.bfloat16, device="cuda")
+    st = torch.zeros(B, N, dtype=torch.float32, device="cuda")
+    dm = torch.zeros(B, D, dtype=torch.float32, device="cuda")
+    p = x.data_ptr()
+    # misaligned x
+    rc = lib.adaln_fwd(p + 2, s.data_ptr(), s.data_ptr(), y.data_ptr(),
+                       st.data_ptr(), st.data_ptr(), B, N, D, 1, None)
+    assert rc == -3
+    # workspace too small
+    need = lib.adaln_bwd_workspace_bytes(B, N, D, 1)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    rc = lib.adaln_bwd(p, p, s.data_ptr(), st.data_ptr(), st.data_ptr(),
+                       y.data_ptr(), dm.data_ptr(), dm.data_ptr(),
+                       ws.data_ptr(), need - 1, B, N, D, 1, None)
+    assert rc == -4
+    torch.cuda.synchronize()
