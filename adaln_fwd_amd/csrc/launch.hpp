@@ -4,6 +4,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <tuple>
+#include <type_traits>
+
 namespace adaln {
 
 // How a token row is spread over a workgroup: W wavefronts share one row and
@@ -38,6 +41,8 @@ constexpr int64_t kMaxGrid = 1 << 20;
 template <typename... P, typename... A>
 inline hipError_t launch_kernel(void (*k)(P...), int64_t blocks,
                                 hipStream_t s, A... args) {
+  static_assert(std::is_same<std::tuple<P...>, std::tuple<A...>>::value,
+                "kernel arguments must match the kernel's parameter types");
   if (blocks <= 0) return hipSuccess;
   const unsigned grid = (unsigned)(blocks < kMaxGrid ? blocks : kMaxGrid);
   void *argv[] = {(void *)&args...};

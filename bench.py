@@ -1,0 +1,295 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused AdaLN forward+backward on one MI355X.
+
+One step is the whole hot path over one batch of synthetic input already
+resident in HBM: adaln_fwd, then the backward pass (adaln_bwd_dx followed by
+adaln_bwd_dmod, exactly what adaln_bwd enqueues), on torch's current stream.
+W untimed warm-up steps run first; then exactly K steps are timed between two
+device synchronisations.  HIP events recorded on the same stream between the
+calls give each kernel's average duration inside the timed region.
+
+Prints one JSON line:
+  value         tokens/s over the timed steps (wall clock)
+  hbm_gbps      algorithmic bytes of the step / step time
+  kernels       per-call average duration, algorithmic bytes and GB/s
+  roofline      the dominant kernel against the 8 TB/s HBM peak; `traffic`
+                from the committed rocprofv3 counter summary when it was taken
+                on the current kernel sources, else null
+  cpu_baseline  the float64 CPU oracle on a bounded sample of the same
+                workload, on this host's cores
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import glob
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = ("fused AdaLN fwd+bwd tokens/s and achieved HBM GB/s (% of peak), "
+          "1 MI355X")
+HBM_PEAK_GBPS = 8000.0
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(ROOT, "adaln_fwd_amd", "csrc", "*")))
+    files.append(os.path.join(ROOT, "include", "adaln.h"))
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(B, N, D, esize, n_tiles):
+    """Bytes each call must move at minimum (reads + writes)."""
+    T = B * N
+    act = T * D * esize          # one [B, N, D] tensor
+    stats = 4 * T                # one [B, N] float32 vector
+    mod = B * D * esize          # one [B, D] modulation vector
+    part = 2 * B * n_tiles * D * 4
+    return {
+        # read x, scale, shift; write y, mean, rstd
+        "fwd": 2 * act + 2 * mod + 2 * stats,
+        # read dy, x, scale, mean, rstd; write dx
+        "bwd_dx": 3 * act + mod + 2 * stats,
+        # read dy, x, mean, rstd; write then read the partials; write
+        # dscale, dshift
+        "bwd_dmod": 2 * act + 2 * stats + 2 * part + 2 * B * D * 4,
+    }
+
+
+def load_traffic(kernel: str, workload: str, src_hash: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if
+    it was measured on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_pmc.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != src_hash:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(inp, budget_s: float, chunk_rows: int = 4096):
+    """The oracle, untuned, on chunks of the workload's token rows until
+    about `budget_s` seconds of oracle time have been spent."""
+    import torch
+    import oracle
+    B, N, D = inp.x.shape
+    x2 = inp.x.reshape(B * N, D)
+    g2 = inp.dy.reshape(B * N, D)
+    rows_done, spent, start = 0, 0.0, 0
+    while spent < budget_s and rows_done < 4 * B * N:
+        r0 = start % (B * N)
+        r1 = min(B * N, r0 + chunk_rows)
+        idx = torch.arange(r0, r1)
+        b = idx // N
+        xs = x2[r0:r1].unsqueeze(1).double().numpy()
+        gs = g2[r0:r1].unsqueeze(1).double().numpy()
+        ss = inp.scale[b].double().numpy()
+        hs = inp.shift[b].double().numpy()
+        t0 = time.perf_counter()
+        oracle.fwd(xs, ss, hs)
+        oracle.bwd(gs, xs, ss)
+        spent += time.perf_counter() - t0
+        rows_done += r1 - r0
+        start = r1
+    return {
+        "value": rows_done / spent,
+        "unit": "tokens/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": (f"{rows_done} token rows of {B}x{N}x{D} (chunks of "
+                   f"{chunk_rows} rows from row 0), forward + backward in "
+                   f"float64, {spent:.1f} s of oracle time"),
+    }
+
+
+def copy_probe(nbytes: int, steps: int, warmup: int) -> int:
+    """torch's copy kernel over `nbytes` (read nbytes + write nbytes)."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(warmup):
+        dst.copy_(src)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for _ in range(steps):
+        dst.copy_(src)
+    ev[1].record()
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / steps
+    moved = 2 * src.numel() * 4
+    print(json.dumps({"probe": "torch_copy", "bytes_per_launch": moved,
+                      "avg_ms": round(ms, 5),
+                      "gbps": round(moved / (ms * 1e-3) / 1e9, 1)}),
+          flush=True)
+    return 0
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="large_model")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-budget", type=float, default=10.0,
+                    help="seconds of oracle time for cpu_baseline (0: skip)")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="time torch's device copy of one workload-sized "
+                         "tensor instead (achievable-bandwidth reference and "
+                         "counter calibration)")
+    args = ap.parse_args(argv)
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on one GPU only: this operator is measured on a "
+              "single MI355X and has no multi-GPU path (requested "
+              f"--gpus {args.gpus}, WORLD_SIZE={world}).", file=sys.stderr)
+        return 2
+    if args.steps < 1 or args.warmup < 0:
+        print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
+        return 2
+
+    import torch
+    import adaln_fwd_amd as A
+    import synth
+
+    A.load()
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        return 1
+    wl = synth.BY_NAME[args.workload]
+    if wl.B is None:
+        print(f"{wl.name} is a schedule, not a single-batch workload",
+              file=sys.stderr)
+        return 2
+    B, N, D = wl.shape
+    dt = synth.torch_dtype(wl.dtype)
+    esize = torch.empty((), dtype=dt).element_size()
+    if args.copy_probe:
+        return copy_probe(B * N * D * esize, args.steps, args.warmup)
+    log(f"workload {wl.name} B={B} N={N} D={D} {wl.dtype}: drawing inputs")
+    inp = synth.make_inputs(wl, seed=args.seed)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    x = inp.x.to(dev)
+    scale = inp.scale.to(dev)
+    shift = inp.shift.to(dev)
+    dy = inp.dy.to(dev)
+    y = torch.empty_like(x)
+    dx = torch.empty_like(x)
+    mean = torch.empty(B, N, dtype=torch.float32, device=dev)
+    rstd = torch.empty(B, N, dtype=torch.float32, device=dev)
+    dscale = torch.empty(B, D, dtype=torch.float32, device=dev)
+    dshift = torch.empty(B, D, dtype=torch.float32, device=dev)
+    wbytes = A.bwd_workspace_bytes(B, N, D, dt)
+    ws = torch.empty(max(wbytes, 1), dtype=torch.uint8, device=dev)
+    n_tiles = wbytes // (2 * 4 * B * D) if B * D else 0
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        A.fwd(x, scale, shift, y=y, mean=mean, rstd=rstd, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        A.bwd_dx(dy, x, scale, mean, rstd, dx=dx, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+        A.bwd_dmod(dy, x, mean, rstd, dscale=dscale, dshift=dshift,
+                   workspace=ws, stream=stream)
+        if ev is not None:
+            ev[3].record(stream)
+
+    log(f"warm-up {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)]
+              for _ in range(args.steps)]
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_step = 1e3 * elapsed / args.steps
+
+    names = ("fwd", "bwd_dx", "bwd_dmod")
+    avg_ms = {n: sum(ev[i].elapsed_time(ev[i + 1]) for ev in events)
+              / args.steps for i, n in enumerate(names)}
+    byts = algorithmic_bytes(B, N, D, esize, n_tiles)
+    kernels = {n: {"avg_ms": round(avg_ms[n], 5),
+                   "bytes": int(byts[n]),
+                   "gbps": round(byts[n] / (avg_ms[n] * 1e-3) / 1e9, 1)}
+               for n in names}
+    step_bytes = sum(byts.values())
+    gbps = step_bytes / (ms_step * 1e-3) / 1e9
+    tokens_s = B * N / (ms_step * 1e-3)
+
+    dom = max(("fwd", "bwd_dx"), key=lambda n: avg_ms[n])
+    src_hash = kernel_source_hash()
+    achieved = byts[dom] / (avg_ms[dom] * 1e-3) / 1e9
+    roofline = {
+        "kernel": dom,
+        "bound": "hbm",
+        "achieved": round(achieved, 1),
+        "peak": HBM_PEAK_GBPS,
+        "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBPS, 4),
+        "traffic": load_traffic(dom, wl.name, src_hash),
+        "algorithmic_bytes_per_launch": int(byts[dom]),
+        "avg_launch_ms": round(avg_ms[dom], 5),
+    }
+
+    cpu = None
+    if args.cpu_budget > 0:
+        log(f"cpu baseline: oracle for ~{args.cpu_budget:.0f} s")
+        cpu = cpu_baseline(inp, args.cpu_budget)
+
+    rec = {
+        "metric": METRIC,
+        "value": round(tokens_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": B, "N": N, "D": D,
+                   "dtype": wl.dtype},
+        "hbm_gbps": round(gbps, 1),
+        "hbm_frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
+        "kernels": kernels,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernel_source_hash": src_hash,
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
