@@ -3,8 +3,9 @@ MI355X (gfx950), as hand-written HIP kernels behind a C ABI
 (include/adaln.h).  PyTorch supplies device memory and streams only."""
 
 from ._lib import AdalnError, BF16, F32, LIB_PATH, load
-from .ops import (bshape, bwd, bwd_dmod, bwd_dx, bwd_workspace_bytes, fwd,
-                  max_d)
+from .ops import (bshape, bwd, bwd_dmod, bwd_dx, bwd_finish, bwd_fused,
+                  bwd_fused_plan, bwd_workspace_bytes, fwd, max_d)
 
 __all__ = ["AdalnError", "BF16", "F32", "LIB_PATH", "load", "bshape", "bwd",
-           "bwd_dmod", "bwd_dx", "bwd_workspace_bytes", "fwd", "max_d"]
+           "bwd_dmod", "bwd_dx", "bwd_finish", "bwd_fused", "bwd_fused_plan", "bwd_workspace_bytes",
+           "fwd", "max_d"]

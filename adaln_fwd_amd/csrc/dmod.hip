@@ -56,8 +56,8 @@ __global__ __launch_bounds__(kBlock) void dmod_partial_kernel(
         const int nn = n + u * kWaves;
         const bool live = nn < n1;
         const int64_t off = (row0 + (live ? nn : n0)) * D + (int64_t)j * E;
-        xv[u] = (live && ok) ? load_vec(x + off) : vzero();
-        gv[u] = (live && ok) ? load_vec(dy + off) : vzero();
+        xv[u] = (live && ok) ? load_stream(x + off) : vzero();
+        gv[u] = (live && ok) ? load_stream(dy + off) : vzero();
         mu[u] = live ? mean[row0 + nn] : 0.f;
         r[u] = live ? rstd[row0 + nn] : 0.f;
       }
@@ -106,15 +106,18 @@ __global__ __launch_bounds__(kBlock) void dmod_partial_kernel(
 }
 
 // dscale[b, d] = sum over t = 0 .. n_tiles-1 of part_scale[b, t, d] (and the
-// same for dshift).  Lane l of every wavefront owns 4 features; wavefront w
-// sums tiles w, w+4, w+8, ... in order, and the four wavefront sums are added
-// in wavefront order.  With n_tiles == 0 the outputs are zero.
-__global__ __launch_bounds__(kBlock) void dmod_finish_kernel(
+// same for dshift).  A workgroup of 16 wavefronts covers 64 float4 columns of
+// one sample: lane l owns 4 features, wavefront w sums tiles w, w+16, w+32,
+// ... in order, and the 16 wavefront sums are added in wavefront order.  The
+// tile split keeps enough loads in flight to stream the partials at a useful
+// fraction of HBM bandwidth.  With n_tiles == 0 the outputs are zero.
+constexpr int kFinishWaves = 16;
+
+__global__ __launch_bounds__(kFinishWaves * kWave) void dmod_finish_kernel(
     const float *__restrict__ part_scale, const float *__restrict__ part_shift,
     float *__restrict__ dscale, float *__restrict__ dshift, int32_t D,
     int32_t n_tiles, int32_t col_blocks, int64_t total_blocks) {
-  constexpr int kWaves = kBlock / kWave;
-  __shared__ float4 stage[kWaves - 1][2][kWave];
+  __shared__ float4 stage[kFinishWaves - 1][2][kWave];
   const int lane = lane_id();
   const int wave = wave_id();
   const int ncol = D / 4;
@@ -131,8 +134,8 @@ __global__ __launch_bounds__(kBlock) void dmod_finish_kernel(
           part_scale + (int64_t)b * n_tiles * D) + c;
       const float4 *ph = reinterpret_cast<const float4 *>(
           part_shift + (int64_t)b * n_tiles * D) + c;
-#pragma unroll 4
-      for (int t = wave; t < n_tiles; t += kWaves) {
+#pragma unroll 8
+      for (int t = wave; t < n_tiles; t += kFinishWaves) {
         const float4 vs = ps[(int64_t)t * ncol];
         const float4 vh = ph[(int64_t)t * ncol];
         as.x += vs.x; as.y += vs.y; as.z += vs.z; as.w += vs.w;
@@ -146,7 +149,7 @@ __global__ __launch_bounds__(kBlock) void dmod_finish_kernel(
     __syncthreads();
     if (wave == 0 && ok) {
 #pragma unroll
-      for (int w = 0; w < kWaves - 1; ++w) {
+      for (int w = 0; w < kFinishWaves - 1; ++w) {
         const float4 vs = stage[w][0][lane];
         const float4 vh = stage[w][1][lane];
         as.x += vs.x; as.y += vs.y; as.z += vs.z; as.w += vs.w;
@@ -159,35 +162,36 @@ __global__ __launch_bounds__(kBlock) void dmod_finish_kernel(
   }
 }
 
-
-hipError_t launch_dmod(int dtype, const DmodPlan &plan, const void *dy,
-                       const void *x, const float *mean, const float *rstd,
-                       float *part_scale, float *part_shift, float *dscale,
-                       float *dshift, int32_t B, int32_t N, int32_t D,
-                       hipStream_t stream) {
+hipError_t launch_dmod_partial(int dtype, const DmodPlan &plan,
+                               const void *dy, const void *x,
+                               const float *mean, const float *rstd,
+                               float *part_scale, float *part_shift,
+                               int32_t B, int32_t N, int32_t D,
+                               hipStream_t stream) {
   const int64_t total_tiles = (int64_t)plan.d_tiles * plan.n_tiles * B;
-  hipError_t e = hipSuccess;
-  if (total_tiles > 0) {
-    if (dtype == 1)
-      e = launch_kernel(dmod_partial_kernel<bf16>, total_tiles, stream,
-                        (const bf16 *)dy, (const bf16 *)x, mean, rstd,
-                        part_scale, part_shift, N, D, (int32_t)plan.d_tiles,
-                        (int32_t)plan.n_tile, (int32_t)plan.n_tiles,
-                        total_tiles);
-    else
-      e = launch_kernel(dmod_partial_kernel<float>, total_tiles, stream,
-                        (const float *)dy, (const float *)x, mean, rstd,
-                        part_scale, part_shift, N, D, (int32_t)plan.d_tiles,
-                        (int32_t)plan.n_tile, (int32_t)plan.n_tiles,
-                        total_tiles);
-    if (e != hipSuccess) return e;
-  }
+  if (dtype == 1)
+    return launch_kernel(dmod_partial_kernel<bf16>, total_tiles, stream,
+                         (const bf16 *)dy, (const bf16 *)x, mean, rstd,
+                         part_scale, part_shift, N, D, (int32_t)plan.d_tiles,
+                         (int32_t)plan.n_tile, (int32_t)plan.n_tiles,
+                         total_tiles);
+  return launch_kernel(dmod_partial_kernel<float>, total_tiles, stream,
+                       (const float *)dy, (const float *)x, mean, rstd,
+                       part_scale, part_shift, N, D, (int32_t)plan.d_tiles,
+                       (int32_t)plan.n_tile, (int32_t)plan.n_tiles,
+                       total_tiles);
+}
+
+hipError_t launch_dmod_finish(const float *part_scale,
+                              const float *part_shift, float *dscale,
+                              float *dshift, int32_t B, int32_t D,
+                              int32_t n_tiles, hipStream_t stream) {
   const int32_t col_blocks = (D / 4 + kWave - 1) / kWave;
   const int64_t total_blocks = (int64_t)col_blocks * B;
-  return launch_kernel(dmod_finish_kernel, total_blocks, stream,
-                       (const float *)part_scale, (const float *)part_shift,
-                       dscale, dshift, D, (int32_t)plan.n_tiles, col_blocks,
-                       total_blocks);
+  return launch_kernel_threads(dmod_finish_kernel, total_blocks,
+                               kFinishWaves * kWave, stream, part_scale,
+                               part_shift, dscale, dshift, D, n_tiles,
+                               col_blocks, total_blocks);
 }
 
 }  // namespace adaln

@@ -33,6 +33,18 @@ struct DmodPlan {
   int n_tiles = 0;
 };
 
+// The fused backward: a workgroup of W wavefronts owns n_tile token rows of
+// one sample; each lane holds V vectors of a row.  ADALN_FUSED_V lists the
+// instantiated V.
+#define ADALN_FUSED_V(X) X(1) X(2) X(3) X(4)
+
+struct FusedPlan {
+  int V = 0;
+  int W = 0;
+  int n_tile = 0;
+  int n_tiles = 0;
+};
+
 // Grid-stride kernels take at most this many workgroups per launch.
 constexpr int64_t kMaxGrid = 1 << 20;
 
@@ -49,11 +61,26 @@ inline hipError_t launch_kernel(void (*k)(P...), int64_t blocks,
   return hipLaunchKernel((const void *)k, dim3(grid), dim3(256), argv, 0, s);
 }
 
+// As launch_kernel, with `threads` threads per workgroup.
+template <typename... P, typename... A>
+inline hipError_t launch_kernel_threads(void (*k)(P...), int64_t blocks,
+                                        int threads, hipStream_t s,
+                                        A... args) {
+  static_assert(std::is_same<std::tuple<P...>, std::tuple<A...>>::value,
+                "kernel arguments must match the kernel's parameter types");
+  if (blocks <= 0) return hipSuccess;
+  const unsigned grid = (unsigned)(blocks < kMaxGrid ? blocks : kMaxGrid);
+  void *argv[] = {(void *)&args...};
+  return hipLaunchKernel((const void *)k, dim3(grid), dim3(threads), argv, 0,
+                         s);
+}
+
 // Returns false if no instantiation holds a row of nvec vectors.
 bool choose_row_plan(int64_t nvec, RowPlan *plan);
 int64_t max_row_vectors();
 
 DmodPlan choose_dmod_plan(int64_t B, int64_t N, int64_t nvec);
+bool choose_fused_plan(int64_t B, int64_t N, int64_t nvec, FusedPlan *plan);
 
 // Launchers: enqueue on `stream`, return hipGetLastError() of the launch.
 hipError_t launch_fwd(int dtype, const RowPlan &plan, const void *x,
@@ -66,10 +93,25 @@ hipError_t launch_bwd_dx(int dtype, const RowPlan &plan, const void *dy,
                          const float *rstd, void *dx, int64_t rows, int32_t N,
                          int32_t D, hipStream_t stream);
 
-hipError_t launch_dmod(int dtype, const DmodPlan &plan, const void *dy,
-                       const void *x, const float *mean, const float *rstd,
-                       float *part_scale, float *part_shift, float *dscale,
-                       float *dshift, int32_t B, int32_t N, int32_t D,
-                       hipStream_t stream);
+// D-tile partial sums only (no finish).
+hipError_t launch_dmod_partial(int dtype, const DmodPlan &plan,
+                               const void *dy, const void *x,
+                               const float *mean, const float *rstd,
+                               float *part_scale, float *part_shift,
+                               int32_t B, int32_t N, int32_t D,
+                               hipStream_t stream);
+
+// dscale/dshift = sums over n_tiles of [B, n_tiles, D] partials, in index
+// order (zero when n_tiles == 0).
+hipError_t launch_dmod_finish(const float *part_scale,
+                              const float *part_shift, float *dscale,
+                              float *dshift, int32_t B, int32_t D,
+                              int32_t n_tiles, hipStream_t stream);
+
+hipError_t launch_bwd_fused(int dtype, const FusedPlan &plan, const void *dy,
+                            const void *x, const void *scale,
+                            const float *mean, const float *rstd, void *dx,
+                            float *part_scale, float *part_shift, int32_t B,
+                            int32_t N, int32_t D, hipStream_t stream);
 
 }  // namespace adaln

@@ -83,7 +83,7 @@ __global__ __launch_bounds__(kBlock) void fwd_kernel(
     for (int k = 0; k < V; ++k) {
       const int j = (k * W + wig) * kWave + lane;
       ok[k] = live && j < nvec;
-      xv[k] = ok[k] ? load_vec(x + off + (int64_t)j * E) : vzero();
+      xv[k] = ok[k] ? load_stream(x + off + (int64_t)j * E) : vzero();
     }
 
     float sum = 0.f;
@@ -129,7 +129,7 @@ __global__ __launch_bounds__(kBlock) void fwd_kernel(
           const float xh = (elem<T>(xv[k], e) - mu) * r;
           o[e] = fmaf(xh, 1.0f + elem<T>(sv, e), elem<T>(hv, e));
         }
-        store_vec(y + off + c, pack<T>(o));
+        store_stream(y + off + c, pack<T>(o));
       }
     }
   }
@@ -165,8 +165,8 @@ __global__ __launch_bounds__(kBlock) void dx_kernel(
     for (int k = 0; k < V; ++k) {
       const int j = (k * W + wig) * kWave + lane;
       ok[k] = live && j < nvec;
-      xv[k] = ok[k] ? load_vec(x + off + (int64_t)j * E) : vzero();
-      gv[k] = ok[k] ? load_vec(dy + off + (int64_t)j * E) : vzero();
+      xv[k] = ok[k] ? load_stream(x + off + (int64_t)j * E) : vzero();
+      gv[k] = ok[k] ? load_stream(dy + off + (int64_t)j * E) : vzero();
     }
 #pragma unroll
     for (int k = 0; k < V; ++k) {
@@ -210,7 +210,7 @@ __global__ __launch_bounds__(kBlock) void dx_kernel(
           const float g = elem<T>(gv[k], e) * (1.0f + elem<T>(sv[k], e));
           o[e] = r * fmaf(-xh, c2, g - c1);
         }
-        store_vec(dx + off + c, pack<T>(o));
+        store_stream(dx + off + c, pack<T>(o));
       }
     }
   }

@@ -9,6 +9,7 @@ current torch stream of that device unless ``stream`` is given.
 
 from __future__ import annotations
 
+import ctypes
 from typing import Optional, Tuple
 
 import torch
@@ -150,6 +151,52 @@ def bwd(dy: torch.Tensor, x: torch.Tensor, scale: torch.Tensor,
     return dx, dscale, dshift
 
 
+def bwd_fused(dy, x, scale, mean, rstd, *, dx=None, workspace=None,
+              stream=None):
+    """First launch of :func:`bwd`: dx plus dscale/dshift partial sums in
+    the workspace.  Returns (dx, workspace); pass the workspace to
+    :func:`bwd_finish`."""
+    B, N, D, dev, dt = _bwd_common(dy, x, scale, mean, rstd)
+    if dx is None:
+        dx = torch.empty_like(x)
+    _check(dx, "dx", (B, N, D), dt, dev)
+    workspace, wbytes = _workspace(workspace, B, N, D, dt, dev)
+    lib = _lib.load()
+    with torch.cuda.device(dev):
+        rc = lib.adaln_bwd_fused(_ptr(dy), _ptr(x), _ptr(scale), _ptr(mean),
+                                 _ptr(rstd), _ptr(dx), _ptr(workspace),
+                                 wbytes, B, N, D, _code(x),
+                                 _stream(dev, stream))
+    _lib.check(rc, "adaln_bwd_fused")
+    return dx, workspace
+
+
+def bwd_finish(workspace, B: int, N: int, D: int, dtype: torch.dtype, *,
+               dscale=None, dshift=None, stream=None):
+    """Second launch of :func:`bwd`: dscale, dshift from the partial sums
+    that :func:`bwd_fused` left in ``workspace``."""
+    dev = workspace.device
+    if dscale is None:
+        dscale = torch.empty(B, D, dtype=torch.float32, device=dev)
+    if dshift is None:
+        dshift = torch.empty(B, D, dtype=torch.float32, device=dev)
+    _check(dscale, "dscale", (B, D), torch.float32, dev)
+    _check(dshift, "dshift", (B, D), torch.float32, dev)
+    if not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    code = _DTYPES.get(dtype)
+    if code is None:
+        raise TypeError(f"unsupported dtype {dtype}")
+    lib = _lib.load()
+    with torch.cuda.device(dev):
+        rc = lib.adaln_bwd_finish(_ptr(workspace),
+                                  workspace.numel() * workspace.element_size(),
+                                  _ptr(dscale), _ptr(dshift), B, N, D, code,
+                                  _stream(dev, stream))
+    _lib.check(rc, "adaln_bwd_finish")
+    return dscale, dshift
+
+
 def bwd_dx(dy, x, scale, mean, rstd, *, dx=None, stream=None):
     """Input gradient only (one launch); returns dx."""
     B, N, D, dev, dt = _bwd_common(dy, x, scale, mean, rstd)
@@ -184,6 +231,15 @@ def bwd_dmod(dy, x, mean, rstd, *, dscale=None, dshift=None, workspace=None,
                                 _stream(dev, stream))
     _lib.check(rc, "adaln_bwd_dmod")
     return dscale, dshift
+
+
+def bwd_fused_plan(B: int, N: int, D: int, dtype: torch.dtype) -> dict:
+    """Launch plan of :func:`bwd_fused` for this shape (host-only)."""
+    out = (ctypes.c_int64 * 4)()
+    rc = _lib.load().adaln_bwd_fused_plan(B, N, D, _DTYPES.get(dtype, -1),
+                                          out)
+    _lib.check(rc, "adaln_bwd_fused_plan")
+    return dict(V=out[0], W=out[1], n_tile=out[2], n_tiles=out[3])
 
 
 def bshape(S: int, m_mem: int, m_comp: int, p: int) -> int:

@@ -2,8 +2,8 @@
 """Benchmark of the fused AdaLN forward+backward on one MI355X.
 
 One step is the whole hot path over one batch of synthetic input already
-resident in HBM: adaln_fwd, then the backward pass (adaln_bwd_dx followed by
-adaln_bwd_dmod, exactly what adaln_bwd enqueues), on torch's current stream.
+resident in HBM: adaln_fwd, then the backward pass as adaln_bwd enqueues it
+(adaln_bwd_fused, then adaln_bwd_finish), on torch's current stream.
 W untimed warm-up steps run first; then exactly K steps are timed between two
 device synchronisations.  HIP events recorded on the same stream between the
 calls give each kernel's average duration inside the timed region.
@@ -63,11 +63,10 @@ def algorithmic_bytes(B, N, D, esize, n_tiles):
     return {
         # read x, scale, shift; write y, mean, rstd
         "fwd": 2 * act + 2 * mod + 2 * stats,
-        # read dy, x, scale, mean, rstd; write dx
-        "bwd_dx": 3 * act + mod + 2 * stats,
-        # read dy, x, mean, rstd; write then read the partials; write
-        # dscale, dshift
-        "bwd_dmod": 2 * act + 2 * stats + 2 * part + 2 * B * D * 4,
+        # read dy, x, scale, mean, rstd; write dx and the partial sums
+        "bwd_fused": 3 * act + mod + 2 * stats + part,
+        # read the partial sums; write dscale, dshift
+        "bwd_finish": part + 2 * B * D * 4,
     }
 
 
@@ -201,7 +200,7 @@ def main(argv=None) -> int:
     dshift = torch.empty(B, D, dtype=torch.float32, device=dev)
     wbytes = A.bwd_workspace_bytes(B, N, D, dt)
     ws = torch.empty(max(wbytes, 1), dtype=torch.uint8, device=dev)
-    n_tiles = wbytes // (2 * 4 * B * D) if B * D else 0
+    n_tiles = A.bwd_fused_plan(B, N, D, dt)["n_tiles"]
     stream = torch.cuda.current_stream(dev)
 
     def step(ev=None):
@@ -210,11 +209,12 @@ def main(argv=None) -> int:
         A.fwd(x, scale, shift, y=y, mean=mean, rstd=rstd, stream=stream)
         if ev is not None:
             ev[1].record(stream)
-        A.bwd_dx(dy, x, scale, mean, rstd, dx=dx, stream=stream)
+        A.bwd_fused(dy, x, scale, mean, rstd, dx=dx, workspace=ws,
+                    stream=stream)
         if ev is not None:
             ev[2].record(stream)
-        A.bwd_dmod(dy, x, mean, rstd, dscale=dscale, dshift=dshift,
-                   workspace=ws, stream=stream)
+        A.bwd_finish(ws, B, N, D, dt, dscale=dscale, dshift=dshift,
+                     stream=stream)
         if ev is not None:
             ev[3].record(stream)
 
@@ -233,7 +233,7 @@ def main(argv=None) -> int:
     elapsed = time.perf_counter() - t0
     ms_step = 1e3 * elapsed / args.steps
 
-    names = ("fwd", "bwd_dx", "bwd_dmod")
+    names = ("fwd", "bwd_fused", "bwd_finish")
     avg_ms = {n: sum(ev[i].elapsed_time(ev[i + 1]) for ev in events)
               / args.steps for i, n in enumerate(names)}
     byts = algorithmic_bytes(B, N, D, esize, n_tiles)
@@ -245,7 +245,7 @@ def main(argv=None) -> int:
     gbps = step_bytes / (ms_step * 1e-3) / 1e9
     tokens_s = B * N / (ms_step * 1e-3)
 
-    dom = max(("fwd", "bwd_dx"), key=lambda n: avg_ms[n])
+    dom = max(names, key=lambda n: avg_ms[n])
     src_hash = kernel_source_hash()
     achieved = byts[dom] / (avg_ms[dom] * 1e-3) / 1e9
     roofline = {

@@ -62,7 +62,7 @@ extern "C" {
                                       or a pointer not 16-byte aligned */
 #define ADALN_ERR_WORKSPACE (-4)   /* workspace NULL or too small */
 #define ADALN_ERR_HIP (-5)         /* the HIP runtime reported an error */
-#define ADALN_ERR_UNSUPPORTED (-6) /* D above adaln_max_d(dtype) */
+#define ADALN_ERR_UNSUPPORTED (-6) /* D too wide for the entry point */
 
 /*
  * Forward pass: mean, rstd and y for every token row, one kernel launch.
@@ -82,15 +82,17 @@ int adaln_fwd(const void *x, const void *scale, const void *shift, void *y,
               int dtype, void *stream);
 
 /*
- * Bytes of device workspace adaln_bwd and adaln_bwd_dmod need for this
- * shape: the per-(sample, n_tile) partial sums of the D-tile reduction.
+ * Bytes of device workspace the backward entry points (adaln_bwd,
+ * adaln_bwd_fused, adaln_bwd_finish, adaln_bwd_dmod) need for this shape:
+ * the per-(sample, n_tile) partial sums of the D-tile reduction.
  * A pure function of its arguments.  Returns 0 for invalid arguments.
  */
 size_t adaln_bwd_workspace_bytes(int64_t B, int64_t N, int64_t D, int dtype);
 
 /*
- * Backward pass: dx, dscale and dshift.  Equivalent to adaln_bwd_dx followed
- * by adaln_bwd_dmod on the same stream.
+ * Backward pass: dx, dscale and dshift.  For rows of at most 2048 vectors it
+ * enqueues adaln_bwd_fused then adaln_bwd_finish (x and dy read once); for
+ * wider rows, adaln_bwd_dx then adaln_bwd_dmod.
  *   dy        [B,N,D] dtype in   upstream gradient dL/dy
  *   x         [B,N,D] dtype in   the forward input
  *   scale     [B,D]   dtype in
@@ -106,6 +108,38 @@ int adaln_bwd(const void *dy, const void *x, const void *scale,
               const float *mean, const float *rstd, void *dx, float *dscale,
               float *dshift, void *workspace, size_t workspace_bytes,
               int64_t B, int64_t N, int64_t D, int dtype, void *stream);
+
+/*
+ * The two launches adaln_bwd makes for rows of at most 2048 vectors
+ * (D <= 16384 bf16 / 8192 f32), exposed so callers can schedule or time them
+ * separately.  adaln_bwd_fused reads x and dy once: it writes dx and, per
+ * (sample, n_tile), float32 partial sums of dscale and dshift into the
+ * workspace -- the D-tile coalesced reduction of section 2.B with dx fused
+ * into the same pass over the rows.  adaln_bwd_finish then sums those
+ * partials over the n_tiles in index order into dscale and dshift.  The
+ * workspace must be the one adaln_bwd_fused filled for the same B, N, D and
+ * dtype, with no other call using it in between.  Both return
+ * ADALN_ERR_UNSUPPORTED for wider rows (adaln_bwd handles those).
+ */
+int adaln_bwd_fused(const void *dy, const void *x, const void *scale,
+                    const float *mean, const float *rstd, void *dx,
+                    void *workspace, size_t workspace_bytes, int64_t B,
+                    int64_t N, int64_t D, int dtype, void *stream);
+
+int adaln_bwd_finish(const void *workspace, size_t workspace_bytes,
+                     float *dscale, float *dshift, int64_t B, int64_t N,
+                     int64_t D, int dtype, void *stream);
+
+/*
+ * Launch plan of adaln_bwd_fused for this shape, for callers that account
+ * for the partial sums it writes: fills out[0..3] with {vectors per lane,
+ * wavefronts per workgroup, n_tile (token rows per workgroup), n_tiles}.
+ * The partials occupy 2*B*n_tiles*D floats at the start of the workspace.
+ * Returns ADALN_ERR_UNSUPPORTED for rows too wide for the fused kernel.
+ * Host-only; no HIP call.
+ */
+int adaln_bwd_fused_plan(int64_t B, int64_t N, int64_t D, int dtype,
+                         int64_t *out);
 
 /*
  * Backward, input gradient only: dx from dy, x, scale and the saved

@@ -185,9 +185,46 @@ def test_guard_bytes_untouched(A):
 
 
 def test_split_entry_points_match_bwd(A):
-    """adaln_bwd equals adaln_bwd_dx followed by adaln_bwd_dmod."""
+    """adaln_bwd is exactly adaln_bwd_fused followed by adaln_bwd_finish."""
     wl = W.custom(2, 700, 3072, "bf16", x_kind="offset", dy_std=1e-2)
-    _say("bwd == bwd_dx + bwd_dmod")
+    _say("bwd == bwd_fused + bwd_finish")
+    dev = P.to_device(synth.make_inputs(wl))
+    out = P.gpu_fwd_bwd(dev)
+    dx, ws = A.bwd_fused(dev["dy"], dev["x"], dev["scale"], out["mean"],
+                         out["rstd"])
+    ds, dh = A.bwd_finish(ws, 2, 700, 3072, torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(dx, out["dx"])
+    assert torch.equal(ds, out["dscale"]) and torch.equal(dh, out["dshift"])
+
+
+@pytest.mark.parametrize("wl", [synth.TINY_F32, synth.IMAGE_BUCKET,
+                                synth.VIDEO_BUCKET,
+                                W.custom(3, 77, 5120, "bf16", x_kind="outliers",
+                                         dy_std=1e-2),
+                                W.custom(2, 50, 520, "bf16")],
+                         ids=lambda w: w.name + f"_{w.D}")
+def test_unfused_entry_points(A, wl):
+    """adaln_bwd_dx and adaln_bwd_dmod (the separate dx kernel and the
+    D-tile reduction grid) against the oracle."""
+    _say(f"unfused bwd_dx + bwd_dmod on {wl.name} {wl.shape}")
+    inp = synth.make_inputs(wl)
+    dev = P.to_device(inp)
+    y, mean, rstd = A.fwd(dev["x"], dev["scale"], dev["shift"])
+    dx = A.bwd_dx(dev["dy"], dev["x"], dev["scale"], mean, rstd)
+    ds, dh = A.bwd_dmod(dev["dy"], dev["x"], mean, rstd)
+    torch.cuda.synchronize()
+    out = dict(y=y.cpu(), mean=mean.cpu(), rstd=rstd.cpu(), dx=dx.cpu(),
+               dscale=ds.cpu(), dshift=dh.cpu())
+    for r in P.compare_full(inp, out, wl.dtype):
+        _say(f"  {r}")
+
+
+def test_fused_unsupported_for_wide_rows(A):
+    """Rows wider than 2048 vectors have no fused plan; adaln_bwd falls back
+    to the unfused kernels and gives the same bits as calling them."""
+    wl = W.custom(1, 9, 32768, "bf16", dy_std=1e-2)
+    _say("wide rows: bwd falls back to bwd_dx + bwd_dmod")
     dev = P.to_device(synth.make_inputs(wl))
     out = P.gpu_fwd_bwd(dev)
     dx = A.bwd_dx(dev["dy"], dev["x"], dev["scale"], out["mean"], out["rstd"])
@@ -195,6 +232,9 @@ def test_split_entry_points_match_bwd(A):
     torch.cuda.synchronize()
     assert torch.equal(dx, out["dx"])
     assert torch.equal(ds, out["dscale"]) and torch.equal(dh, out["dshift"])
+    with pytest.raises(A.AdalnError):
+        A.bwd_fused(dev["dy"], dev["x"], dev["scale"], out["mean"],
+                    out["rstd"])
 
 
 def test_empty(A):
