@@ -6,7 +6,7 @@
 #include <stdio.h>
 #include <stdint.h>
 
-#include "../../include/adaln.h"
+#include "adaln.h"
 #include "launch.hpp"
 
 #define ADALN_API extern "C" __attribute__((visibility("default")))
@@ -90,10 +90,10 @@ size_t partial_bytes(int64_t n_tiles, int64_t B, int64_t D) {
 size_t workspace_bytes(int64_t B, int64_t N, int64_t D, int dtype) {
   const int64_t nvec = D / elems_per_vec(dtype);
   const DmodPlan dp = choose_dmod_plan(B, N, nvec);
-  FusedPlan fp;
+  StreamPlan sp;
   const size_t a = partial_bytes(dp.n_tiles, B, D);
-  const size_t b = choose_fused_plan(B, N, nvec, &fp)
-                       ? partial_bytes(fp.n_tiles, B, D)
+  const size_t b = choose_stream_plan(B, N, nvec, true, &sp)
+                       ? partial_bytes(sp.bps, B, D)
                        : 0;
   return a > b ? a : b;
 }
@@ -144,33 +144,63 @@ DmodPlan choose_dmod_plan(int64_t B, int64_t N, int64_t nvec) {
   return p;
 }
 
-// The fused backward.  V is the smallest number of vectors per lane (at most
-// 4) that lets at most 8 wavefronts hold a row: small V keeps the per-lane
-// accumulators (2*V*E floats) in registers.  Wider rows (more than 2048
-// vectors) have no fused plan and take the dx + D-tile kernels instead.  n_tile
-// aims at about ADALN_FUSED_TARGET_WAVES wavefronts over the whole grid and
-// is at least 16 rows, since each tile writes 8 bytes of partials per
-// feature.
-#ifndef ADALN_FUSED_TARGET_WAVES
-#define ADALN_FUSED_TARGET_WAVES 2048
-#endif
-
-bool choose_fused_plan(int64_t B, int64_t N, int64_t nvec, FusedPlan *plan) {
-  FusedPlan p;
-  for (int v = 1; v <= 4 && p.V == 0; ++v) {
-    const int64_t w = (nvec + 64 * v - 1) / (64 * v);
-    if (w <= 8) {
-      p.V = v;
-      p.W = (int)w;
-    }
+// Row-stream plans (rows of up to 1024 vectors for the forward, 640 for the
+// backward).  V is the smallest
+// instantiated count that holds the row.  The kernel's occupancy OCC fixes a
+// persistent grid of G = 256 * OCC workgroups (OCC per CU on a 256-CU
+// MI355X), spread over the samples: bps = max(1, G / B) workgroups per
+// sample, `groups` = G / bps samples in flight.  The plan depends only on the
+// shape, so the workspace size ([B, bps, D] partial sums of the backward) is
+// a pure function of it; on a part with another CU count the kernels remain
+// correct and only use the GPU less evenly.
+bool choose_stream_plan(int64_t B, int64_t N, int64_t nvec, bool bwd,
+                        StreamPlan *plan) {
+  StreamPlan p;
+#define ADALN_STREAM_PLAN_CASE(V_) \
+  if (p.V == 0 && 64 * V_ >= nvec) p.V = V_;
+  ADALN_STREAM_V(ADALN_STREAM_PLAN_CASE)
+#undef ADALN_STREAM_PLAN_CASE
+  if (p.V == 0 || (bwd && p.V > kMaxBwdStreamV)) return false;
+  if (B > 0 && N > 0) {
+    const int occ = bwd ? bwd_stream_occ(p.V) : fwd_stream_occ(p.V);
+    const int64_t G = (int64_t)kCUs * occ;
+    const int64_t bps = G / B > 1 ? G / B : 1;
+    const int64_t groups = G / bps;
+    p.bps = (int)bps;
+    p.groups = (int)groups;
+    p.grid = (int)(bps * (groups < B ? groups : B));
   }
+  *plan = p;
+  return true;
+}
+
+// Forward rows wider than 1024 vectors: W wavefronts share a row; the V (of
+// the instantiated ones) that wastes the fewest vector slots, the smallest
+// such V among equals.  Tiles: about two rounds of the workgroups 256 CUs
+// hold at the kernel's occupancy, spread over the samples.
+bool choose_tile_plan(int64_t B, int64_t N, int64_t nvec, TilePlan *plan) {
+  TilePlan p;
+  int64_t best_waste = -1;
+#define ADALN_FWD_PLAN_CASE(V_)                                        \
+  {                                                                    \
+    const int64_t w = (nvec + 64 * V_ - 1) / (64 * V_);                \
+    const int64_t waste = 64 * V_ * w - nvec;                          \
+    if (w <= kMaxRowWaves && (best_waste < 0 || waste < best_waste)) { \
+      best_waste = waste;                                              \
+      p.V = V_;                                                        \
+      p.W = (int)w;                                                    \
+    }                                                                  \
+  }
+  ADALN_FWD_V(ADALN_FWD_PLAN_CASE)
+#undef ADALN_FWD_PLAN_CASE
   if (p.V == 0) return false;
   if (B > 0 && N > 0) {
-    int64_t target_blocks = ADALN_FUSED_TARGET_WAVES / p.W;
-    if (target_blocks < 1) target_blocks = 1;
-    int64_t tiles_per_sample = (target_blocks + B - 1) / B;
+    int64_t per_cu = 4 * fwd_waves_per_simd(p.V) / p.W;
+    if (per_cu < 1) per_cu = 1;
+    const int64_t target = (int64_t)kCUs * per_cu * 2;
+    const int64_t tiles_per_sample = target > B ? (target + B - 1) / B : 1;
     int64_t n_tile = (N + tiles_per_sample - 1) / tiles_per_sample;
-    if (n_tile < 16) n_tile = 16;
+    if (n_tile < 2) n_tile = 2;
     p.n_tile = (int)n_tile;
     p.n_tiles = (int)((N + n_tile - 1) / n_tile);
   }
@@ -243,12 +273,21 @@ ADALN_API int adaln_fwd(const void *x, const void *scale, const void *shift,
   ADALN_TRY(check_ptr(mean, rows, "mean"));
   ADALN_TRY(check_ptr(rstd, rows, "rstd"));
   if (!rows) return ok();
-  RowPlan plan;
-  if (!choose_row_plan(D / elems_per_vec(dtype), &plan))
-    return fail(ADALN_ERR_UNSUPPORTED, "no row plan for D=%lld", (long long)D);
-  const hipError_t e =
-      launch_fwd(dtype, plan, x, scale, shift, y, mean, rstd, B * N,
-                 (int32_t)N, (int32_t)D, (hipStream_t)stream);
+  const int64_t nvec = D / elems_per_vec(dtype);
+  hipError_t e = hipSuccess;
+  StreamPlan sp;
+  TilePlan tp;
+  if (choose_stream_plan(B, N, nvec, false, &sp))
+    e = launch_fwd_stream(dtype, sp, x, scale, shift, y, mean, rstd,
+                          (int32_t)B, (int32_t)N, (int32_t)D,
+                          (hipStream_t)stream);
+  else if (choose_tile_plan(B, N, nvec, &tp))
+    e = launch_fwd_tiles(dtype, tp, x, scale, shift, y, mean, rstd,
+                         (int32_t)B, (int32_t)N, (int32_t)D,
+                         (hipStream_t)stream);
+  else
+    return fail(ADALN_ERR_UNSUPPORTED, "no forward plan for D=%lld",
+                (long long)D);
   if (e != hipSuccess) return hip_fail(e, "adaln_fwd launch");
   return ok();
 }
@@ -340,15 +379,15 @@ ADALN_API int adaln_bwd_fused(const void *dy, const void *x, const void *scale,
   ADALN_TRY(check_ptr(mean, rows, "mean"));
   ADALN_TRY(check_ptr(rstd, rows, "rstd"));
   ADALN_TRY(check_ptr(dx, rows, "dx"));
-  FusedPlan plan;
-  if (!choose_fused_plan(B, N, D / elems_per_vec(dtype), &plan))
+  StreamPlan plan;
+  if (!choose_stream_plan(B, N, D / elems_per_vec(dtype), true, &plan))
     return fail(ADALN_ERR_UNSUPPORTED,
                 "D=%lld is too wide for the fused backward", (long long)D);
   ADALN_TRY(check_workspace(workspace, workspace_bytes_given,
                             workspace_bytes(B, N, D, dtype)));
   if (!rows) return ok();
   float *part_scale = static_cast<float *>(workspace);
-  float *part_shift = part_scale + (size_t)B * plan.n_tiles * D;
+  float *part_shift = part_scale + (size_t)B * plan.bps * D;
   const hipError_t e = launch_bwd_fused(
       dtype, plan, dy, x, scale, mean, rstd, dx, part_scale, part_shift,
       (int32_t)B, (int32_t)N, (int32_t)D, (hipStream_t)stream);
@@ -360,14 +399,14 @@ ADALN_API int adaln_bwd_fused_plan(int64_t B, int64_t N, int64_t D,
                                    int dtype, int64_t *out) {
   ADALN_TRY(check_shape(B, N, D, dtype));
   if (out == nullptr) return fail(ADALN_ERR_INVALID, "out is NULL");
-  FusedPlan plan;
-  if (!choose_fused_plan(B, N, D / elems_per_vec(dtype), &plan))
+  StreamPlan plan;
+  if (!choose_stream_plan(B, N, D / elems_per_vec(dtype), true, &plan))
     return fail(ADALN_ERR_UNSUPPORTED,
                 "D=%lld is too wide for the fused backward", (long long)D);
   out[0] = plan.V;
-  out[1] = plan.W;
-  out[2] = plan.n_tile;
-  out[3] = plan.n_tiles;
+  out[1] = 1;
+  out[2] = plan.grid;
+  out[3] = plan.bps;
   return ok();
 }
 
@@ -378,8 +417,8 @@ ADALN_API int adaln_bwd_finish(const void *workspace,
   ADALN_TRY(check_shape(B, N, D, dtype));
   ADALN_TRY(check_ptr(dscale, B > 0, "dscale"));
   ADALN_TRY(check_ptr(dshift, B > 0, "dshift"));
-  FusedPlan plan;
-  if (!choose_fused_plan(B, N, D / elems_per_vec(dtype), &plan))
+  StreamPlan plan;
+  if (!choose_stream_plan(B, N, D / elems_per_vec(dtype), true, &plan))
     return fail(ADALN_ERR_UNSUPPORTED,
                 "D=%lld is too wide for the fused backward", (long long)D);
   ADALN_TRY(check_workspace(workspace, workspace_bytes_given,
@@ -387,11 +426,10 @@ ADALN_API int adaln_bwd_finish(const void *workspace,
   if (B == 0) return ok();
   const float *part_scale = static_cast<const float *>(workspace);
   const float *part_shift =
-      plan.n_tiles > 0 ? part_scale + (size_t)B * plan.n_tiles * D : nullptr;
+      plan.bps > 0 ? part_scale + (size_t)B * plan.bps * D : nullptr;
   const hipError_t e =
       launch_dmod_finish(part_scale, part_shift, dscale, dshift, (int32_t)B,
-                         (int32_t)D, (int32_t)plan.n_tiles,
-                         (hipStream_t)stream);
+                         (int32_t)D, (int32_t)plan.bps, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "adaln_bwd_finish launch");
   return ok();
 }
@@ -414,8 +452,8 @@ ADALN_API int adaln_bwd(const void *dy, const void *x, const void *scale,
   ADALN_TRY(check_ptr(dshift, B > 0, "dshift"));
   ADALN_TRY(check_workspace(workspace, workspace_bytes_given,
                             workspace_bytes(B, N, D, dtype)));
-  FusedPlan plan;
-  if (choose_fused_plan(B, N, D / elems_per_vec(dtype), &plan)) {
+  StreamPlan plan;
+  if (choose_stream_plan(B, N, D / elems_per_vec(dtype), true, &plan)) {
     ADALN_TRY(adaln_bwd_fused(dy, x, scale, mean, rstd, dx, workspace,
                               workspace_bytes_given, B, N, D, dtype, stream));
     return adaln_bwd_finish(workspace, workspace_bytes_given, dscale, dshift,

@@ -1,61 +1,61 @@
 // Fused backward of the AdaLN operator: dx and the D-tile partial sums of
-// dscale/dshift in one pass over x and dy.
+// dscale/dshift in one pass over x and dy (rows of up to 640 16-byte
+// vectors; wider rows use the separate dx and D-tile kernels).
 //
 // The D-tile coalesced reduction of the AdaptiveLoad technical summary
 // (section 2.B, backward pass) pins each thread to a feature and accumulates
-// down the token rows of a sequence tile.  dx needs every feature of a row
-// for its two row sums, so here one workgroup owns an n_tile of token rows of
-// one sample and all D features: its W wavefronts each own one d_tile of
-// 64*V vectors (lane l holds vectors (k*W + w)*64 + l, k < V), so each
-// wavefront is one (d_tile, n_tile) cell of the grid.  Per row the wavefronts
-// reduce sum(g) and sum(g*xhat) with DPP, combine through LDS (one barrier),
-// write dx, and add dy*xhat and dy into per-lane float32 accumulators that
-// stay in registers down the whole tile.  The next row is loaded before the
-// current one is reduced.  x and dy are read once instead of twice, which
-// cuts the backward pass from five tensor passes to three.
+// down the token rows of a sequence tile, so that every access of a
+// wavefront is contiguous along D.  Here each wavefront owns whole rows (lane
+// l holds vectors k*64 + l, k < V), which it needs anyway for the two row
+// sums of dx, and keeps one float32 accumulator of dy*xhat and one of dy per
+// feature it holds: its lanes are pinned to their features for every row it
+// visits, and each of its loads covers 1 KiB of contiguous memory.
 //
-// Partials go to the workspace as [B, n_tiles, D] for dscale and for dshift
-// and are summed over n_tiles in index order by dmod_finish_kernel.
+// Grid: as in the forward stream kernel, a small persistent grid (OCC
+// four-wavefront workgroups per CU) is spread over the samples, bps
+// workgroups per sample, and each wavefront walks its sample's rows with a
+// stride of 4*bps rows, so the active wavefronts sweep a narrow window of
+// memory in order.  The set of rows a workgroup visits in one sample is its
+// sequence tile.  At the end of a sample the four wavefronts' accumulators
+// are added in wavefront order through LDS and written as one partial row
+// per (sample, workgroup): the workspace holds [B, bps, D] partial sums for
+// dscale and for dshift, which dmod_finish_kernel adds over the bps
+// workgroups in index order.  No floating-point atomics anywhere.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace adaln {
 
-constexpr int kMaxWaves = 8;  // 512 threads
-
-template <typename T, int V>
-__global__ __launch_bounds__(kMaxWaves * kWave) void bwd_fused_kernel(
+template <typename T, int V, bool FULL, int PF, int OCC>
+__global__ __launch_bounds__(kBlock)
+__attribute__((amdgpu_waves_per_eu(OCC, OCC))) void bwd_stream_kernel(
     const T *__restrict__ dy, const T *__restrict__ x,
     const T *__restrict__ scale, const float *__restrict__ mean,
     const float *__restrict__ rstd, T *__restrict__ dx,
     float *__restrict__ part_scale, float *__restrict__ part_shift,
-    int32_t N, int32_t D, int32_t n_tile, int32_t n_tiles,
-    int32_t total_tiles) {
+    int32_t B, int32_t N, int32_t D, int32_t bps, int32_t groups) {
   constexpr int E = Elems<T>::value;
-  __shared__ float red[2][2][kMaxWaves];  // [parity][sum][wave]
+  constexpr int kWaves = kBlock / kWave;
+  extern __shared__ float stage[];  // one wavefront's accumulators
   const int lane = lane_id();
   const int wave = wave_id();
-  const int W = __builtin_amdgcn_readfirstlane(blockDim.x / kWave);
   const int nvec = D / E;
   const float inv_d = 1.0f / (float)D;
+  const int slot = blockIdx.x / bps;
+  const int k_in = blockIdx.x - slot * bps;
+  if (slot >= groups) return;  // whole workgroup, before any barrier
+  const int stride = bps * kWaves;
 
   int jv[V];
   bool ok[V];
 #pragma unroll
   for (int k = 0; k < V; ++k) {
-    jv[k] = (k * W + wave) * kWave + lane;
-    ok[k] = jv[k] < nvec;
+    jv[k] = k * kWave + lane;
+    ok[k] = FULL || jv[k] < nvec;
   }
-  int parity = 0;
 
-  for (int tile = blockIdx.x; tile < total_tiles; tile += gridDim.x) {
-    const int b = tile / n_tiles;
-    const int t = tile - b * n_tiles;
-    const int n0 = t * n_tile;
-    const int n1 = min(N, n0 + n_tile);
+  for (int b = slot; b < B; b += groups) {
     const int64_t row0 = (int64_t)b * N;
-
-    // 1 + scale for this sample, held for the whole tile
     Vec sv[V];
 #pragma unroll
     for (int k = 0; k < V; ++k)
@@ -68,63 +68,38 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void bwd_fused_kernel(
 #pragma unroll
       for (int e = 0; e < E; ++e) acc_s[k][e] = acc_h[k][e] = 0.f;
 
-    // prefetch the first row
-    Vec xa[V], ga[V];
-    {
-      const int64_t off = (row0 + n0) * D;
+    auto load_row = [&](Vec (&xv)[V], Vec (&gv)[V], float (&st)[2], int n) {
+      st[0] = mean[row0 + n];
+      st[1] = rstd[row0 + n];
+      const int64_t off = (row0 + n) * D;
 #pragma unroll
       for (int k = 0; k < V; ++k) {
-        xa[k] = ok[k] ? load_stream(x + off + (int64_t)jv[k] * E) : vzero();
-        ga[k] = ok[k] ? load_stream(dy + off + (int64_t)jv[k] * E) : vzero();
+        xv[k] = ok[k] ? load_stream(x + off + (int64_t)jv[k] * E) : vzero();
+        gv[k] = ok[k] ? load_stream(dy + off + (int64_t)jv[k] * E) : vzero();
       }
-    }
-    float mu = mean[row0 + n0];
-    float r = rstd[row0 + n0];
+    };
 
-    for (int n = n0; n < n1; ++n) {
-      // issue the next row's loads before touching this one
-      const bool more = n + 1 < n1;
-      const int64_t noff = (row0 + (more ? n + 1 : n)) * D;
-      Vec xb[V], gb[V];
-#pragma unroll
-      for (int k = 0; k < V; ++k) {
-        xb[k] = (more && ok[k]) ? load_stream(x + noff + (int64_t)jv[k] * E)
-                                : vzero();
-        gb[k] = (more && ok[k]) ? load_stream(dy + noff + (int64_t)jv[k] * E)
-                                : vzero();
-      }
-      const float mu_n = more ? mean[row0 + n + 1] : 0.f;
-      const float r_n = more ? rstd[row0 + n + 1] : 0.f;
-
+    auto do_row = [&](Vec (&xv)[V], Vec (&gv)[V], const float (&st)[2],
+                      int n) {
+      const float mu = st[0];
+      const float r = st[1];
       // row sums of g = dy * (1 + scale) and g * xhat
       float s1 = 0.f, s2 = 0.f;
 #pragma unroll
       for (int k = 0; k < V; ++k) {
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-          const float xh = (elem<T>(xa[k], e) - mu) * r;
-          const float g = elem<T>(ga[k], e) * (1.0f + elem<T>(sv[k], e));
+          const float xh = (elem<T>(xv[k], e) - mu) * r;
+          const float g = elem<T>(gv[k], e) * (1.0f + elem<T>(sv[k], e));
           s1 += g;
           s2 = fmaf(g, xh, s2);
         }
       }
       wave_sum2(s1, s2);
-      if (lane == 0) {
-        red[parity][0][wave] = s1;
-        red[parity][1][wave] = s2;
-      }
-      __syncthreads();
-      float t1 = red[parity][0][0], t2 = red[parity][1][0];
-      for (int w = 1; w < W; ++w) {
-        t1 += red[parity][0][w];
-        t2 += red[parity][1][w];
-      }
-      parity ^= 1;
-      const float c1 = t1 * inv_d;
-      const float c2 = t2 * inv_d;
-
+      const float c1 = s1 * inv_d;
+      const float c2 = s2 * inv_d;
 #pragma unroll
-      for (int k = 0; k < V; ++k) opaque(xa[k]), opaque(ga[k]);
+      for (int k = 0; k < V; ++k) opaque(xv[k]), opaque(gv[k]);
 
       const int64_t off = (row0 + n) * D;
 #pragma unroll
@@ -133,8 +108,8 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void bwd_fused_kernel(
           float o[E];
 #pragma unroll
           for (int e = 0; e < E; ++e) {
-            const float xh = (elem<T>(xa[k], e) - mu) * r;
-            const float gy = elem<T>(ga[k], e);
+            const float xh = (elem<T>(xv[k], e) - mu) * r;
+            const float gy = elem<T>(gv[k], e);
             const float g = gy * (1.0f + elem<T>(sv[k], e));
             o[e] = r * fmaf(-xh, c2, g - c1);
             acc_s[k][e] = fmaf(gy, xh, acc_s[k][e]);
@@ -143,29 +118,78 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void bwd_fused_kernel(
           store_stream(dx + off + (int64_t)jv[k] * E, pack<T>(o));
         }
       }
+    };
 
-#pragma unroll
-      for (int k = 0; k < V; ++k) {
-        xa[k] = xb[k];
-        ga[k] = gb[k];
+    int n = k_in * kWaves + wave;
+    if constexpr (PF == 1) {
+      for (; n < N; n += stride) {
+        Vec xv[V], gv[V];
+        float st[2];
+        load_row(xv, gv, st, n);
+        do_row(xv, gv, st, n);
       }
-      mu = mu_n;
-      r = r_n;
+    } else if (n < N) {
+      // the wavefront's next row is in flight while one is processed; in the
+      // loop body every load is unconditional
+      Vec xa[V], ga[V], xb[V], gb[V];
+      float sa[2], sb[2];
+      load_row(xa, ga, sa, n);
+      for (; n + 2 * stride < N; n += 2 * stride) {
+        load_row(xb, gb, sb, n + stride);
+        do_row(xa, ga, sa, n);
+        load_row(xa, ga, sa, n + 2 * stride);
+        do_row(xb, gb, sb, n + stride);
+      }
+      if (n + stride < N) {
+        load_row(xb, gb, sb, n + stride);
+        do_row(xa, ga, sa, n);
+        do_row(xb, gb, sb, n + stride);
+      } else {
+        do_row(xa, ga, sa, n);
+      }
     }
 
-    const int64_t po = ((int64_t)b * n_tiles + t) * D;
+    // Add the four wavefronts' accumulators in wavefront order: wavefront w
+    // (w = 1, 2, 3) stages its values, wavefront 0 adds them.  Lane-major
+    // layout [value][lane] keeps the LDS accesses conflict-free.
+#pragma unroll 1
+    for (int w = 1; w < kWaves; ++w) {
+      __syncthreads();
+      if (wave == w) {
 #pragma unroll
-    for (int k = 0; k < V; ++k) {
-      if (ok[k]) {
-        const int64_t c = po + (int64_t)jv[k] * E;
+        for (int k = 0; k < V; ++k)
 #pragma unroll
-        for (int q = 0; q < E / 4; ++q) {
-          *reinterpret_cast<float4 *>(part_scale + c + 4 * q) =
-              make_float4(acc_s[k][4 * q], acc_s[k][4 * q + 1],
-                          acc_s[k][4 * q + 2], acc_s[k][4 * q + 3]);
-          *reinterpret_cast<float4 *>(part_shift + c + 4 * q) =
-              make_float4(acc_h[k][4 * q], acc_h[k][4 * q + 1],
-                          acc_h[k][4 * q + 2], acc_h[k][4 * q + 3]);
+          for (int e = 0; e < E; ++e) {
+            stage[((k * E + e) * 2 + 0) * kWave + lane] = acc_s[k][e];
+            stage[((k * E + e) * 2 + 1) * kWave + lane] = acc_h[k][e];
+          }
+      }
+      __syncthreads();
+      if (wave == 0) {
+#pragma unroll
+        for (int k = 0; k < V; ++k)
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            acc_s[k][e] += stage[((k * E + e) * 2 + 0) * kWave + lane];
+            acc_h[k][e] += stage[((k * E + e) * 2 + 1) * kWave + lane];
+          }
+      }
+    }
+    if (wave == 0) {
+      const int64_t po = ((int64_t)b * bps + k_in) * D;
+#pragma unroll
+      for (int k = 0; k < V; ++k) {
+        if (ok[k]) {
+          const int64_t c = po + (int64_t)jv[k] * E;
+#pragma unroll
+          for (int q = 0; q < E / 4; ++q) {
+            *reinterpret_cast<float4 *>(part_scale + c + 4 * q) =
+                make_float4(acc_s[k][4 * q], acc_s[k][4 * q + 1],
+                            acc_s[k][4 * q + 2], acc_s[k][4 * q + 3]);
+            *reinterpret_cast<float4 *>(part_shift + c + 4 * q) =
+                make_float4(acc_h[k][4 * q], acc_h[k][4 * q + 1],
+                            acc_h[k][4 * q + 2], acc_h[k][4 * q + 3]);
+          }
         }
       }
     }
@@ -174,35 +198,50 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void bwd_fused_kernel(
 
 namespace {
 
-template <typename T, int V>
-hipError_t fused_v(const FusedPlan &plan, const void *dy, const void *x,
-                   const void *scale, const float *mean, const float *rstd,
-                   void *dx, float *part_scale, float *part_shift, int32_t B,
-                   int32_t N, int32_t D, hipStream_t s) {
-  const int32_t total = B * plan.n_tiles;
-  return launch_kernel_threads(
-      bwd_fused_kernel<T, V>, total, plan.W * kWave, s, (const T *)dy,
-      (const T *)x, (const T *)scale, mean, rstd, (T *)dx, part_scale,
-      part_shift, N, D, (int32_t)plan.n_tile, (int32_t)plan.n_tiles, total);
+template <typename T, int V, bool FULL>
+hipError_t bwd_stream_v(const StreamPlan &plan, const void *dy, const void *x,
+                        const void *scale, const float *mean,
+                        const float *rstd, void *dx, float *part_scale,
+                        float *part_shift, int32_t B, int32_t N, int32_t D,
+                        hipStream_t s) {
+  constexpr int E = Elems<T>::value;
+  const size_t lds = (size_t)V * E * 2 * kWave * sizeof(float);
+  return launch_kernel_lds(
+      bwd_stream_kernel<T, V, FULL, bwd_stream_pf(V), bwd_stream_occ(V)>,
+      plan.grid, kBlock, lds, s, (const T *)dy, (const T *)x,
+      (const T *)scale, mean, rstd, (T *)dx, part_scale, part_shift, B, N, D,
+      (int32_t)plan.bps, (int32_t)plan.groups);
 }
 
 }  // namespace
 
-#define ADALN_FUSED_CASE(V_)                                                 \
-  if (plan.V == V_)                                                          \
-    return dtype == 1                                                        \
-               ? fused_v<bf16, V_>(plan, dy, x, scale, mean, rstd, dx,       \
-                                   part_scale, part_shift, B, N, D, stream) \
-               : fused_v<float, V_>(plan, dy, x, scale, mean, rstd, dx,      \
-                                    part_scale, part_shift, B, N, D, stream);
+#define ADALN_BWD_STREAM_CASE(V_)                                              \
+  if (plan.V == V_) {                                                          \
+    if (full)                                                                  \
+      return dtype == 1                                                        \
+                 ? bwd_stream_v<bf16, V_, true>(plan, dy, x, scale, mean,      \
+                                                rstd, dx, part_scale,          \
+                                                part_shift, B, N, D, stream)   \
+                 : bwd_stream_v<float, V_, true>(plan, dy, x, scale, mean,     \
+                                                 rstd, dx, part_scale,         \
+                                                 part_shift, B, N, D, stream); \
+    return dtype == 1                                                          \
+               ? bwd_stream_v<bf16, V_, false>(plan, dy, x, scale, mean, rstd, \
+                                               dx, part_scale, part_shift, B,  \
+                                               N, D, stream)                   \
+               : bwd_stream_v<float, V_, false>(plan, dy, x, scale, mean,      \
+                                                rstd, dx, part_scale,          \
+                                                part_shift, B, N, D, stream);  \
+  }
 
-hipError_t launch_bwd_fused(int dtype, const FusedPlan &plan, const void *dy,
+hipError_t launch_bwd_fused(int dtype, const StreamPlan &plan, const void *dy,
                             const void *x, const void *scale,
                             const float *mean, const float *rstd, void *dx,
                             float *part_scale, float *part_shift, int32_t B,
                             int32_t N, int32_t D, hipStream_t stream) {
-  if (plan.W < 1 || plan.W > kMaxWaves) return hipErrorInvalidValue;
-  ADALN_FUSED_V(ADALN_FUSED_CASE)
+  const int E = dtype == 1 ? 8 : 4;
+  const bool full = (int64_t)plan.V * kWave * E == D;
+  ADALN_BWD_STREAM_V(ADALN_BWD_STREAM_CASE)
   return hipErrorInvalidValue;
 }
 

@@ -33,17 +33,84 @@ struct DmodPlan {
   int n_tiles = 0;
 };
 
-// The fused backward: a workgroup of W wavefronts owns n_tile token rows of
-// one sample; each lane holds V vectors of a row.  ADALN_FUSED_V lists the
-// instantiated V.
-#define ADALN_FUSED_V(X) X(1) X(2) X(3) X(4)
+// Row-stream kernels (the forward and the fused backward for rows of up to
+// 1024 vectors): one wavefront per row, lane l holding vectors k*64 + l,
+// k < V.  A persistent grid of `grid` four-wavefront workgroups: the samples
+// are processed `groups` at a time, with `bps` workgroups per sample, and
+// each wavefront walks its sample's rows with a stride of 4*bps.
+struct StreamPlan {
+  int V = 0;
+  int grid = 0;
+  int bps = 0;     // workgroups per sample (partial rows per sample)
+  int groups = 0;  // samples in flight
+};
 
-struct FusedPlan {
+#define ADALN_STREAM_V(X) X(1) X(2) X(3) X(4) X(5) X(6) X(8) X(10) X(12) X(16)
+#define ADALN_BWD_STREAM_V(X) X(1) X(2) X(3) X(4) X(5) X(6) X(8) X(10)
+constexpr int kMaxStreamVectors = 16 * 64;
+
+// Rows in flight per wavefront (PF) and waves per SIMD (OCC) of each stream
+// kernel instantiation.  OCC also fixes the grid: OCC workgroups per CU.
+// Short rows get two rows in flight and two workgroups per CU to keep enough
+// bytes in flight; long rows get the whole register file of one wavefront
+// per SIMD (the backward's per-lane accumulators need it).
+#ifndef ADALN_FWD_PF_SHORT
+#define ADALN_FWD_PF_SHORT 2
+#endif
+#ifndef ADALN_FWD_PF_LONG
+#define ADALN_FWD_PF_LONG 2
+#endif
+#ifndef ADALN_FWD_OCC_SHORT
+#define ADALN_FWD_OCC_SHORT 2
+#endif
+#ifndef ADALN_FWD_OCC_LONG
+#define ADALN_FWD_OCC_LONG 1
+#endif
+#ifndef ADALN_BWD_PF_SHORT
+#define ADALN_BWD_PF_SHORT 2
+#endif
+#ifndef ADALN_BWD_PF_LONG
+#define ADALN_BWD_PF_LONG 1
+#endif
+#ifndef ADALN_BWD_OCC_SHORT
+#define ADALN_BWD_OCC_SHORT 2
+#endif
+#ifndef ADALN_BWD_OCC_LONG
+#define ADALN_BWD_OCC_LONG 1
+#endif
+constexpr int fwd_stream_pf(int V) {
+  return V <= 8 ? ADALN_FWD_PF_SHORT : ADALN_FWD_PF_LONG;
+}
+constexpr int fwd_stream_occ(int V) {
+  return V <= 4 ? ADALN_FWD_OCC_SHORT : ADALN_FWD_OCC_LONG;
+}
+constexpr int bwd_stream_pf(int V) {
+  return V <= 6 ? ADALN_BWD_PF_SHORT : ADALN_BWD_PF_LONG;
+}
+constexpr int bwd_stream_occ(int V) {
+  return V <= 2 ? ADALN_BWD_OCC_SHORT : ADALN_BWD_OCC_LONG;
+}
+// The backward's per-lane accumulators (2*V*E floats) outgrow even the full
+// register file beyond V = 10; wider rows take the separate dx and D-tile
+// kernels.
+constexpr int kMaxBwdStreamV = 10;
+
+// Tile kernel of the forward for rows wider than 1024 vectors: a workgroup
+// of W wavefronts owns n_tile consecutive token rows of one sample, and lane
+// l of wavefront w holds vectors (k*W + w)*64 + l, k < V, of each row.
+struct TilePlan {
   int V = 0;
   int W = 0;
   int n_tile = 0;
-  int n_tiles = 0;
+  int n_tiles = 0;  // tiles per sample
 };
+
+constexpr int kMaxRowWaves = 8;  // at most 512 threads per tile workgroup
+#define ADALN_FWD_V(X) X(1) X(2) X(3) X(4) X(5) X(6) X(8)
+constexpr int kCUs = 256;
+constexpr int fwd_waves_per_simd(int V) {
+  return V <= 1 ? 8 : V == 2 ? 4 : V <= 4 ? 3 : 2;
+}
 
 // Grid-stride kernels take at most this many workgroups per launch.
 constexpr int64_t kMaxGrid = 1 << 20;
@@ -59,6 +126,21 @@ inline hipError_t launch_kernel(void (*k)(P...), int64_t blocks,
   const unsigned grid = (unsigned)(blocks < kMaxGrid ? blocks : kMaxGrid);
   void *argv[] = {(void *)&args...};
   return hipLaunchKernel((const void *)k, dim3(grid), dim3(256), argv, 0, s);
+}
+
+// As launch_kernel, with `threads` threads and `lds` bytes of dynamic LDS
+// per workgroup.
+template <typename... P, typename... A>
+inline hipError_t launch_kernel_lds(void (*k)(P...), int64_t blocks,
+                                    int threads, size_t lds, hipStream_t s,
+                                    A... args) {
+  static_assert(std::is_same<std::tuple<P...>, std::tuple<A...>>::value,
+                "kernel arguments must match the kernel's parameter types");
+  if (blocks <= 0) return hipSuccess;
+  const unsigned grid = (unsigned)(blocks < kMaxGrid ? blocks : kMaxGrid);
+  void *argv[] = {(void *)&args...};
+  return hipLaunchKernel((const void *)k, dim3(grid), dim3(threads), argv, lds,
+                         s);
 }
 
 // As launch_kernel, with `threads` threads per workgroup.
@@ -80,13 +162,17 @@ bool choose_row_plan(int64_t nvec, RowPlan *plan);
 int64_t max_row_vectors();
 
 DmodPlan choose_dmod_plan(int64_t B, int64_t N, int64_t nvec);
-bool choose_fused_plan(int64_t B, int64_t N, int64_t nvec, FusedPlan *plan);
+// Row-stream plan for the forward (bwd = false) or the fused backward; false
+// when the row is wider than kMaxStreamVectors.
+bool choose_stream_plan(int64_t B, int64_t N, int64_t nvec, bool bwd,
+                        StreamPlan *plan);
+bool choose_tile_plan(int64_t B, int64_t N, int64_t nvec, TilePlan *plan);
 
 // Launchers: enqueue on `stream`, return hipGetLastError() of the launch.
-hipError_t launch_fwd(int dtype, const RowPlan &plan, const void *x,
-                      const void *scale, const void *shift, void *y,
-                      float *mean, float *rstd, int64_t rows, int32_t N,
-                      int32_t D, hipStream_t stream);
+hipError_t launch_fwd_tiles(int dtype, const TilePlan &plan, const void *x,
+                            const void *scale, const void *shift, void *y,
+                            float *mean, float *rstd, int32_t B, int32_t N,
+                            int32_t D, hipStream_t stream);
 
 hipError_t launch_bwd_dx(int dtype, const RowPlan &plan, const void *dy,
                          const void *x, const void *scale, const float *mean,
@@ -108,7 +194,12 @@ hipError_t launch_dmod_finish(const float *part_scale,
                               float *dshift, int32_t B, int32_t D,
                               int32_t n_tiles, hipStream_t stream);
 
-hipError_t launch_bwd_fused(int dtype, const FusedPlan &plan, const void *dy,
+hipError_t launch_fwd_stream(int dtype, const StreamPlan &plan, const void *x,
+                             const void *scale, const void *shift, void *y,
+                             float *mean, float *rstd, int32_t B, int32_t N,
+                             int32_t D, hipStream_t stream);
+
+hipError_t launch_bwd_fused(int dtype, const StreamPlan &plan, const void *dy,
                             const void *x, const void *scale,
                             const float *mean, const float *rstd, void *dx,
                             float *part_scale, float *part_shift, int32_t B,

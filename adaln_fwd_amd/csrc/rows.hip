@@ -1,40 +1,17 @@
-// Row kernels of the fused AdaLN operator: the forward pass and the input
-// gradient dx.  One token row of D features lives in the registers of W
-// wavefronts (V 16-byte vectors per lane); the row is read from HBM once.
-//
-// Forward (AdaptiveLoad technical summary, section 2.B, forward pass): the
-// row's mean and variance are reduced inside the wavefront with DPP, across
-// wavefronts through LDS, and kept in registers; the modulation is applied on
-// the pass that writes y, so x is read once and y written once.  Statistics
-// are two-pass over the register-resident row (mean, then the centred sum of
-// squares), which costs no extra memory traffic.
-//
-// dx: the exact gradient of y = xhat * (1 + scale) + shift with respect to x,
-// reusing the mean and rstd the forward pass saved.
+// Row kernel of the input gradient dx on its own (adaln_bwd_dx, and the
+// backward of rows too wide for the fused kernel): the exact gradient of
+// y = xhat * (1 + scale) + shift with respect to x, reusing the mean and rstd
+// the forward pass saved.  One token row of D features lives in the
+// registers of W wavefronts (V 16-byte vectors per lane); the two row sums
+// are reduced inside the wavefront with DPP and across wavefronts in LDS.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace adaln {
 
-// Sum of one value over the W wavefronts of a row group.  `red` holds 4
-// floats of LDS; callers alternate between two such arrays so a barrier
-// always separates a read of one from the next write to it.
-template <int W>
-__device__ __forceinline__ float group_sum(float v, float *red, int wave,
-                                           int grp) {
-  v = wave_sum(v);
-  if constexpr (W == 1) {
-    return v;
-  } else {
-    if (lane_id() == 0) red[wave] = v;
-    __syncthreads();
-    float t = red[grp * W];
-#pragma unroll
-    for (int w = 1; w < W; ++w) t += red[grp * W + w];
-    return t;
-  }
-}
-
+// Sums of two values over the W wavefronts of a row group, through 8 floats
+// of LDS; callers alternate between two such arrays so a barrier always
+// separates a read of one from the next write to it.
 template <int W>
 __device__ __forceinline__ void group_sum2(float &a, float &b, float *red,
                                            int wave, int grp) {
@@ -53,85 +30,6 @@ __device__ __forceinline__ void group_sum2(float &a, float &b, float *red,
     }
     a = ta;
     b = tb;
-  }
-}
-
-template <typename T, int V, int W>
-__global__ __launch_bounds__(kBlock) void fwd_kernel(
-    const T *__restrict__ x, const T *__restrict__ scale,
-    const T *__restrict__ shift, T *__restrict__ y, float *__restrict__ mean,
-    float *__restrict__ rstd, int32_t rows, int32_t N, int32_t D) {
-  constexpr int E = Elems<T>::value;
-  constexpr int G = 4 / W;  // rows per workgroup
-  __shared__ float red[2][4];
-  const int lane = lane_id();
-  const int wave = wave_id();
-  const int grp = wave / W;
-  const int wig = wave - grp * W;
-  const int nvec = D / E;
-  const int row_blocks = (rows + G - 1) / G;
-  const float inv_d = 1.0f / (float)D;
-
-  for (int rb = blockIdx.x; rb < row_blocks; rb += gridDim.x) {
-    const int row = rb * G + grp;
-    const bool live = row < rows;
-    const int64_t off = (int64_t)(live ? row : 0) * D;
-
-    Vec xv[V];
-    bool ok[V];
-#pragma unroll
-    for (int k = 0; k < V; ++k) {
-      const int j = (k * W + wig) * kWave + lane;
-      ok[k] = live && j < nvec;
-      xv[k] = ok[k] ? load_stream(x + off + (int64_t)j * E) : vzero();
-    }
-
-    float sum = 0.f;
-#pragma unroll
-    for (int k = 0; k < V; ++k)
-#pragma unroll
-      for (int e = 0; e < E; ++e) sum += elem<T>(xv[k], e);
-    const float mu = group_sum<W>(sum, red[0], wave, grp) * inv_d;
-#pragma unroll
-    for (int k = 0; k < V; ++k) opaque(xv[k]);
-
-    float sq = 0.f;
-#pragma unroll
-    for (int k = 0; k < V; ++k) {
-      if (ok[k]) {
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-          const float c = elem<T>(xv[k], e) - mu;
-          sq = fmaf(c, c, sq);
-        }
-      }
-    }
-    const float var = group_sum<W>(sq, red[1], wave, grp) * inv_d;
-#pragma unroll
-    for (int k = 0; k < V; ++k) opaque(xv[k]);
-    const float r = 1.0f / sqrtf(var + kEps);
-
-    if (live && wig == 0 && lane == 0) {
-      mean[row] = mu;
-      rstd[row] = r;
-    }
-
-    const int64_t moff = (int64_t)(live ? row / N : 0) * D;
-#pragma unroll
-    for (int k = 0; k < V; ++k) {
-      if (ok[k]) {
-        const int64_t c = (int64_t)((k * W + wig) * kWave + lane) * E;
-        const Vec sv = load_vec(scale + moff + c);
-        const Vec hv = load_vec(shift + moff + c);
-        float o[E];
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-          const float xh = (elem<T>(xv[k], e) - mu) * r;
-          o[e] = fmaf(xh, 1.0f + elem<T>(sv, e), elem<T>(hv, e));
-        }
-        store_stream(y + off + c, pack<T>(o));
-      }
-    }
   }
 }
 
@@ -221,17 +119,6 @@ __global__ __launch_bounds__(kBlock) void dx_kernel(
 namespace {
 
 template <typename T, int V, int W>
-hipError_t fwd_vw(const void *x, const void *scale, const void *shift, void *y,
-                  float *mean, float *rstd, int64_t rows, int32_t N, int32_t D,
-                  hipStream_t s) {
-  constexpr int G = 4 / W;
-  return launch_kernel(
-      fwd_kernel<T, V, W>, (rows + G - 1) / G, s, (const T *)x,
-      (const T *)scale, (const T *)shift, (T *)y, mean, rstd, (int32_t)rows,
-      N, D);
-}
-
-template <typename T, int V, int W>
 hipError_t dx_vw(const void *dy, const void *x, const void *scale,
                  const float *mean, const float *rstd, void *dx, int64_t rows,
                  int32_t N, int32_t D, hipStream_t s) {
@@ -243,27 +130,12 @@ hipError_t dx_vw(const void *dy, const void *x, const void *scale,
 
 }  // namespace
 
-#define ADALN_FWD_CASE(V_, W_)                                               \
-  if (plan.V == V_ && plan.W == W_)                                          \
-    return dtype == 1 ? fwd_vw<bf16, V_, W_>(x, scale, shift, y, mean, rstd, \
-                                             rows, N, D, stream)             \
-                      : fwd_vw<float, V_, W_>(x, scale, shift, y, mean,      \
-                                              rstd, rows, N, D, stream);
-
 #define ADALN_DX_CASE(V_, W_)                                               \
   if (plan.V == V_ && plan.W == W_)                                         \
     return dtype == 1 ? dx_vw<bf16, V_, W_>(dy, x, scale, mean, rstd, dx,   \
                                             rows, N, D, stream)             \
                       : dx_vw<float, V_, W_>(dy, x, scale, mean, rstd, dx,  \
                                              rows, N, D, stream);
-
-hipError_t launch_fwd(int dtype, const RowPlan &plan, const void *x,
-                      const void *scale, const void *shift, void *y,
-                      float *mean, float *rstd, int64_t rows, int32_t N,
-                      int32_t D, hipStream_t stream) {
-  ADALN_ROW_PLANS(ADALN_FWD_CASE)
-  return hipErrorInvalidValue;
-}
 
 hipError_t launch_bwd_dx(int dtype, const RowPlan &plan, const void *dy,
                          const void *x, const void *scale, const float *mean,

@@ -239,7 +239,8 @@ def bwd_fused_plan(B: int, N: int, D: int, dtype: torch.dtype) -> dict:
     rc = _lib.load().adaln_bwd_fused_plan(B, N, D, _DTYPES.get(dtype, -1),
                                           out)
     _lib.check(rc, "adaln_bwd_fused_plan")
-    return dict(V=out[0], W=out[1], n_tile=out[2], n_tiles=out[3])
+    return dict(V=out[0], waves_per_row=out[1], workgroups=out[2],
+                partial_rows=out[3])
 
 
 def bshape(S: int, m_mem: int, m_comp: int, p: int) -> int:

@@ -200,7 +200,7 @@ def main(argv=None) -> int:
     dshift = torch.empty(B, D, dtype=torch.float32, device=dev)
     wbytes = A.bwd_workspace_bytes(B, N, D, dt)
     ws = torch.empty(max(wbytes, 1), dtype=torch.uint8, device=dev)
-    n_tiles = A.bwd_fused_plan(B, N, D, dt)["n_tiles"]
+    n_tiles = A.bwd_fused_plan(B, N, D, dt)["partial_rows"]
     stream = torch.cuda.current_stream(dev)
 
     def step(ev=None):

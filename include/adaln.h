@@ -90,7 +90,7 @@ int adaln_fwd(const void *x, const void *scale, const void *shift, void *y,
 size_t adaln_bwd_workspace_bytes(int64_t B, int64_t N, int64_t D, int dtype);
 
 /*
- * Backward pass: dx, dscale and dshift.  For rows of at most 2048 vectors it
+ * Backward pass: dx, dscale and dshift.  For rows of at most 640 vectors it
  * enqueues adaln_bwd_fused then adaln_bwd_finish (x and dy read once); for
  * wider rows, adaln_bwd_dx then adaln_bwd_dmod.
  *   dy        [B,N,D] dtype in   upstream gradient dL/dy
@@ -110,13 +110,14 @@ int adaln_bwd(const void *dy, const void *x, const void *scale,
               int64_t B, int64_t N, int64_t D, int dtype, void *stream);
 
 /*
- * The two launches adaln_bwd makes for rows of at most 2048 vectors
- * (D <= 16384 bf16 / 8192 f32), exposed so callers can schedule or time them
+ * The two launches adaln_bwd makes for rows of at most 640 vectors
+ * (D <= 5120 bf16 / 2560 f32), exposed so callers can schedule or time them
  * separately.  adaln_bwd_fused reads x and dy once: it writes dx and, per
  * (sample, n_tile), float32 partial sums of dscale and dshift into the
  * workspace -- the D-tile coalesced reduction of section 2.B with dx fused
- * into the same pass over the rows.  adaln_bwd_finish then sums those
- * partials over the n_tiles in index order into dscale and dshift.  The
+ * into the same pass over the rows: one partial row per (sample, workgroup).
+ * adaln_bwd_finish then sums those partials over the workgroups of each
+ * sample in index order into dscale and dshift.  The
  * workspace must be the one adaln_bwd_fused filled for the same B, N, D and
  * dtype, with no other call using it in between.  Both return
  * ADALN_ERR_UNSUPPORTED for wider rows (adaln_bwd handles those).
@@ -133,8 +134,8 @@ int adaln_bwd_finish(const void *workspace, size_t workspace_bytes,
 /*
  * Launch plan of adaln_bwd_fused for this shape, for callers that account
  * for the partial sums it writes: fills out[0..3] with {vectors per lane,
- * wavefronts per workgroup, n_tile (token rows per workgroup), n_tiles}.
- * The partials occupy 2*B*n_tiles*D floats at the start of the workspace.
+ * wavefronts per row (1), workgroups launched, partial rows per sample P}.
+ * The partials occupy 2*B*P*D floats at the start of the workspace.
  * Returns ADALN_ERR_UNSUPPORTED for rows too wide for the fused kernel.
  * Host-only; no HIP call.
  */

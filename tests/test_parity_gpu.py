@@ -220,10 +220,11 @@ def test_unfused_entry_points(A, wl):
         _say(f"  {r}")
 
 
-def test_fused_unsupported_for_wide_rows(A):
-    """Rows wider than 2048 vectors have no fused plan; adaln_bwd falls back
+@pytest.mark.parametrize("D", [5128, 8192, 32768])
+def test_fused_unsupported_for_wide_rows(A, D):
+    """Rows wider than 640 vectors have no fused plan; adaln_bwd falls back
     to the unfused kernels and gives the same bits as calling them."""
-    wl = W.custom(1, 9, 32768, "bf16", dy_std=1e-2)
+    wl = W.custom(1, 9, D, "bf16", dy_std=1e-2)
     _say("wide rows: bwd falls back to bwd_dx + bwd_dmod")
     dev = P.to_device(synth.make_inputs(wl))
     out = P.gpu_fwd_bwd(dev)
