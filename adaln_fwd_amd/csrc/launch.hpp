@@ -79,7 +79,7 @@ constexpr int kMaxStreamVectors = 16 * 64;
 #define ADALN_BWD_OCC_LONG 1
 #endif
 constexpr int fwd_stream_pf(int V) {
-  return V <= 8 ? ADALN_FWD_PF_SHORT : ADALN_FWD_PF_LONG;
+  return V <= 8 ? ADALN_FWD_PF_SHORT : V <= 12 ? ADALN_FWD_PF_LONG : 1;
 }
 constexpr int fwd_stream_occ(int V) {
   return V <= 4 ? ADALN_FWD_OCC_SHORT : ADALN_FWD_OCC_LONG;

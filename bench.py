@@ -4,8 +4,12 @@
 One step is the whole hot path over one batch of synthetic input already
 resident in HBM: adaln_fwd, then the backward pass as adaln_bwd enqueues it
 (adaln_bwd_fused, then adaln_bwd_finish), on torch's current stream.
-W untimed warm-up steps run first; then exactly K steps are timed between two
-device synchronisations.  HIP events recorded on the same stream between the
+For --workload mixed_schedule a step is one pass over all 64 buckets of the
+mixed-length schedule in schedule order (each bucket a forward and a
+backward); one input set per bucket shape is drawn and kept resident, since
+the kernels' time does not depend on the values.  W untimed warm-up steps
+run first; then exactly K steps are timed between two device
+synchronisations.  HIP events recorded on the same stream between the
 calls give each kernel's average duration inside the timed region.
 
 Prints one JSON line:
@@ -141,6 +145,26 @@ def copy_probe(nbytes: int, steps: int, warmup: int) -> int:
     return 0
 
 
+def make_job(A, torch, inp, dev, esize):
+    """Device buffers of one batch shape, plus its algorithmic bytes."""
+    B, N, D = inp.x.shape
+    dt = inp.x.dtype
+    job = {k: getattr(inp, k).to(dev) for k in ("x", "scale", "shift", "dy")}
+    job["y"] = torch.empty_like(job["x"])
+    job["dx"] = torch.empty_like(job["x"])
+    job["mean"] = torch.empty(B, N, dtype=torch.float32, device=dev)
+    job["rstd"] = torch.empty(B, N, dtype=torch.float32, device=dev)
+    job["dscale"] = torch.empty(B, D, dtype=torch.float32, device=dev)
+    job["dshift"] = torch.empty(B, D, dtype=torch.float32, device=dev)
+    wbytes = A.bwd_workspace_bytes(B, N, D, dt)
+    job["ws"] = torch.empty(max(wbytes, 1), dtype=torch.uint8, device=dev)
+    job["shape"] = (B, N, D)
+    job["tokens"] = B * N
+    part_rows = A.bwd_fused_plan(B, N, D, dt)["partial_rows"]
+    job["bytes"] = algorithmic_bytes(B, N, D, esize, part_rows)
+    return job
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -175,55 +199,65 @@ def main(argv=None) -> int:
         print("no GPU visible", file=sys.stderr)
         return 1
     wl = synth.BY_NAME[args.workload]
-    if wl.B is None:
-        print(f"{wl.name} is a schedule, not a single-batch workload",
-              file=sys.stderr)
-        return 2
-    B, N, D = wl.shape
-    dt = synth.torch_dtype(wl.dtype)
-    esize = torch.empty((), dtype=dt).element_size()
-    if args.copy_probe:
-        return copy_probe(B * N * D * esize, args.steps, args.warmup)
-    log(f"workload {wl.name} B={B} N={N} D={D} {wl.dtype}: drawing inputs")
-    inp = synth.make_inputs(wl, seed=args.seed)
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
-    x = inp.x.to(dev)
-    scale = inp.scale.to(dev)
-    shift = inp.shift.to(dev)
-    dy = inp.dy.to(dev)
-    y = torch.empty_like(x)
-    dx = torch.empty_like(x)
-    mean = torch.empty(B, N, dtype=torch.float32, device=dev)
-    rstd = torch.empty(B, N, dtype=torch.float32, device=dev)
-    dscale = torch.empty(B, D, dtype=torch.float32, device=dev)
-    dshift = torch.empty(B, D, dtype=torch.float32, device=dev)
-    wbytes = A.bwd_workspace_bytes(B, N, D, dt)
-    ws = torch.empty(max(wbytes, 1), dtype=torch.uint8, device=dev)
-    n_tiles = A.bwd_fused_plan(B, N, D, dt)["partial_rows"]
     stream = torch.cuda.current_stream(dev)
+    dt = synth.torch_dtype(wl.dtype)
+    esize = torch.empty((), dtype=dt).element_size()
+
+    if wl.B is None:
+        # the mixed-length schedule: one step = every bucket, in order
+        sched = synth.mixed_schedule(args.seed)
+        shapes = {S: A.bshape(S, synth.MIXED_M_MEM, synth.MIXED_M_COMP,
+                              synth.MIXED_P) for S in sorted(set(sched))}
+        D = wl.D
+        if args.copy_probe:
+            big = max(b * S for S, b in shapes.items())
+            return copy_probe(big * D * esize, args.steps, args.warmup)
+        log(f"schedule of {len(sched)} buckets, D={D}: drawing one input set "
+            f"per bucket shape {shapes}")
+        jobs = {}
+        for S, Bk in shapes.items():
+            inp = synth.make_inputs(synth.mixed_bucket(Bk, S), seed=args.seed,
+                                    bucket=sched.index(S))
+            jobs[S] = make_job(A, torch, inp, dev, esize)
+        order = [jobs[S] for S in sched]
+        first_inp = None
+    else:
+        B, N, D = wl.shape
+        if args.copy_probe:
+            return copy_probe(B * N * D * esize, args.steps, args.warmup)
+        log(f"workload {wl.name} B={B} N={N} D={D} {wl.dtype}: drawing inputs")
+        first_inp = synth.make_inputs(wl, seed=args.seed)
+        order = [make_job(A, torch, first_inp, dev, esize)]
+
+    names = ("fwd", "bwd_fused", "bwd_finish")
 
     def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
-        A.fwd(x, scale, shift, y=y, mean=mean, rstd=rstd, stream=stream)
-        if ev is not None:
-            ev[1].record(stream)
-        A.bwd_fused(dy, x, scale, mean, rstd, dx=dx, workspace=ws,
-                    stream=stream)
-        if ev is not None:
-            ev[2].record(stream)
-        A.bwd_finish(ws, B, N, D, dt, dscale=dscale, dshift=dshift,
-                     stream=stream)
-        if ev is not None:
-            ev[3].record(stream)
+        for j, job in enumerate(order):
+            e = ev[j] if ev is not None else None
+            if e is not None:
+                e[0].record(stream)
+            A.fwd(job["x"], job["scale"], job["shift"], y=job["y"],
+                  mean=job["mean"], rstd=job["rstd"], stream=stream)
+            if e is not None:
+                e[1].record(stream)
+            A.bwd_fused(job["dy"], job["x"], job["scale"], job["mean"],
+                        job["rstd"], dx=job["dx"], workspace=job["ws"],
+                        stream=stream)
+            if e is not None:
+                e[2].record(stream)
+            A.bwd_finish(job["ws"], *job["shape"], dt, dscale=job["dscale"],
+                         dshift=job["dshift"], stream=stream)
+            if e is not None:
+                e[3].record(stream)
 
     log(f"warm-up {args.warmup} steps")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)]
-              for _ in range(args.steps)]
+    events = [[[torch.cuda.Event(enable_timing=True) for _ in range(4)]
+               for _ in order] for _ in range(args.steps)]
     log(f"timing {args.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -233,21 +267,27 @@ def main(argv=None) -> int:
     elapsed = time.perf_counter() - t0
     ms_step = 1e3 * elapsed / args.steps
 
-    names = ("fwd", "bwd_fused", "bwd_finish")
-    avg_ms = {n: sum(ev[i].elapsed_time(ev[i + 1]) for ev in events)
-              / args.steps for i, n in enumerate(names)}
-    byts = algorithmic_bytes(B, N, D, esize, n_tiles)
-    kernels = {n: {"avg_ms": round(avg_ms[n], 5),
-                   "bytes": int(byts[n]),
-                   "gbps": round(byts[n] / (avg_ms[n] * 1e-3) / 1e9, 1)}
+    # per-kernel time and algorithmic bytes, summed over the jobs of a step
+    tot_ms = {n: 0.0 for n in names}
+    tot_bytes = {n: 0 for n in names}
+    for j, job in enumerate(order):
+        for i, n in enumerate(names):
+            tot_ms[n] += sum(ev[j][i].elapsed_time(ev[j][i + 1])
+                             for ev in events) / args.steps
+            tot_bytes[n] += job["bytes"][n]
+    launches = len(order)
+    kernels = {n: {"avg_ms": round(tot_ms[n] / launches, 5),
+                   "bytes": int(tot_bytes[n] / launches),
+                   "gbps": round(tot_bytes[n] / (tot_ms[n] * 1e-3) / 1e9, 1)}
                for n in names}
-    step_bytes = sum(byts.values())
+    step_bytes = sum(tot_bytes.values())
+    tokens = sum(job["tokens"] for job in order)
     gbps = step_bytes / (ms_step * 1e-3) / 1e9
-    tokens_s = B * N / (ms_step * 1e-3)
+    tokens_s = tokens / (ms_step * 1e-3)
 
-    dom = max(names, key=lambda n: avg_ms[n])
+    dom = max(names, key=lambda n: tot_ms[n])
     src_hash = kernel_source_hash()
-    achieved = byts[dom] / (avg_ms[dom] * 1e-3) / 1e9
+    achieved = tot_bytes[dom] / (tot_ms[dom] * 1e-3) / 1e9
     roofline = {
         "kernel": dom,
         "bound": "hbm",
@@ -256,14 +296,21 @@ def main(argv=None) -> int:
         "unit": "GB/s",
         "frac": round(achieved / HBM_PEAK_GBPS, 4),
         "traffic": load_traffic(dom, wl.name, src_hash),
-        "algorithmic_bytes_per_launch": int(byts[dom]),
-        "avg_launch_ms": round(avg_ms[dom], 5),
+        "algorithmic_bytes_per_launch": int(tot_bytes[dom] / launches),
+        "avg_launch_ms": round(tot_ms[dom] / launches, 5),
     }
+    if wl.B is None:
+        config = {"workload": wl.name, "buckets": len(order), "D": D,
+                  "tokens": tokens, "dtype": wl.dtype,
+                  "bucket_batch": {str(S): b for S, b in shapes.items()}}
+    else:
+        config = {"workload": wl.name, "B": B, "N": N, "D": D,
+                  "dtype": wl.dtype}
 
     cpu = None
-    if args.cpu_budget > 0:
+    if args.cpu_budget > 0 and first_inp is not None:
         log(f"cpu baseline: oracle for ~{args.cpu_budget:.0f} s")
-        cpu = cpu_baseline(inp, args.cpu_budget)
+        cpu = cpu_baseline(first_inp, args.cpu_budget)
 
     rec = {
         "metric": METRIC,
@@ -278,8 +325,7 @@ def main(argv=None) -> int:
         "vs_baseline": None,
         "dtype": wl.dtype,
         "data": "synthetic",
-        "config": {"workload": wl.name, "B": B, "N": N, "D": D,
-                   "dtype": wl.dtype},
+        "config": config,
         "hbm_gbps": round(gbps, 1),
         "hbm_frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
         "kernels": kernels,
