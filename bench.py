@@ -46,15 +46,92 @@ def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
+# Sources that determine each kernel's code and launch shape.
+_SHARED = ("common.hpp", "launch.hpp", "abi.hip")
+KERNEL_SOURCES = {
+    "fwd": ("fwd.hip",) + _SHARED,
+    "bwd_fused": ("bwd_fused.hip",) + _SHARED,
+    "bwd_finish": ("dmod.hip",) + _SHARED,
+}
+# rocprofv3 kernel-name prefixes of each step component
+KERNEL_SYMBOLS = {
+    "fwd": "void adaln::fwd_stream_kernel",
+    "bwd_fused": "void adaln::bwd_stream_kernel",
+    "bwd_finish": "adaln::dmod_finish_kernel",
+}
+
+
+def kernel_source_hash(kernel: str = None) -> str:
+    """Hash of the sources of one step component (all of them if None)."""
     h = hashlib.sha256()
-    files = sorted(glob.glob(os.path.join(ROOT, "adaln_fwd_amd", "csrc", "*")))
+    csrc = os.path.join(ROOT, "adaln_fwd_amd", "csrc")
+    if kernel is None:
+        files = sorted(glob.glob(os.path.join(csrc, "*")))
+    else:
+        files = [os.path.join(csrc, f) for f in sorted(KERNEL_SOURCES[kernel])]
     files.append(os.path.join(ROOT, "include", "adaln.h"))
     for f in files:
         h.update(os.path.basename(f).encode())
         with open(f, "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
+
+
+def traffic_from_counters(pmc_dir: str, workload: str, copy_bytes: int):
+    """Per-launch HBM bytes of each step component from four rocprofv3
+    --pmc runs under pmc_dir: fetch/ and write/ (FETCH_SIZE, WRITE_SIZE of
+    bench.py) and copy_fetch/, copy_write/ (the same counters over the copy
+    probe, which reads and writes copy_bytes each).  Each counter is scaled
+    by the ratio of the copy's known size to what the counter read for it."""
+    import csv
+
+    def per_kernel(sub, counter):
+        vals = {}
+        path = os.path.join(pmc_dir, sub, "run_counter_collection.csv")
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] == counter:
+                    vals.setdefault(r["Kernel_Name"], []).append(
+                        float(r["Counter_Value"]))
+        return vals
+
+    def copy_kib(sub, counter):
+        vals = per_kernel(sub, counter)
+        # the copy probe is the only kernel launched more than once
+        name = max(vals, key=lambda k: len(vals[k]))
+        v = vals[name]
+        return name, sum(v) / len(v)
+
+    cname, copy_fetch = copy_kib("copy_fetch", "FETCH_SIZE")
+    _, copy_write = copy_kib("copy_write", "WRITE_SIZE")
+    f_fetch = copy_bytes / (copy_fetch * 1024.0)
+    f_write = copy_bytes / (copy_write * 1024.0)
+    fetch = per_kernel("fetch", "FETCH_SIZE")
+    write = per_kernel("write", "WRITE_SIZE")
+    out = {}
+    for comp, sym in KERNEL_SYMBOLS.items():
+        fk = [v for k, v in fetch.items() if k.startswith(sym)]
+        wk = [v for k, v in write.items() if k.startswith(sym)]
+        if not fk or not wk:
+            continue
+        fa = sum(fk[0]) / len(fk[0])
+        wa = sum(wk[0]) / len(wk[0])
+        out[comp] = {
+            "kernel": comp,
+            "workload": workload,
+            "fetch_kib_per_launch": round(fa, 3),
+            "write_kib_per_launch": round(wa, 3),
+            "copy_probe": {"kernel": cname, "bytes_read": copy_bytes,
+                           "bytes_written": copy_bytes,
+                           "fetch_kib": round(copy_fetch, 3),
+                           "write_kib": round(copy_write, 3)},
+            "fetch_scale": round(f_fetch, 6),
+            "write_scale": round(f_write, 6),
+            "hbm_bytes_per_launch": int(round(fa * 1024 * f_fetch
+                                              + wa * 1024 * f_write)),
+            "source_hash": kernel_source_hash(comp),
+        }
+    return out
 
 
 def algorithmic_bytes(B, N, D, esize, n_tiles):
@@ -174,11 +251,23 @@ def main(argv=None) -> int:
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-budget", type=float, default=10.0,
                     help="seconds of oracle time for cpu_baseline (0: skip)")
+    ap.add_argument("--traffic-from", metavar="DIR",
+                    help="print per-kernel HBM traffic computed from the "
+                         "rocprofv3 --pmc CSVs under DIR and exit")
     ap.add_argument("--copy-probe", action="store_true",
                     help="time torch's device copy of one workload-sized "
                          "tensor instead (achievable-bandwidth reference and "
                          "counter calibration)")
     args = ap.parse_args(argv)
+
+    if args.traffic_from:
+        import synth
+        wl = synth.BY_NAME[args.workload]
+        esize = 4 if wl.dtype == "f32" else 2
+        copy_bytes = wl.B * wl.N * wl.D * esize
+        print(json.dumps(traffic_from_counters(args.traffic_from, wl.name,
+                                               copy_bytes), indent=1))
+        return 0
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -295,7 +384,7 @@ def main(argv=None) -> int:
         "peak": HBM_PEAK_GBPS,
         "unit": "GB/s",
         "frac": round(achieved / HBM_PEAK_GBPS, 4),
-        "traffic": load_traffic(dom, wl.name, src_hash),
+        "traffic": load_traffic(dom, wl.name, kernel_source_hash(dom)),
         "algorithmic_bytes_per_launch": int(tot_bytes[dom] / launches),
         "avg_launch_ms": round(tot_ms[dom] / launches, 5),
     }
