@@ -106,40 +106,45 @@ __global__ __launch_bounds__(kBlock) void dmod_partial_kernel(
 }
 
 // dscale[b, d] = sum over t = 0 .. n_tiles-1 of part_scale[b, t, d] (and the
-// same for dshift).  A workgroup of 16 wavefronts covers 64 float4 columns of
-// one sample: lane l owns 4 features, wavefront w sums tiles w, w+16, w+32,
-// ... in order, and the 16 wavefront sums are added in wavefront order.  The
-// tile split keeps enough loads in flight to stream the partials at a useful
-// fraction of HBM bandwidth.  With n_tiles == 0 the outputs are zero.
+// same for dshift).  A workgroup of 16 wavefronts covers 64 features of one
+// sample, one per lane; wavefront w sums the contiguous range of tiles
+// [w*n_tiles/16, (w+1)*n_tiles/16) in index order, issuing up to 16 loads
+// per array before adding them, and the 16 wavefront sums are added in
+// wavefront order.  One feature per lane (rather than four) spreads a
+// 5120-feature sample over 80 workgroups, so enough CUs stream the partials.
+// With n_tiles == 0 the outputs are zero.
 constexpr int kFinishWaves = 16;
+constexpr int kFinishBatch = 16;
 
 __global__ __launch_bounds__(kFinishWaves * kWave) void dmod_finish_kernel(
     const float *__restrict__ part_scale, const float *__restrict__ part_shift,
     float *__restrict__ dscale, float *__restrict__ dshift, int32_t D,
     int32_t n_tiles, int32_t col_blocks, int64_t total_blocks) {
-  __shared__ float4 stage[kFinishWaves - 1][2][kWave];
+  __shared__ float stage[kFinishWaves - 1][2][kWave];
   const int lane = lane_id();
   const int wave = wave_id();
-  const int ncol = D / 4;
+  const int t0 = (int)((int64_t)wave * n_tiles / kFinishWaves);
+  const int t1 = (int)((int64_t)(wave + 1) * n_tiles / kFinishWaves);
 
   for (int64_t blk = blockIdx.x; blk < total_blocks; blk += gridDim.x) {
     const int cb = (int)(blk % col_blocks);
     const int b = (int)(blk / col_blocks);
     const int c = cb * kWave + lane;
-    const bool ok = c < ncol;
-    float4 as = make_float4(0.f, 0.f, 0.f, 0.f);
-    float4 ah = as;
-    if (ok) {
-      const float4 *ps = reinterpret_cast<const float4 *>(
-          part_scale + (int64_t)b * n_tiles * D) + c;
-      const float4 *ph = reinterpret_cast<const float4 *>(
-          part_shift + (int64_t)b * n_tiles * D) + c;
-#pragma unroll 8
-      for (int t = wave; t < n_tiles; t += kFinishWaves) {
-        const float4 vs = ps[(int64_t)t * ncol];
-        const float4 vh = ph[(int64_t)t * ncol];
-        as.x += vs.x; as.y += vs.y; as.z += vs.z; as.w += vs.w;
-        ah.x += vh.x; ah.y += vh.y; ah.z += vh.z; ah.w += vh.w;
+    const bool ok = c < D;
+    const int64_t base = (int64_t)b * n_tiles * D + c;
+    float as = 0.f, ah = 0.f;
+    for (int t = t0; t < t1; t += kFinishBatch) {
+      float vs[kFinishBatch], vh[kFinishBatch];
+#pragma unroll
+      for (int i = 0; i < kFinishBatch; ++i) {
+        const bool live = ok && t + i < t1;
+        vs[i] = live ? part_scale[base + (int64_t)(t + i) * D] : 0.f;
+        vh[i] = live ? part_shift[base + (int64_t)(t + i) * D] : 0.f;
+      }
+#pragma unroll
+      for (int i = 0; i < kFinishBatch; ++i) {
+        as += vs[i];
+        ah += vh[i];
       }
     }
     if (wave > 0) {
@@ -150,13 +155,11 @@ __global__ __launch_bounds__(kFinishWaves * kWave) void dmod_finish_kernel(
     if (wave == 0 && ok) {
 #pragma unroll
       for (int w = 0; w < kFinishWaves - 1; ++w) {
-        const float4 vs = stage[w][0][lane];
-        const float4 vh = stage[w][1][lane];
-        as.x += vs.x; as.y += vs.y; as.z += vs.z; as.w += vs.w;
-        ah.x += vh.x; ah.y += vh.y; ah.z += vh.z; ah.w += vh.w;
+        as += stage[w][0][lane];
+        ah += stage[w][1][lane];
       }
-      reinterpret_cast<float4 *>(dscale + (int64_t)b * D)[c] = as;
-      reinterpret_cast<float4 *>(dshift + (int64_t)b * D)[c] = ah;
+      dscale[(int64_t)b * D + c] = as;
+      dshift[(int64_t)b * D + c] = ah;
     }
     __syncthreads();
   }
@@ -186,7 +189,7 @@ hipError_t launch_dmod_finish(const float *part_scale,
                               const float *part_shift, float *dscale,
                               float *dshift, int32_t B, int32_t D,
                               int32_t n_tiles, hipStream_t stream) {
-  const int32_t col_blocks = (D / 4 + kWave - 1) / kWave;
+  const int32_t col_blocks = (D + kWave - 1) / kWave;
   const int64_t total_blocks = (int64_t)col_blocks * B;
   return launch_kernel_threads(dmod_finish_kernel, total_blocks,
                                kFinishWaves * kWave, stream, part_scale,

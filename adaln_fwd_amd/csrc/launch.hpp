@@ -51,20 +51,14 @@ constexpr int kMaxStreamVectors = 16 * 64;
 
 // Rows in flight per wavefront (PF) and waves per SIMD (OCC) of each stream
 // kernel instantiation.  OCC also fixes the grid: OCC workgroups per CU.
-// Short rows get two rows in flight and two workgroups per CU to keep enough
-// bytes in flight; long rows get the whole register file of one wavefront
-// per SIMD (the backward's per-lane accumulators need it).
+// Short rows get two rows in flight and several workgroups per CU to keep
+// enough bytes in flight; long rows get the whole register file of one
+// wavefront per SIMD (the backward's per-lane accumulators need it).
 #ifndef ADALN_FWD_PF_SHORT
 #define ADALN_FWD_PF_SHORT 2
 #endif
 #ifndef ADALN_FWD_PF_LONG
 #define ADALN_FWD_PF_LONG 2
-#endif
-#ifndef ADALN_FWD_OCC_SHORT
-#define ADALN_FWD_OCC_SHORT 2
-#endif
-#ifndef ADALN_FWD_OCC_LONG
-#define ADALN_FWD_OCC_LONG 1
 #endif
 #ifndef ADALN_BWD_PF_SHORT
 #define ADALN_BWD_PF_SHORT 2
@@ -78,17 +72,26 @@ constexpr int kMaxStreamVectors = 16 * 64;
 #ifndef ADALN_BWD_OCC_LONG
 #define ADALN_BWD_OCC_LONG 1
 #endif
+#ifndef ADALN_BWD_SHORT_V
+#define ADALN_BWD_SHORT_V 2
+#endif
 constexpr int fwd_stream_pf(int V) {
   return V <= 8 ? ADALN_FWD_PF_SHORT : V <= 12 ? ADALN_FWD_PF_LONG : 1;
 }
+// Forward occupancy per V: the highest of {4, 2, 1} at which the
+// instantiation compiles without register spills.
 constexpr int fwd_stream_occ(int V) {
-  return V <= 4 ? ADALN_FWD_OCC_SHORT : ADALN_FWD_OCC_LONG;
+#ifdef ADALN_FWD_OCC_ALL
+  return ADALN_FWD_OCC_ALL;
+#else
+  return (V == 1 || V == 3) ? 4 : V <= 4 ? 2 : 1;
+#endif
 }
 constexpr int bwd_stream_pf(int V) {
   return V <= 6 ? ADALN_BWD_PF_SHORT : ADALN_BWD_PF_LONG;
 }
 constexpr int bwd_stream_occ(int V) {
-  return V <= 2 ? ADALN_BWD_OCC_SHORT : ADALN_BWD_OCC_LONG;
+  return V <= ADALN_BWD_SHORT_V ? ADALN_BWD_OCC_SHORT : ADALN_BWD_OCC_LONG;
 }
 // The backward's per-lane accumulators (2*V*E floats) outgrow even the full
 // register file beyond V = 10; wider rows take the separate dx and D-tile
