@@ -153,6 +153,13 @@ DmodPlan choose_dmod_plan(int64_t B, int64_t N, int64_t nvec) {
 // shape, so the workspace size ([B, bps, D] partial sums of the backward) is
 // a pure function of it; on a part with another CU count the kernels remain
 // correct and only use the GPU less evenly.
+#ifndef ADALN_FWD_MIN_BPS
+#define ADALN_FWD_MIN_BPS 1
+#endif
+#ifndef ADALN_BWD_MIN_BPS
+#define ADALN_BWD_MIN_BPS 1
+#endif
+
 bool choose_stream_plan(int64_t B, int64_t N, int64_t nvec, bool bwd,
                         StreamPlan *plan) {
   StreamPlan p;
@@ -164,7 +171,9 @@ bool choose_stream_plan(int64_t B, int64_t N, int64_t nvec, bool bwd,
   if (B > 0 && N > 0) {
     const int occ = bwd ? bwd_stream_occ(p.V) : fwd_stream_occ(p.V);
     const int64_t G = (int64_t)kCUs * occ;
-    const int64_t bps = G / B > 1 ? G / B : 1;
+    const int64_t min_bps = bwd ? ADALN_BWD_MIN_BPS : ADALN_FWD_MIN_BPS;
+    int64_t bps = G / B > 1 ? G / B : 1;
+    if (bps < min_bps) bps = min_bps < G ? min_bps : G;
     const int64_t groups = G / bps;
     p.bps = (int)bps;
     p.groups = (int)groups;

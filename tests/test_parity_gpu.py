@@ -73,6 +73,10 @@ def test_video_bucket_full(A):
     (2, 17, 8192, "f32", "normal"),        # two wavefronts per row, f32
     (1, 5, 16384, "f32", "normal"),        # largest f32 row
     (3, 257, 1024, "f32", "offset"),
+    (600, 5, 1536, "bf16", "offset"),      # more samples than workgroups
+    (1100, 1, 5120, "bf16", "outliers"),   # several samples per workgroup
+    (2000, 3, 64, "f32", "normal"),
+    (300, 17, 520, "bf16", "normal"),      # many samples, ragged row
 ])
 def test_shapes(A, B, N, D, dtype, kind):
     wl = W.custom(B, N, D, dtype, x_kind=kind, dy_std=1e-2 if dtype ==
