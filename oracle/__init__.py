@@ -40,6 +40,12 @@ def _load():
     lib.oracle_fwd.restype = None
     lib.oracle_bwd.argtypes = [vp, vp, vp, i64, i64, i64, f64, vp, vp, vp]
     lib.oracle_bwd.restype = None
+    lib.oracle_fwd_segments.argtypes = [vp, vp, vp, vp, vp, i64, i64, f64,
+                                        vp, vp, vp]
+    lib.oracle_fwd_segments.restype = None
+    lib.oracle_bwd_segments.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64,
+                                        f64, vp, vp, vp]
+    lib.oracle_bwd_segments.restype = None
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
     lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
@@ -98,6 +104,59 @@ def bwd(dy, x, scale, eps: float = 1e-6, want_dx: bool = True,
     dshift = np.empty((B, D), np.float64) if want_dmod else None
     _load().oracle_bwd(_ptr(dy), _ptr(x), _ptr(scale), B, N, D, float(eps),
                        _ptr(dx), _ptr(dscale), _ptr(dshift))
+    return dx, dscale, dshift
+
+
+def _segments(seg_offsets, seg_mod, T: int, nmod: int):
+    off = np.ascontiguousarray(np.asarray(seg_offsets, dtype=np.int64))
+    nseg = off.size - 1
+    assert nseg >= 0 and off[0] == 0 and off[-1] == T
+    assert np.all(np.diff(off) >= 0)
+    mod = None
+    if seg_mod is not None:
+        mod = np.ascontiguousarray(np.asarray(seg_mod, dtype=np.int32))
+        assert mod.shape == (nseg,)
+        assert nseg == 0 or (mod.min() >= 0 and mod.max() < nmod)
+    else:
+        assert nseg <= nmod
+    return off, mod, nseg
+
+
+def fwd_segments(x, scale, shift, seg_offsets, seg_mod=None,
+                 eps: float = 1e-6, want_y: bool = True):
+    """Forward over a packed [T, D] array of segments; segment s is rows
+    seg_offsets[s]..seg_offsets[s+1]-1, modulated by scale/shift[seg_mod[s]]
+    (row s if seg_mod is None).  Returns (y [T,D] or None, mean [T],
+    rstd [T]) in float64."""
+    x, scale, shift = _f64(x), _f64(scale), _f64(shift)
+    T, D = x.shape
+    nmod = scale.shape[0]
+    assert scale.shape == (nmod, D) and shift.shape == (nmod, D)
+    off, mod, nseg = _segments(seg_offsets, seg_mod, T, nmod)
+    y = np.empty((T, D), np.float64) if want_y else None
+    mean = np.empty(T, np.float64)
+    rstd = np.empty(T, np.float64)
+    _load().oracle_fwd_segments(_ptr(x), _ptr(scale), _ptr(shift), _ptr(off),
+                                _ptr(mod), nseg, D, float(eps), _ptr(y),
+                                _ptr(mean), _ptr(rstd))
+    return y, mean, rstd
+
+
+def bwd_segments(dy, x, scale, seg_offsets, seg_mod=None, eps: float = 1e-6,
+                 want_dx: bool = True, want_dmod: bool = True):
+    """Backward of :func:`fwd_segments`.  Returns (dx [T,D] or None,
+    dscale [nmod,D] or None, dshift [nmod,D] or None) in float64."""
+    dy, x, scale = _f64(dy), _f64(x), _f64(scale)
+    T, D = x.shape
+    nmod = scale.shape[0]
+    assert dy.shape == (T, D) and scale.shape == (nmod, D)
+    off, mod, nseg = _segments(seg_offsets, seg_mod, T, nmod)
+    dx = np.empty((T, D), np.float64) if want_dx else None
+    dscale = np.empty((nmod, D), np.float64) if want_dmod else None
+    dshift = np.empty((nmod, D), np.float64) if want_dmod else None
+    _load().oracle_bwd_segments(_ptr(dy), _ptr(x), _ptr(scale), _ptr(off),
+                                _ptr(mod), nseg, nmod, D, float(eps),
+                                _ptr(dx), _ptr(dscale), _ptr(dshift))
     return dx, dscale, dshift
 
 

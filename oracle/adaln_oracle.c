@@ -205,6 +205,133 @@ void oracle_bwd(const double *dy, const double *x, const double *scale,
     free(r);
 }
 
+/* Packed variable-length layout (the unpadded mixed-length batches of
+ * section 2.A, and the separately modulated text and video token segments of
+ * MMDiT samples): the token rows of nseg segments lie back to back in one
+ * [T, D] array, segment s being rows off[s] .. off[s+1]-1 with off[0] = 0 and
+ * T = off[nseg], and segment s is modulated by vector mod[s] of scale, shift:
+ * [nmod, D] (mod == NULL: vector s).  Each row is normalised and modulated
+ * exactly as in oracle_fwd; the caller guarantees a valid table. */
+static int64_t seg_mod_of(const int32_t *mod, int64_t s)
+{
+    return mod ? (int64_t)mod[s] : s;
+}
+
+void oracle_fwd_segments(const double *x, const double *scale,
+                         const double *shift, const int64_t *off,
+                         const int32_t *mod, int64_t nseg, int64_t D,
+                         double eps, double *y, double *mean, double *rstd)
+{
+    for (int64_t s = 0; s < nseg; ++s) {
+        int64_t m = seg_mod_of(mod, s);
+#pragma omp parallel for schedule(static)
+        for (int64_t row = off[s]; row < off[s + 1]; ++row) {
+            const double *xr = x + row * D;
+            double mu, r;
+            row_stats(xr, D, eps, &mu, &r);
+            if (mean)
+                mean[row] = mu;
+            if (rstd)
+                rstd[row] = r;
+            if (y) {
+                for (int64_t d = 0; d < D; ++d) {
+                    double xhat = (xr[d] - mu) * r;
+                    y[row * D + d] = xhat * (1.0 + scale[m * D + d])
+                                     + shift[m * D + d];
+                }
+            }
+        }
+    }
+}
+
+/* Backward of oracle_fwd_segments.  dx as in oracle_bwd, row by row with the
+ * row's segment's scale; dscale[m] and dshift[m] sum dy * xhat and dy over
+ * the rows of every segment s with mod[s] == m, segments in index order and
+ * rows in order within each (zero where no segment uses m). */
+void oracle_bwd_segments(const double *dy, const double *x,
+                         const double *scale, const int64_t *off,
+                         const int32_t *mod, int64_t nseg, int64_t nmod,
+                         int64_t D, double eps, double *dx, double *dscale,
+                         double *dshift)
+{
+    int64_t rows = nseg > 0 ? off[nseg] : 0;
+    double *mu = (double *)malloc(sizeof(double) * (size_t)(rows > 0 ? rows : 1));
+    double *r = (double *)malloc(sizeof(double) * (size_t)(rows > 0 ? rows : 1));
+    if (!mu || !r)
+        abort();
+
+#pragma omp parallel for schedule(static)
+    for (int64_t row = 0; row < rows; ++row)
+        row_stats(x + row * D, D, eps, &mu[row], &r[row]);
+
+    if (dx) {
+        for (int64_t s = 0; s < nseg; ++s) {
+            int64_t m = seg_mod_of(mod, s);
+#pragma omp parallel for schedule(static)
+            for (int64_t row = off[s]; row < off[s + 1]; ++row) {
+                const double *xr = x + row * D;
+                const double *gr = dy + row * D;
+                double sum_g = 0.0, sum_gx = 0.0;
+                for (int64_t d = 0; d < D; ++d) {
+                    double g = gr[d] * (1.0 + scale[m * D + d]);
+                    double xhat = (xr[d] - mu[row]) * r[row];
+                    sum_g += g;
+                    sum_gx += g * xhat;
+                }
+                double c1 = sum_g / (double)D;
+                double c2 = sum_gx / (double)D;
+                for (int64_t d = 0; d < D; ++d) {
+                    double g = gr[d] * (1.0 + scale[m * D + d]);
+                    double xhat = (xr[d] - mu[row]) * r[row];
+                    dx[row * D + d] = r[row] * (g - c1 - xhat * c2);
+                }
+            }
+        }
+    }
+
+    if (dscale || dshift) {
+        /* one (modulation vector, block of 64 features) pair per work item;
+         * each walks the rows of the segments that use the vector and keeps
+         * one running sum per feature it owns */
+        const int64_t FB = 64;
+        int64_t nfb = (D + FB - 1) / FB;
+#pragma omp parallel for schedule(static) collapse(2)
+        for (int64_t m = 0; m < nmod; ++m) {
+            for (int64_t fb = 0; fb < nfb; ++fb) {
+                double acc_s[64], acc_h[64];
+                int64_t d0 = fb * FB;
+                int64_t nd = (D - d0) < FB ? (D - d0) : FB;
+                for (int64_t j = 0; j < nd; ++j) {
+                    acc_s[j] = 0.0;
+                    acc_h[j] = 0.0;
+                }
+                for (int64_t s = 0; s < nseg; ++s) {
+                    if (seg_mod_of(mod, s) != m)
+                        continue;
+                    for (int64_t row = off[s]; row < off[s + 1]; ++row) {
+                        for (int64_t j = 0; j < nd; ++j) {
+                            int64_t d = d0 + j;
+                            double g = dy[row * D + d];
+                            double xhat = (x[row * D + d] - mu[row]) * r[row];
+                            acc_s[j] += g * xhat;
+                            acc_h[j] += g;
+                        }
+                    }
+                }
+                for (int64_t j = 0; j < nd; ++j) {
+                    if (dscale)
+                        dscale[m * D + d0 + j] = acc_s[j];
+                    if (dshift)
+                        dshift[m * D + d0 + j] = acc_h[j];
+                }
+            }
+        }
+    }
+
+    free(mu);
+    free(r);
+}
+
 /* Number of threads an OpenMP parallel region of this library uses. */
 int oracle_num_threads(void)
 {

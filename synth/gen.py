@@ -24,8 +24,9 @@ from typing import List, Optional
 import numpy as np
 import torch
 
-from .workloads import (MIXED_BUCKETS, MIXED_LENGTHS, MIXED_SCHEDULE,
-                        Workload)
+from .workloads import (MIXED_BUCKETS, MIXED_LENGTHS, MIXED_M_MEM,
+                        MIXED_SCHEDULE, MMDIT_PACKED, MMDIT_TEXT_TOKENS,
+                        PACKED_MIXED, Workload)
 
 TENSOR_X = 0
 TENSOR_OFFSET = 1
@@ -33,6 +34,7 @@ TENSOR_SCALE = 2
 TENSOR_SHIFT = 3
 TENSOR_DY = 4
 SCHEDULE_KEY = 0xC4
+PACK_KEY = 0xC5
 
 # Target number of elements per independently seeded block.
 BLOCK_ELEMS = 1 << 22
@@ -180,3 +182,94 @@ def mixed_schedule(seed: int = 0, count: int = MIXED_BUCKETS) -> List[int]:
     g = np.random.Generator(np.random.PCG64(ss))
     idx = g.integers(0, len(MIXED_LENGTHS), size=count)
     return [int(MIXED_LENGTHS[i]) for i in idx]
+
+
+@dataclass
+class PackedInputs:
+    """Host tensors of one packed call: x, dy [T, D]; scale, shift
+    [nmod, D]; segment s is rows seg_offsets[s] .. seg_offsets[s+1]-1 and
+    uses modulation vector seg_mod[s] (vector s if seg_mod is None)."""
+    x: torch.Tensor
+    scale: torch.Tensor
+    shift: torch.Tensor
+    dy: Optional[torch.Tensor]
+    seg_offsets: np.ndarray
+    seg_mod: Optional[np.ndarray]
+    workload: Workload
+    seed: int
+
+    @property
+    def lengths(self) -> np.ndarray:
+        return np.diff(self.seg_offsets)
+
+
+def pack_lengths(seed: int = 0, budget: int = MIXED_M_MEM,
+                 max_segments: int = 128, max_misses: int = 16) -> List[int]:
+    """Sequence lengths of one pack of the packed mixed-length layout:
+    lengths drawn uniformly from the mixed schedule's four, a draw that
+    would overflow the token budget skipped, until ``max_misses`` draws in a
+    row were skipped or the pack holds ``max_segments`` sequences."""
+    ss = np.random.SeedSequence(seed, spawn_key=(PACKED_MIXED.index,
+                                                 PACK_KEY))
+    g = np.random.Generator(np.random.PCG64(ss))
+    out: List[int] = []
+    total, misses = 0, 0
+    while misses < max_misses and len(out) < max_segments:
+        S = int(MIXED_LENGTHS[int(g.integers(0, len(MIXED_LENGTHS)))])
+        if total + S > budget:
+            misses += 1
+            continue
+        misses = 0
+        out.append(S)
+        total += S
+    return out
+
+
+def mmdit_layout(B: int, text: int = MMDIT_TEXT_TOKENS,
+                 video: int = MMDIT_PACKED.N - MMDIT_TEXT_TOKENS):
+    """Segment lengths and modulation indices of B two-stream samples packed
+    as [text_0, video_0, text_1, video_1, ...], with the modulation vectors
+    laid out [2, B, D]: text of sample b uses vector b, its video B + b."""
+    lengths, mods = [], []
+    for b in range(B):
+        lengths += [text, video]
+        mods += [b, B + b]
+    return lengths, mods
+
+
+def make_packed(wl: Workload, lengths, seg_mod=None, nmod: Optional[int] = None,
+                seed: int = 0, with_dy: bool = True,
+                workers: Optional[int] = None,
+                pin_memory: bool = False) -> PackedInputs:
+    """Draw the inputs of a packed layout with workload ``wl``'s dtype and
+    distributions: x, dy over the T = sum(lengths) rows, scale and shift for
+    ``nmod`` vectors (default: one per segment, or max(seg_mod) + 1)."""
+    lengths = [int(v) for v in lengths]
+    off = np.concatenate([[0], np.cumsum(lengths, dtype=np.int64)]).astype(
+        np.int64)
+    mods = None if seg_mod is None else np.asarray(seg_mod, dtype=np.int32)
+    if nmod is None:
+        nmod = len(lengths) if mods is None else (
+            int(mods.max()) + 1 if mods.size else 0)
+    T, D = int(off[-1]), wl.D
+    dt = torch_dtype(wl.dtype)
+    offsets = _offsets(wl, seed) if wl.x_kind == "offset" else None
+
+    def empty(*shape):
+        return torch.empty(*shape, dtype=dt, pin_memory=pin_memory)
+
+    x = empty(T, D)
+    _draw_rows(x, T, D, _x_block(wl, seed, 0, offsets), workers)
+    scale = empty(nmod, D)
+    _draw_rows(scale, nmod, D,
+               _normal_block(wl, seed, 0, TENSOR_SCALE, wl.mod_std), 1)
+    shift = empty(nmod, D)
+    _draw_rows(shift, nmod, D,
+               _normal_block(wl, seed, 0, TENSOR_SHIFT, wl.mod_std), 1)
+    dy = None
+    if with_dy:
+        dy = empty(T, D)
+        _draw_rows(dy, T, D,
+                   _normal_block(wl, seed, 0, TENSOR_DY, wl.dy_std), workers)
+    return PackedInputs(x=x, scale=scale, shift=shift, dy=dy, seg_offsets=off,
+                        seg_mod=mods, workload=wl, seed=seed)

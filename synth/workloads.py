@@ -98,8 +98,27 @@ MIXED_SCHEDULE = Workload(
     note="64 buckets with S drawn uniformly from {1560, 8190, 16380, 32760}, "
          "batch per bucket from the dual-constraint rule")
 
+# Packed (unpadded) layouts: the token rows of several sequences back to back
+# in one [T, D] tensor, each sequence (segment) with its own modulation.
+PACKED_MIXED = Workload(
+    name="packed_mixed", index=5, B=None, N=None, D=3072, dtype="bf16",
+    x_kind="offset", mod_std=0.1, dy_std=1e-2,
+    note="mixed-length samples (lengths uniform over the mixed schedule's "
+         "four) packed back to back up to the 131072-token memory budget, "
+         "one modulation vector per sample")
+
+MMDIT_TEXT_TOKENS = 512
+MMDIT_PACKED = Workload(
+    name="mmdit_packed", index=6, B=4, N=MMDIT_TEXT_TOKENS + 16380, D=3072,
+    dtype="bf16", x_kind="offset", mod_std=0.1, dy_std=1e-2,
+    note="4 samples of a two-stream (MMDiT) block, each a 512-token text "
+         "segment followed by a 16380-token video segment; text and video "
+         "tokens have their own modulation vectors, laid out [2, B, D] "
+         "(text of every sample, then video)")
+
 ALL = (TINY_F32, IMAGE_BUCKET, VIDEO_BUCKET, LARGE_MODEL, MIXED_SCHEDULE)
-BY_NAME = {w.name: w for w in ALL}
+PACKED = (PACKED_MIXED, MMDIT_PACKED)
+BY_NAME = {w.name: w for w in ALL + PACKED}
 
 
 def custom(B: int, N: int, D: int, dtype: str, x_kind: str = "normal",
