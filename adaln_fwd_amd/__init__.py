@@ -4,8 +4,10 @@ MI355X (gfx950), as hand-written HIP kernels behind a C ABI
 
 from ._lib import AdalnError, BF16, F32, LIB_PATH, load
 from .ops import (bshape, bwd, bwd_dmod, bwd_dx, bwd_finish, bwd_fused,
-                  bwd_fused_plan, bwd_workspace_bytes, fwd, max_d)
+                  bwd_fused_plan, bwd_segments, bwd_segments_workspace_bytes,
+                  bwd_workspace_bytes, fwd, fwd_segments, max_d)
 
 __all__ = ["AdalnError", "BF16", "F32", "LIB_PATH", "load", "bshape", "bwd",
-           "bwd_dmod", "bwd_dx", "bwd_finish", "bwd_fused", "bwd_fused_plan", "bwd_workspace_bytes",
-           "fwd", "max_d"]
+           "bwd_dmod", "bwd_dx", "bwd_finish", "bwd_fused", "bwd_fused_plan",
+           "bwd_segments", "bwd_segments_workspace_bytes",
+           "bwd_workspace_bytes", "fwd", "fwd_segments", "max_d"]

@@ -41,6 +41,12 @@ SIGNATURES = {
                             _INT, _VP]),
     "adaln_bwd_dmod": (_INT, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _I64,
                               _I64, _I64, _INT, _VP]),
+    "adaln_fwd_segments": (_INT, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                                  _I64, _I64, _I64, _INT, _VP]),
+    "adaln_bwd_segments_workspace_bytes": (_SZ, [_VP, _I64, _I64, _INT]),
+    "adaln_bwd_segments": (_INT, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                                  _SZ, _VP, _VP, _I64, _I64, _I64, _INT,
+                                  _VP]),
     "adaln_bshape": (_I64, [_I64, _I64, _I64, ctypes.c_int32]),
     "adaln_max_d": (_I64, [_INT]),
     "adaln_strerror": (ctypes.c_char_p, [_INT]),

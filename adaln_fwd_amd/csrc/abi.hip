@@ -217,6 +217,38 @@ bool choose_tile_plan(int64_t B, int64_t N, int64_t nvec, TilePlan *plan) {
   return true;
 }
 
+// Segment plans: segment s of N_s rows gets bps_s = max(1, floor(G * N_s /
+// T)) workgroups (none if it is empty), G = 256 * OCC for the kernel's
+// occupancy and T the total rows, so the grid is spread over the segments in
+// proportion to their rows.  Every (segment, workgroup) pair has one partial
+// row: the workspace holds [2][total workgroups][D] floats.
+bool plan_segments(const int64_t *off, const int32_t *mod, int64_t nseg,
+                   int64_t nvec, bool bwd, SegMap *map, int *V_out) {
+  StreamPlan sp;
+  if (!choose_stream_plan(1, 1, nvec, bwd, &sp)) return false;
+  const int occ = bwd ? bwd_stream_occ(sp.V) : fwd_stream_occ(sp.V);
+  const int64_t G = (int64_t)kCUs * occ;
+  const int64_t T = nseg > 0 ? off[nseg] : 0;
+  int64_t wg = 0;
+  map->nseg = (int32_t)nseg;
+  for (int64_t s = 0; s < nseg; ++s) {
+    const int64_t rows = off[s + 1] - off[s];
+    int64_t bps = 0;
+    if (rows > 0) {
+      bps = G * rows / T;
+      if (bps < 1) bps = 1;
+    }
+    map->wg_start[s] = (int32_t)wg;
+    map->row_start[s] = off[s];
+    map->mod[s] = mod ? mod[s] : (int32_t)s;
+    wg += bps;
+  }
+  map->wg_start[nseg] = (int32_t)wg;
+  map->row_start[nseg] = T;
+  *V_out = sp.V;
+  return true;
+}
+
 }  // namespace adaln
 
 using namespace adaln;
@@ -472,4 +504,125 @@ ADALN_API int adaln_bwd(const void *dy, const void *x, const void *scale,
   ADALN_TRY(adaln_bwd_dx(dy, x, scale, mean, rstd, dx, B, N, D, dtype, stream));
   return adaln_bwd_dmod(dy, x, mean, rstd, dscale, dshift, workspace,
                         workspace_bytes_given, B, N, D, dtype, stream);
+}
+
+// ------------------------------------------------------ packed segments
+
+namespace {
+
+// Validates the segment table (host arrays) and the shape.
+int check_segments(const int64_t *off, const int32_t *mod, int64_t nseg,
+                   int64_t nmod, int64_t D, int dtype) {
+  ADALN_TRY(check_shape(1, 0, D, dtype));
+  if (nseg < 0 || nseg > kMaxSegments)
+    return fail(ADALN_ERR_INVALID, "nseg=%lld outside [0, %d]",
+                (long long)nseg, kMaxSegments);
+  if (nmod < 0 || nmod > kMaxB)
+    return fail(ADALN_ERR_INVALID, "nmod=%lld is invalid", (long long)nmod);
+  if (nseg == 0) return ADALN_OK;
+  if (off == nullptr) return fail(ADALN_ERR_INVALID, "seg_offsets is NULL");
+  if (off[0] != 0) return fail(ADALN_ERR_INVALID, "seg_offsets[0] must be 0");
+  for (int64_t s = 0; s < nseg; ++s) {
+    if (off[s + 1] < off[s])
+      return fail(ADALN_ERR_INVALID, "seg_offsets decrease at %lld",
+                  (long long)s);
+    const int64_t m = mod ? mod[s] : s;
+    if (m < 0 || m >= nmod)
+      return fail(ADALN_ERR_INVALID,
+                  "segment %lld uses modulation vector %lld of %lld",
+                  (long long)s, (long long)m, (long long)nmod);
+  }
+  if (off[nseg] > kMaxRows)
+    return fail(ADALN_ERR_INVALID, "more than 2^31-1 rows");
+  if (nmod > kMaxRows / D) return fail(ADALN_ERR_INVALID, "nmod*D too large");
+  return ADALN_OK;
+}
+
+}  // namespace
+
+ADALN_API size_t adaln_bwd_segments_workspace_bytes(const int64_t *seg_offsets,
+                                                    int64_t nseg, int64_t D,
+                                                    int dtype) {
+  if (check_segments(seg_offsets, nullptr, nseg, nseg > 0 ? nseg : 1, D,
+                     dtype) != ADALN_OK)
+    return 0;
+  SegMap map;
+  int V = 0;
+  if (!plan_segments(seg_offsets, nullptr, nseg, D / elems_per_vec(dtype),
+                     true, &map, &V))
+    return 0;
+  ok();
+  return partial_bytes(map.wg_start[nseg], 1, D);
+}
+
+ADALN_API int adaln_fwd_segments(const void *x, const void *scale,
+                                 const void *shift, void *y, float *mean,
+                                 float *rstd, const int64_t *seg_offsets,
+                                 const int32_t *seg_mod, int64_t nseg,
+                                 int64_t nmod, int64_t D, int dtype,
+                                 void *stream) {
+  ADALN_TRY(check_segments(seg_offsets, seg_mod, nseg, nmod, D, dtype));
+  const int64_t T = nseg > 0 ? seg_offsets[nseg] : 0;
+  const bool rows = T > 0;
+  ADALN_TRY(check_ptr(x, rows, "x"));
+  ADALN_TRY(check_ptr(scale, rows, "scale"));
+  ADALN_TRY(check_ptr(shift, rows, "shift"));
+  ADALN_TRY(check_ptr(y, rows, "y"));
+  ADALN_TRY(check_ptr(mean, rows, "mean"));
+  ADALN_TRY(check_ptr(rstd, rows, "rstd"));
+  SegMap map;
+  int V = 0;
+  if (!plan_segments(seg_offsets, seg_mod, nseg, D / elems_per_vec(dtype),
+                     false, &map, &V))
+    return fail(ADALN_ERR_UNSUPPORTED,
+                "D=%lld is too wide for the segment kernels", (long long)D);
+  if (!rows) return ok();
+  const hipError_t e =
+      launch_fwd_segments(dtype, V, map, x, scale, shift, y, mean, rstd,
+                          (int32_t)D, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "adaln_fwd_segments launch");
+  return ok();
+}
+
+ADALN_API int adaln_bwd_segments(const void *dy, const void *x,
+                                 const void *scale, const float *mean,
+                                 const float *rstd, void *dx, float *dscale,
+                                 float *dshift, void *workspace,
+                                 size_t workspace_bytes_given,
+                                 const int64_t *seg_offsets,
+                                 const int32_t *seg_mod, int64_t nseg,
+                                 int64_t nmod, int64_t D, int dtype,
+                                 void *stream) {
+  ADALN_TRY(check_segments(seg_offsets, seg_mod, nseg, nmod, D, dtype));
+  const int64_t T = nseg > 0 ? seg_offsets[nseg] : 0;
+  const bool rows = T > 0;
+  ADALN_TRY(check_ptr(dy, rows, "dy"));
+  ADALN_TRY(check_ptr(x, rows, "x"));
+  ADALN_TRY(check_ptr(scale, rows, "scale"));
+  ADALN_TRY(check_ptr(mean, rows, "mean"));
+  ADALN_TRY(check_ptr(rstd, rows, "rstd"));
+  ADALN_TRY(check_ptr(dx, rows, "dx"));
+  ADALN_TRY(check_ptr(dscale, nmod > 0, "dscale"));
+  ADALN_TRY(check_ptr(dshift, nmod > 0, "dshift"));
+  SegMap map;
+  int V = 0;
+  if (!plan_segments(seg_offsets, seg_mod, nseg, D / elems_per_vec(dtype),
+                     true, &map, &V))
+    return fail(ADALN_ERR_UNSUPPORTED,
+                "D=%lld is too wide for the segment kernels", (long long)D);
+  const size_t need = partial_bytes(map.wg_start[nseg], 1, D);
+  ADALN_TRY(check_workspace(workspace, workspace_bytes_given, need));
+  if (nmod == 0) return ok();
+  float *part_scale = static_cast<float *>(workspace);
+  float *part_shift = part_scale + (size_t)map.wg_start[nseg] * D;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipSuccess;
+  if (rows)
+    e = launch_bwd_segments(dtype, V, map, dy, x, scale, mean, rstd, dx,
+                            part_scale, part_shift, (int32_t)D, s);
+  if (e == hipSuccess)
+    e = launch_finish_segments(part_scale, part_shift, dscale, dshift, map,
+                               (int32_t)nmod, (int32_t)D, s);
+  if (e != hipSuccess) return hip_fail(e, "adaln_bwd_segments launch");
+  return ok();
 }

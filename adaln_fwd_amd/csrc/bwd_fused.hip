@@ -26,14 +26,14 @@
 
 namespace adaln {
 
-template <typename T, int V, bool FULL, int PF, int OCC>
+template <typename T, int V, bool FULL, int PF, int OCC, class Map>
 __global__ __launch_bounds__(kBlock)
 __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void bwd_stream_kernel(
     const T *__restrict__ dy, const T *__restrict__ x,
     const T *__restrict__ scale, const float *__restrict__ mean,
     const float *__restrict__ rstd, T *__restrict__ dx,
     float *__restrict__ part_scale, float *__restrict__ part_shift,
-    int32_t B, int32_t N, int32_t D, int32_t bps, int32_t groups) {
+    int32_t D, Map map) {
   constexpr int E = Elems<T>::value;
   constexpr int kWaves = kBlock / kWave;
   extern __shared__ float stage[];  // one wavefront's accumulators
@@ -41,10 +41,6 @@ __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void bwd_stream_kernel(
   const int wave = wave_id();
   const int nvec = D / E;
   const float inv_d = 1.0f / (float)D;
-  const int slot = blockIdx.x / bps;
-  const int k_in = blockIdx.x - slot * bps;
-  if (slot >= groups) return;  // whole workgroup, before any barrier
-  const int stride = bps * kWaves;
 
   int jv[V];
   bool ok[V];
@@ -54,12 +50,16 @@ __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void bwd_stream_kernel(
     ok[k] = FULL || jv[k] < nvec;
   }
 
-  for (int b = slot; b < B; b += groups) {
-    const int64_t row0 = (int64_t)b * N;
+  // One segment (a sample, or a packed sequence): rows [row0, row0 + N),
+  // modulated by vector `mod`; this workgroup is number k_in of bps and
+  // writes partial row part_row.  Workgroup-uniform (barriers below).
+  for_each_segment(map, [&](int64_t row0, int N, int mod, int k_in, int bps,
+                            int part_row) {
+    const int stride = bps * kWaves;
     Vec sv[V];
 #pragma unroll
     for (int k = 0; k < V; ++k)
-      sv[k] = ok[k] ? load_vec(scale + (int64_t)b * D + (int64_t)jv[k] * E)
+      sv[k] = ok[k] ? load_vec(scale + (int64_t)mod * D + (int64_t)jv[k] * E)
                     : vzero();
 
     float acc_s[V][E], acc_h[V][E];
@@ -176,7 +176,7 @@ __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void bwd_stream_kernel(
       }
     }
     if (wave == 0) {
-      const int64_t po = ((int64_t)b * bps + k_in) * D;
+      const int64_t po = (int64_t)part_row * D;
 #pragma unroll
       for (int k = 0; k < V; ++k) {
         if (ok[k]) {
@@ -193,56 +193,82 @@ __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void bwd_stream_kernel(
         }
       }
     }
-  }
+  });
 }
 
 namespace {
 
-template <typename T, int V, bool FULL>
-hipError_t bwd_stream_v(const StreamPlan &plan, const void *dy, const void *x,
-                        const void *scale, const float *mean,
+template <typename T, int V, bool FULL, class Map>
+hipError_t bwd_stream_v(int64_t grid, const Map &map, const void *dy,
+                        const void *x, const void *scale, const float *mean,
                         const float *rstd, void *dx, float *part_scale,
-                        float *part_shift, int32_t B, int32_t N, int32_t D,
-                        hipStream_t s) {
+                        float *part_shift, int32_t D, hipStream_t s) {
   constexpr int E = Elems<T>::value;
   const size_t lds = (size_t)V * E * 2 * kWave * sizeof(float);
   return launch_kernel_lds(
-      bwd_stream_kernel<T, V, FULL, bwd_stream_pf(V), bwd_stream_occ(V)>,
-      plan.grid, kBlock, lds, s, (const T *)dy, (const T *)x,
-      (const T *)scale, mean, rstd, (T *)dx, part_scale, part_shift, B, N, D,
-      (int32_t)plan.bps, (int32_t)plan.groups);
+      bwd_stream_kernel<T, V, FULL, bwd_stream_pf(V), bwd_stream_occ(V), Map>,
+      grid, kBlock, lds, s, (const T *)dy, (const T *)x, (const T *)scale,
+      mean, rstd, (T *)dx, part_scale, part_shift, D, map);
 }
 
 }  // namespace
 
-#define ADALN_BWD_STREAM_CASE(V_)                                              \
-  if (plan.V == V_) {                                                          \
-    if (full)                                                                  \
-      return dtype == 1                                                        \
-                 ? bwd_stream_v<bf16, V_, true>(plan, dy, x, scale, mean,      \
-                                                rstd, dx, part_scale,          \
-                                                part_shift, B, N, D, stream)   \
-                 : bwd_stream_v<float, V_, true>(plan, dy, x, scale, mean,     \
-                                                 rstd, dx, part_scale,         \
-                                                 part_shift, B, N, D, stream); \
-    return dtype == 1                                                          \
-               ? bwd_stream_v<bf16, V_, false>(plan, dy, x, scale, mean, rstd, \
-                                               dx, part_scale, part_shift, B,  \
-                                               N, D, stream)                   \
-               : bwd_stream_v<float, V_, false>(plan, dy, x, scale, mean,      \
-                                                rstd, dx, part_scale,          \
-                                                part_shift, B, N, D, stream);  \
+#define ADALN_BWD_STREAM_CASE(V_)                                             \
+  if (V == V_) {                                                              \
+    if (full)                                                                 \
+      return dtype == 1                                                       \
+                 ? bwd_stream_v<bf16, V_, true>(grid, map, dy, x, scale,      \
+                                                mean, rstd, dx, part_scale,   \
+                                                part_shift, D, stream)        \
+                 : bwd_stream_v<float, V_, true>(grid, map, dy, x, scale,     \
+                                                 mean, rstd, dx, part_scale,  \
+                                                 part_shift, D, stream);      \
+    return dtype == 1                                                         \
+               ? bwd_stream_v<bf16, V_, false>(grid, map, dy, x, scale, mean, \
+                                               rstd, dx, part_scale,          \
+                                               part_shift, D, stream)         \
+               : bwd_stream_v<float, V_, false>(grid, map, dy, x, scale,      \
+                                                mean, rstd, dx, part_scale,   \
+                                                part_shift, D, stream);       \
   }
+
+namespace {
+
+template <class Map>
+hipError_t bwd_stream_dispatch(int dtype, int V, int64_t grid, const Map &map,
+                               const void *dy, const void *x,
+                               const void *scale, const float *mean,
+                               const float *rstd, void *dx, float *part_scale,
+                               float *part_shift, int32_t D,
+                               hipStream_t stream) {
+  const int E = dtype == 1 ? 8 : 4;
+  const bool full = (int64_t)V * kWave * E == D;
+  ADALN_BWD_STREAM_V(ADALN_BWD_STREAM_CASE)
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
 
 hipError_t launch_bwd_fused(int dtype, const StreamPlan &plan, const void *dy,
                             const void *x, const void *scale,
                             const float *mean, const float *rstd, void *dx,
                             float *part_scale, float *part_shift, int32_t B,
                             int32_t N, int32_t D, hipStream_t stream) {
-  const int E = dtype == 1 ? 8 : 4;
-  const bool full = (int64_t)plan.V * kWave * E == D;
-  ADALN_BWD_STREAM_V(ADALN_BWD_STREAM_CASE)
-  return hipErrorInvalidValue;
+  const UniformMap map{B, N, plan.bps, plan.groups};
+  return bwd_stream_dispatch(dtype, plan.V, plan.grid, map, dy, x, scale,
+                             mean, rstd, dx, part_scale, part_shift, D,
+                             stream);
+}
+
+hipError_t launch_bwd_segments(int dtype, int V, const SegMap &map,
+                               const void *dy, const void *x,
+                               const void *scale, const float *mean,
+                               const float *rstd, void *dx, float *part_scale,
+                               float *part_shift, int32_t D,
+                               hipStream_t stream) {
+  return bwd_stream_dispatch(dtype, V, map.wg_start[map.nseg], map, dy, x,
+                             scale, mean, rstd, dx, part_scale, part_shift, D,
+                             stream);
 }
 
 }  // namespace adaln

@@ -165,6 +165,78 @@ __global__ __launch_bounds__(kFinishWaves * kWave) void dmod_finish_kernel(
   }
 }
 
+// Segment variant: dscale[m, d] = sum over the segments s with mod[s] == m,
+// in index order, of the partial rows of their workgroups
+// [wg_start[s], wg_start[s+1]).  Wavefront w takes rows wg_start[s] + w,
+// + 16, ... of each such segment (up to 8 loads per array in flight), and
+// the 16 wavefront sums are added in wavefront order.
+constexpr int kSegBatch = 8;
+
+__global__ __launch_bounds__(kFinishWaves * kWave) void finish_segments_kernel(
+    const float *__restrict__ part_scale, const float *__restrict__ part_shift,
+    float *__restrict__ dscale, float *__restrict__ dshift, int32_t D,
+    int32_t col_blocks, int64_t total_blocks, SegMap map) {
+  __shared__ float stage[kFinishWaves - 1][2][kWave];
+  const int lane = lane_id();
+  const int wave = wave_id();
+
+  for (int64_t blk = blockIdx.x; blk < total_blocks; blk += gridDim.x) {
+    const int cb = (int)(blk % col_blocks);
+    const int m = (int)(blk / col_blocks);
+    const int c = cb * kWave + lane;
+    const bool ok = c < D;
+    float as = 0.f, ah = 0.f;
+    for (int s = 0; s < map.nseg; ++s) {
+      if (map.mod[s] != m) continue;
+      const int end = map.wg_start[s + 1];
+      for (int w0 = map.wg_start[s] + wave; w0 < end;
+           w0 += kFinishWaves * kSegBatch) {
+        float vs[kSegBatch], vh[kSegBatch];
+#pragma unroll
+        for (int i = 0; i < kSegBatch; ++i) {
+          const int w = w0 + i * kFinishWaves;
+          const bool live = ok && w < end;
+          vs[i] = live ? part_scale[(int64_t)w * D + c] : 0.f;
+          vh[i] = live ? part_shift[(int64_t)w * D + c] : 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < kSegBatch; ++i) {
+          as += vs[i];
+          ah += vh[i];
+        }
+      }
+    }
+    if (wave > 0) {
+      stage[wave - 1][0][lane] = as;
+      stage[wave - 1][1][lane] = ah;
+    }
+    __syncthreads();
+    if (wave == 0 && ok) {
+#pragma unroll
+      for (int w = 0; w < kFinishWaves - 1; ++w) {
+        as += stage[w][0][lane];
+        ah += stage[w][1][lane];
+      }
+      dscale[(int64_t)m * D + c] = as;
+      dshift[(int64_t)m * D + c] = ah;
+    }
+    __syncthreads();
+  }
+}
+
+hipError_t launch_finish_segments(const float *part_scale,
+                                  const float *part_shift, float *dscale,
+                                  float *dshift, const SegMap &map,
+                                  int32_t nmod, int32_t D,
+                                  hipStream_t stream) {
+  const int32_t col_blocks = (D + kWave - 1) / kWave;
+  const int64_t total_blocks = (int64_t)col_blocks * nmod;
+  return launch_kernel_threads(finish_segments_kernel, total_blocks,
+                               kFinishWaves * kWave, stream, part_scale,
+                               part_shift, dscale, dshift, D, col_blocks,
+                               total_blocks, map);
+}
+
 hipError_t launch_dmod_partial(int dtype, const DmodPlan &plan,
                                const void *dy, const void *x,
                                const float *mean, const float *rstd,

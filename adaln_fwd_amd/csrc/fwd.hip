@@ -28,23 +28,18 @@
 
 namespace adaln {
 
-template <typename T, int V, bool FULL, int PF, int OCC>
+template <typename T, int V, bool FULL, int PF, int OCC, class Map>
 __global__ __launch_bounds__(kBlock)
 __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void fwd_stream_kernel(
     const T *__restrict__ x, const T *__restrict__ scale,
     const T *__restrict__ shift, T *__restrict__ y, float *__restrict__ mean,
-    float *__restrict__ rstd, int32_t B, int32_t N, int32_t D, int32_t bps,
-    int32_t groups) {
+    float *__restrict__ rstd, int32_t D, Map map) {
   constexpr int E = Elems<T>::value;
   constexpr int kWaves = kBlock / kWave;
   const int lane = lane_id();
   const int wave = wave_id();
   const int nvec = D / E;
   const float inv_d = 1.0f / (float)D;
-  const int slot = blockIdx.x / bps;
-  const int k_in = blockIdx.x - slot * bps;
-  if (slot >= groups) return;  // whole workgroup: no barriers below
-  const int stride = bps * kWaves;
 
   int jv[V];
   bool ok[V];
@@ -54,12 +49,15 @@ __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void fwd_stream_kernel(
     ok[k] = FULL || jv[k] < nvec;
   }
 
-  for (int b = slot; b < B; b += groups) {
-    const int64_t row0 = (int64_t)b * N;
+  // One segment (a sample, or a packed sequence): rows [row0, row0 + N),
+  // modulated by vector `mod`; this workgroup is number k_in of bps.
+  for_each_segment(map, [&](int64_t row0, int N, int mod, int k_in, int bps,
+                            int) {
+    const int stride = bps * kWaves;
     Vec sv[V], hv[V];
 #pragma unroll
     for (int k = 0; k < V; ++k) {
-      const int64_t c = (int64_t)b * D + (int64_t)jv[k] * E;
+      const int64_t c = (int64_t)mod * D + (int64_t)jv[k] * E;
       sv[k] = ok[k] ? load_vec(scale + c) : vzero();
       hv[k] = ok[k] ? load_vec(shift + c) : vzero();
     }
@@ -139,7 +137,7 @@ __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void fwd_stream_kernel(
         do_row(xa, n);
       }
     }
-  }
+  });
 }
 
 template <typename T, int V, bool FULL>
@@ -288,42 +286,65 @@ hipError_t fwd_v(const TilePlan &plan, const void *x, const void *scale,
       (int32_t)plan.n_tile, (int32_t)plan.n_tiles, total);
 }
 
-template <typename T, int V, bool FULL>
-hipError_t fwd_stream_v(const StreamPlan &plan, const void *x,
+template <typename T, int V, bool FULL, class Map>
+hipError_t fwd_stream_v(int64_t grid, const Map &map, const void *x,
                         const void *scale, const void *shift, void *y,
-                        float *mean, float *rstd, int32_t B, int32_t N,
-                        int32_t D, hipStream_t s) {
+                        float *mean, float *rstd, int32_t D, hipStream_t s) {
   return launch_kernel(
-      fwd_stream_kernel<T, V, FULL, fwd_stream_pf(V), fwd_stream_occ(V)>,
-      plan.grid, s, (const T *)x, (const T *)scale, (const T *)shift, (T *)y,
-      mean, rstd, B, N, D, (int32_t)plan.bps, (int32_t)plan.groups);
+      fwd_stream_kernel<T, V, FULL, fwd_stream_pf(V), fwd_stream_occ(V), Map>,
+      grid, s, (const T *)x, (const T *)scale, (const T *)shift, (T *)y, mean,
+      rstd, D, map);
 }
 
 }  // namespace
 
-#define ADALN_FWD_STREAM_CASE(V_)                                             \
-  if (plan.V == V_) {                                                         \
-    if (full)                                                                 \
-      return dtype == 1                                                       \
-                 ? fwd_stream_v<bf16, V_, true>(plan, x, scale, shift, y,     \
-                                                mean, rstd, B, N, D, stream)  \
-                 : fwd_stream_v<float, V_, true>(plan, x, scale, shift, y,    \
-                                                 mean, rstd, B, N, D, stream);\
-    return dtype == 1                                                         \
-               ? fwd_stream_v<bf16, V_, false>(plan, x, scale, shift, y,      \
-                                               mean, rstd, B, N, D, stream)   \
-               : fwd_stream_v<float, V_, false>(plan, x, scale, shift, y,     \
-                                                mean, rstd, B, N, D, stream); \
+#define ADALN_FWD_STREAM_CASE(V_)                                            \
+  if (V == V_) {                                                             \
+    if (full)                                                                \
+      return dtype == 1 ? fwd_stream_v<bf16, V_, true>(grid, map, x, scale,   \
+                                                       shift, y, mean, rstd,  \
+                                                       D, stream)             \
+                        : fwd_stream_v<float, V_, true>(grid, map, x, scale,  \
+                                                        shift, y, mean, rstd, \
+                                                        D, stream);           \
+    return dtype == 1 ? fwd_stream_v<bf16, V_, false>(grid, map, x, scale,    \
+                                                      shift, y, mean, rstd,   \
+                                                      D, stream)              \
+                      : fwd_stream_v<float, V_, false>(grid, map, x, scale,   \
+                                                       shift, y, mean, rstd,  \
+                                                       D, stream);            \
   }
+
+namespace {
+
+template <class Map>
+hipError_t fwd_stream_dispatch(int dtype, int V, int64_t grid, const Map &map,
+                               const void *x, const void *scale,
+                               const void *shift, void *y, float *mean,
+                               float *rstd, int32_t D, hipStream_t stream) {
+  const int E = dtype == 1 ? 8 : 4;
+  const bool full = (int64_t)V * kWave * E == D;
+  ADALN_STREAM_V(ADALN_FWD_STREAM_CASE)
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
 
 hipError_t launch_fwd_stream(int dtype, const StreamPlan &plan, const void *x,
                              const void *scale, const void *shift, void *y,
                              float *mean, float *rstd, int32_t B, int32_t N,
                              int32_t D, hipStream_t stream) {
-  const int E = dtype == 1 ? 8 : 4;
-  const bool full = (int64_t)plan.V * kWave * E == D;
-  ADALN_STREAM_V(ADALN_FWD_STREAM_CASE)
-  return hipErrorInvalidValue;
+  const UniformMap map{B, N, plan.bps, plan.groups};
+  return fwd_stream_dispatch(dtype, plan.V, plan.grid, map, x, scale, shift,
+                             y, mean, rstd, D, stream);
+}
+
+hipError_t launch_fwd_segments(int dtype, int V, const SegMap &map,
+                               const void *x, const void *scale,
+                               const void *shift, void *y, float *mean,
+                               float *rstd, int32_t D, hipStream_t stream) {
+  return fwd_stream_dispatch(dtype, V, map.wg_start[map.nseg], map, x, scale,
+                             shift, y, mean, rstd, D, stream);
 }
 
 #define ADALN_FWD_TILE_CASE(V_)                                                \

@@ -6,6 +6,7 @@
 
 #include <tuple>
 #include <type_traits>
+#include <utility>
 
 namespace adaln {
 
@@ -44,6 +45,60 @@ struct StreamPlan {
   int bps = 0;     // workgroups per sample (partial rows per sample)
   int groups = 0;  // samples in flight
 };
+
+// How a stream kernel's workgroups map to token rows.  UniformMap: B samples
+// of N rows, `groups` samples in flight, bps workgroups per sample; a
+// workgroup visits samples slot, slot + groups, ...  SegMap: up to
+// kMaxSegments segments of any length, segment s owning the workgroups
+// [wg_start[s], wg_start[s+1]) and the rows [row_start[s], row_start[s+1]),
+// modulated by vector mod[s].  Either way each (segment, workgroup) pair
+// writes one partial row: row part_row of the backward's workspace.
+struct UniformMap {
+  int32_t B;
+  int32_t N;
+  int32_t bps;
+  int32_t groups;
+};
+
+constexpr int kMaxSegments = 128;
+
+struct SegMap {
+  int32_t nseg;
+  int32_t wg_start[kMaxSegments + 1];
+  int32_t mod[kMaxSegments];
+  int64_t row_start[kMaxSegments + 1];
+};
+
+// Calls f(row0, rows, mod, k_in, bps, part_row) for each segment the calling
+// workgroup works on.  Workgroup-uniform, so a kernel may place barriers in
+// f.
+template <class F>
+__device__ __forceinline__ void for_each_segment(const UniformMap &m, F &&f) {
+  const int slot = blockIdx.x / m.bps;
+  const int k_in = blockIdx.x - slot * m.bps;
+  if (slot >= m.groups) return;
+  for (int b = slot; b < m.B; b += m.groups)
+    f((int64_t)b * m.N, m.N, b, k_in, m.bps, b * m.bps + k_in);
+}
+
+template <class F>
+__device__ __forceinline__ void for_each_segment(const SegMap &m, F &&f) {
+  const int bid = blockIdx.x;
+  if (bid >= m.wg_start[m.nseg]) return;
+  int lo = 0, hi = m.nseg - 1;  // last s with wg_start[s] <= bid
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) / 2;
+    if (m.wg_start[mid] <= bid)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  // segments without rows own no workgroups, so wg_start[lo + 1] > bid
+  const int s = lo;
+  const int bps = m.wg_start[s + 1] - m.wg_start[s];
+  f(m.row_start[s], (int)(m.row_start[s + 1] - m.row_start[s]), m.mod[s],
+    bid - m.wg_start[s], bps, bid);
+}
 
 #define ADALN_STREAM_V(X) X(1) X(2) X(3) X(4) X(5) X(6) X(8) X(10) X(12) X(16)
 #define ADALN_BWD_STREAM_V(X) X(1) X(2) X(3) X(4) X(5) X(6) X(8) X(10)
@@ -201,6 +256,27 @@ hipError_t launch_fwd_stream(int dtype, const StreamPlan &plan, const void *x,
                              const void *scale, const void *shift, void *y,
                              float *mean, float *rstd, int32_t B, int32_t N,
                              int32_t D, hipStream_t stream);
+
+hipError_t launch_fwd_segments(int dtype, int V, const SegMap &map,
+                               const void *x, const void *scale,
+                               const void *shift, void *y, float *mean,
+                               float *rstd, int32_t D, hipStream_t stream);
+
+hipError_t launch_bwd_segments(int dtype, int V, const SegMap &map,
+                               const void *dy, const void *x,
+                               const void *scale, const float *mean,
+                               const float *rstd, void *dx, float *part_scale,
+                               float *part_shift, int32_t D,
+                               hipStream_t stream);
+
+// dscale[m] / dshift[m] = sum over the segments s with mod[s] == m, in index
+// order, of their workgroups' partial rows, in order (zero for an m no
+// segment uses).
+hipError_t launch_finish_segments(const float *part_scale,
+                                  const float *part_shift, float *dscale,
+                                  float *dshift, const SegMap &map,
+                                  int32_t nmod, int32_t D,
+                                  hipStream_t stream);
 
 hipError_t launch_bwd_fused(int dtype, const StreamPlan &plan, const void *dy,
                             const void *x, const void *scale,

@@ -243,6 +243,129 @@ def bwd_fused_plan(B: int, N: int, D: int, dtype: torch.dtype) -> dict:
                 partial_rows=out[3])
 
 
+class _SegTable:
+    """Host copies of a segment table in the ABI's layout (int64 offsets,
+    int32 modulation indices), kept alive for the duration of a call."""
+
+    def __init__(self, seg_offsets, seg_mod):
+        offs = [int(v) for v in seg_offsets]
+        if len(offs) < 1:
+            raise ValueError("seg_offsets needs at least one entry (0)")
+        self.nseg = len(offs) - 1
+        self.rows = offs[-1]
+        self.offsets = (ctypes.c_int64 * len(offs))(*offs)
+        self.mod = None
+        if seg_mod is not None:
+            mods = [int(v) for v in seg_mod]
+            if len(mods) != self.nseg:
+                raise ValueError(f"seg_mod has {len(mods)} entries for "
+                                 f"{self.nseg} segments")
+            self.mod = (ctypes.c_int32 * max(len(mods), 1))(*mods)
+
+    @property
+    def offsets_ptr(self):
+        return ctypes.cast(self.offsets, ctypes.c_void_p)
+
+    @property
+    def mod_ptr(self):
+        return None if self.mod is None else ctypes.cast(self.mod,
+                                                         ctypes.c_void_p)
+
+
+def bwd_segments_workspace_bytes(seg_offsets, D: int,
+                                 dtype: torch.dtype) -> int:
+    tab = _SegTable(seg_offsets, None)
+    return int(_lib.load().adaln_bwd_segments_workspace_bytes(
+        tab.offsets_ptr, tab.nseg, D, _DTYPES.get(dtype, -1)))
+
+
+def fwd_segments(x: torch.Tensor, scale: torch.Tensor, shift: torch.Tensor,
+                 seg_offsets, seg_mod=None, *, y=None, mean=None, rstd=None,
+                 stream=None):
+    """Packed variable-length forward: x [T, D] holds the token rows of
+    several segments back to back, segment s being rows
+    seg_offsets[s] .. seg_offsets[s+1]-1 and modulated by
+    scale/shift[seg_mod[s]] (row s if seg_mod is None); scale, shift:
+    [nmod, D].  Returns (y, mean, rstd) with mean, rstd float32 [T]."""
+    tab = _SegTable(seg_offsets, seg_mod)
+    if x.dim() != 2:
+        raise ValueError(f"x must be [T, D], got shape {tuple(x.shape)}")
+    T, D = x.shape
+    if T != tab.rows:
+        raise ValueError(f"x has {T} rows, seg_offsets ends at {tab.rows}")
+    nmod = scale.shape[0] if scale.dim() == 2 else -1
+    dev, dt = x.device, x.dtype
+    code = _code(x)
+    _check(x, "x", (T, D), dt, dev)
+    _check(scale, "scale", (nmod, D), dt, dev)
+    _check(shift, "shift", (nmod, D), dt, dev)
+    if y is None:
+        y = torch.empty_like(x)
+    if mean is None:
+        mean = torch.empty(T, dtype=torch.float32, device=dev)
+    if rstd is None:
+        rstd = torch.empty(T, dtype=torch.float32, device=dev)
+    _check(y, "y", (T, D), dt, dev)
+    _check(mean, "mean", (T,), torch.float32, dev)
+    _check(rstd, "rstd", (T,), torch.float32, dev)
+    lib = _lib.load()
+    with torch.cuda.device(dev):
+        rc = lib.adaln_fwd_segments(_ptr(x), _ptr(scale), _ptr(shift),
+                                    _ptr(y), _ptr(mean), _ptr(rstd),
+                                    tab.offsets_ptr, tab.mod_ptr, tab.nseg,
+                                    nmod, D, code, _stream(dev, stream))
+    _lib.check(rc, "adaln_fwd_segments")
+    return y, mean, rstd
+
+
+def bwd_segments(dy, x, scale, mean, rstd, seg_offsets, seg_mod=None, *,
+                 dx=None, dscale=None, dshift=None, workspace=None,
+                 stream=None):
+    """Backward of :func:`fwd_segments`; returns (dx, dscale, dshift) with
+    dscale, dshift float32 [nmod, D] summed over every segment that uses
+    each modulation vector."""
+    tab = _SegTable(seg_offsets, seg_mod)
+    if x.dim() != 2:
+        raise ValueError(f"x must be [T, D], got shape {tuple(x.shape)}")
+    T, D = x.shape
+    if T != tab.rows:
+        raise ValueError(f"x has {T} rows, seg_offsets ends at {tab.rows}")
+    nmod = scale.shape[0] if scale.dim() == 2 else -1
+    dev, dt = x.device, x.dtype
+    code = _code(x)
+    _check(dy, "dy", (T, D), dt, dev)
+    _check(x, "x", (T, D), dt, dev)
+    _check(scale, "scale", (nmod, D), dt, dev)
+    _check(mean, "mean", (T,), torch.float32, dev)
+    _check(rstd, "rstd", (T,), torch.float32, dev)
+    if dx is None:
+        dx = torch.empty_like(x)
+    if dscale is None:
+        dscale = torch.empty(nmod, D, dtype=torch.float32, device=dev)
+    if dshift is None:
+        dshift = torch.empty(nmod, D, dtype=torch.float32, device=dev)
+    _check(dx, "dx", (T, D), dt, dev)
+    _check(dscale, "dscale", (nmod, D), torch.float32, dev)
+    _check(dshift, "dshift", (nmod, D), torch.float32, dev)
+    lib = _lib.load()
+    need = int(lib.adaln_bwd_segments_workspace_bytes(tab.offsets_ptr,
+                                                      tab.nseg, D, code))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    if workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous tensor on {dev}")
+    wbytes = workspace.numel() * workspace.element_size()
+    with torch.cuda.device(dev):
+        rc = lib.adaln_bwd_segments(_ptr(dy), _ptr(x), _ptr(scale),
+                                    _ptr(mean), _ptr(rstd), _ptr(dx),
+                                    _ptr(dscale), _ptr(dshift),
+                                    _ptr(workspace), wbytes, tab.offsets_ptr,
+                                    tab.mod_ptr, tab.nseg, nmod, D, code,
+                                    _stream(dev, stream))
+    _lib.check(rc, "adaln_bwd_segments")
+    return dx, dscale, dshift
+
+
 def bshape(S: int, m_mem: int, m_comp: int, p: int) -> int:
     """Dual-constraint bucket batch size (host integer arithmetic in the
     library); raises on invalid arguments."""

@@ -166,6 +166,42 @@ int adaln_bwd_dmod(const void *dy, const void *x, const float *mean,
                    int64_t N, int64_t D, int dtype, void *stream);
 
 /*
+ * Packed variable-length AdaLN: the token rows of several sequences
+ * ("segments") concatenated in one [T, D] tensor and processed in one launch
+ * per pass -- mixed-length samples of a bucket without padding, or the text
+ * and video token segments of MMDiT samples, each with its own modulation.
+ *   seg_offsets  host int64 [nseg+1]: segment s is rows [off[s], off[s+1]);
+ *                off[0] = 0, non-decreasing, T = off[nseg] < 2^31
+ *   seg_mod      host int32 [nseg] or NULL: segment s is modulated by
+ *                scale[seg_mod[s]], shift[seg_mod[s]] (NULL: vector s)
+ *   nseg         0 .. 128 segments;  nmod: number of modulation vectors
+ *   x, y, dy, dx [T, D] dtype;  mean, rstd [T] f32
+ *   scale, shift [nmod, D] dtype;  dscale, dshift [nmod, D] f32, where
+ *                dscale[m] sums dy*xhat over every row of every segment
+ *                with seg_mod[s] == m (zero for an unused m)
+ * The per-row math is that of adaln_fwd / adaln_bwd.  Rows of up to 1024
+ * (forward) / 640 (backward) vectors; wider rows return
+ * ADALN_ERR_UNSUPPORTED.  The workspace of adaln_bwd_segments is
+ * adaln_bwd_segments_workspace_bytes(seg_offsets, nseg, D, dtype) bytes; the
+ * host arrays are read during the call only.
+ */
+int adaln_fwd_segments(const void *x, const void *scale, const void *shift,
+                       void *y, float *mean, float *rstd,
+                       const int64_t *seg_offsets, const int32_t *seg_mod,
+                       int64_t nseg, int64_t nmod, int64_t D, int dtype,
+                       void *stream);
+
+size_t adaln_bwd_segments_workspace_bytes(const int64_t *seg_offsets,
+                                          int64_t nseg, int64_t D, int dtype);
+
+int adaln_bwd_segments(const void *dy, const void *x, const void *scale,
+                       const float *mean, const float *rstd, void *dx,
+                       float *dscale, float *dshift, void *workspace,
+                       size_t workspace_bytes, const int64_t *seg_offsets,
+                       const int32_t *seg_mod, int64_t nseg, int64_t nmod,
+                       int64_t D, int dtype, void *stream);
+
+/*
  * Dual-constraint bucket batch size of section 2.A:
  *     max(1, min(floor(m_mem / S), floor(m_comp / S^p)))
  * in exact integer arithmetic.  When S^p exceeds the int64 range the compute

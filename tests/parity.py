@@ -176,3 +176,70 @@ def sample_rows(total: int, k: int, seed: int = 0) -> np.ndarray:
     edge = np.r_[np.arange(min(8, total)), np.arange(max(0, total - 8), total)]
     rnd = g.choice(total, size=min(k, total), replace=False)
     return np.unique(np.r_[edge, rnd])
+
+
+# ------------------------------------------------------- packed segments
+
+def packed_to_device(inp, device="cuda"):
+    return {k: (None if v is None else v.to(device))
+            for k, v in (("x", inp.x), ("scale", inp.scale),
+                         ("shift", inp.shift), ("dy", inp.dy))}
+
+
+def gpu_packed(inp, dev: Dict[str, torch.Tensor], stream=None):
+    """adaln_fwd_segments then adaln_bwd_segments on a packed layout."""
+    import adaln_fwd_amd as A
+    off, mod = inp.seg_offsets, inp.seg_mod
+    y, mean, rstd = A.fwd_segments(dev["x"], dev["scale"], dev["shift"], off,
+                                   mod, stream=stream)
+    dx, dscale, dshift = A.bwd_segments(dev["dy"], dev["x"], dev["scale"],
+                                        mean, rstd, off, mod, stream=stream)
+    return dict(y=y, mean=mean, rstd=rstd, dx=dx, dscale=dscale,
+                dshift=dshift)
+
+
+def row_mods(inp) -> np.ndarray:
+    """Modulation vector of every token row of a packed layout."""
+    lengths = np.diff(inp.seg_offsets)
+    idx = (np.arange(lengths.size) if inp.seg_mod is None
+           else np.asarray(inp.seg_mod))
+    return np.repeat(idx, lengths).astype(np.int64)
+
+
+def compare_packed_full(inp, out, dtype: str, with_rows: bool = True):
+    import oracle
+    off, mod = inp.seg_offsets, inp.seg_mod
+    reps = []
+    if with_rows:
+        y, mean, rstd = oracle.fwd_segments(inp.x, inp.scale, inp.shift, off,
+                                            mod)
+        dx, ds, dh = oracle.bwd_segments(inp.dy, inp.x, inp.scale, off, mod)
+        reps += check_out("y", out["y"], y, dtype)
+        reps += check_out("dx", out["dx"], dx, dtype)
+        reps += check_stats(out["mean"], out["rstd"], mean, rstd, inp.x)
+    else:
+        _, ds, dh = oracle.bwd_segments(inp.dy, inp.x, inp.scale, off, mod,
+                                        want_dx=False)
+    reps.append(check_dmod("dscale", out["dscale"], ds))
+    reps.append(check_dmod("dshift", out["dshift"], dh))
+    return reps
+
+
+def compare_packed_rows(inp, got, rows: np.ndarray, dtype: str):
+    """GPU outputs on sampled rows of a packed layout (``got`` holds y, dx,
+    mean and rstd of just those rows, in order) against the oracle, which
+    takes each row as a one-row segment with its modulation vector."""
+    import oracle
+    rows = np.asarray(rows, dtype=np.int64)
+    t = torch.from_numpy(rows)
+    xr, gr = inp.x[t], inp.dy[t]
+    mods = row_mods(inp)[rows].astype(np.int32)
+    off = np.arange(rows.size + 1, dtype=np.int64)
+    y, mean, rstd = oracle.fwd_segments(xr, inp.scale, inp.shift, off, mods)
+    dx, _, _ = oracle.bwd_segments(gr, xr, inp.scale, off, mods,
+                                   want_dmod=False)
+    reps = []
+    reps += check_out("y", got["y"], y, dtype)
+    reps += check_out("dx", got["dx"], dx, dtype)
+    reps += check_stats(got["mean"], got["rstd"], mean, rstd, xr)
+    return reps

@@ -125,6 +125,85 @@ def test_workspace_bytes(lib):
         assert 1 <= n_tiles <= N
 
 
+def _table(offs, mods=None):
+    o = (ctypes.c_int64 * len(offs))(*offs)
+    m = None if mods is None else (ctypes.c_int32 * len(mods))(*mods)
+    return (ctypes.cast(o, ctypes.c_void_p),
+            None if m is None else ctypes.cast(m, ctypes.c_void_p), (o, m))
+
+
+def test_segments_validation(lib):
+    _no_gpu()
+    p = 0x1000
+    f = lib.adaln_fwd_segments
+    off, mod, keep = _table([0, 100, 250], [1, 0])
+    assert f(p, p, p, p, p, p, off, mod, 2, 2, 1536, 7, None) == _lib.ERR_DTYPE
+    assert f(p, p, p, p, p, p, off, mod, 2, 2, 1540, 1, None) == _lib.ERR_ALIGN
+    assert f(p + 8, p, p, p, p, p, off, mod, 2, 2, 1536, 1,
+             None) == _lib.ERR_ALIGN
+    assert f(p, p, p, None, p, p, off, mod, 2, 2, 1536, 1,
+             None) == _lib.ERR_INVALID
+    # modulation index out of range
+    assert f(p, p, p, p, p, p, off, mod, 2, 1, 1536, 1,
+             None) == _lib.ERR_INVALID
+    assert b"modulation" in lib.adaln_last_error()
+    # identity table needs nmod >= nseg
+    assert f(p, p, p, p, p, p, off, None, 2, 1, 1536, 1,
+             None) == _lib.ERR_INVALID
+    # table errors: NULL, first offset, decreasing, too many segments
+    assert f(p, p, p, p, p, p, None, None, 2, 2, 1536, 1,
+             None) == _lib.ERR_INVALID
+    bad, _, k2 = _table([5, 100, 250])
+    assert f(p, p, p, p, p, p, bad, None, 2, 2, 1536, 1,
+             None) == _lib.ERR_INVALID
+    dec, _, k3 = _table([0, 100, 50])
+    assert f(p, p, p, p, p, p, dec, None, 2, 2, 1536, 1,
+             None) == _lib.ERR_INVALID
+    many, _, k4 = _table(list(range(130)))
+    assert f(p, p, p, p, p, p, many, None, 129, 129, 1536, 1,
+             None) == _lib.ERR_INVALID
+    # rows wider than the segment kernels take
+    assert f(p, p, p, p, p, p, off, mod, 2, 2, 16384, 1,
+             None) == _lib.ERR_UNSUPPORTED
+    g = lib.adaln_bwd_segments
+    need = lib.adaln_bwd_segments_workspace_bytes(off, 2, 1536, 1)
+    assert need > 0
+    assert g(p, p, p, p, p, p, p, p, p, need - 4, off, mod, 2, 2, 1536, 1,
+             None) == _lib.ERR_WORKSPACE
+    assert g(p, p, p, p, p, p, p, None, p, need, off, mod, 2, 2, 1536, 1,
+             None) == _lib.ERR_INVALID
+    assert g(p, p, p, p, p, p, p, p, p, need, off, mod, 2, 2, 8192, 1,
+             None) == _lib.ERR_UNSUPPORTED
+    # nothing to do: no segments and no modulation vectors
+    assert f(None, None, None, None, None, None, None, None, 0, 0, 64, 1,
+             None) == _lib.OK
+    assert g(None, None, None, None, None, None, None, None, None, 0, None,
+             None, 0, 0, 64, 1, None) == _lib.OK
+    del keep, k2, k3, k4
+
+
+def test_segments_workspace_bytes(lib):
+    ws = lib.adaln_bwd_segments_workspace_bytes
+    for offs, D, dt in [([0, 100, 250], 1536, 1), ([0, 32760, 32760, 33272],
+                                                    3072, 1),
+                        ([0] + [1560 * (i + 1) for i in range(84)], 3072, 1),
+                        ([0, 7], 64, 0)]:
+        off, _, keep = _table(offs)
+        nseg = len(offs) - 1
+        n = ws(off, nseg, D, dt)
+        assert n % (2 * 4 * D) == 0
+        wgs = n // (2 * 4 * D)
+        busy = sum(1 for a, b in zip(offs, offs[1:]) if b > a)
+        # at least one workgroup per non-empty segment, at most the grid
+        # plus one per segment
+        assert busy <= wgs <= 1024 + nseg
+        del keep
+    off, _, keep = _table([0, 10])
+    assert ws(off, 1, 60, 1) == 0            # invalid: 0
+    assert ws(off, 200, 64, 1) == 0
+    assert ws(None, 0, 64, 1) == 0           # no segments: no partials
+
+
 def test_max_d(lib):
     assert lib.adaln_max_d(1) == 32768
     assert lib.adaln_max_d(0) == 16384

@@ -1,0 +1,191 @@
+"""Packed variable-length entry points (adaln_fwd_segments,
+adaln_bwd_segments) against the oracle's segment functions: several
+sequences back to back in one [T, D] tensor, each with its own modulation
+vector -- mixed-length samples packed without padding, and the text and
+video token segments of two-stream (MMDiT) samples.
+
+Small layouts are compared in full (every output element); the full-size
+packed mixed-length pack and the MMDiT layout on sampled rows, with dscale
+and dshift compared in full.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from synth import workloads as W
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(f"[segments] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module")
+def A():
+    import adaln_fwd_amd
+    adaln_fwd_amd.load()
+    return adaln_fwd_amd
+
+
+def _wl(D, dtype, x_kind="offset", dy_std=1e-2):
+    return W.custom(1, 1, D, dtype, x_kind=x_kind, dy_std=dy_std, index=107)
+
+
+SMALL = [
+    # D, dtype, lengths, seg_mod (None: identity), nmod
+    (256, "f32", [300, 0, 1, 77, 1024], [2, 0, 2, 1, 0], 4),   # vector 3 unused
+    (1536, "bf16", [1560, 390, 5], None, 3),
+    (520, "bf16", [17, 250, 3], [0, 0, 0], 1),                  # ragged row
+    (2560, "f32", [100, 200], [1, 0], 2),                       # widest f32 bwd
+    (5120, "bf16", [40, 1, 333], None, 3),                      # widest bf16 bwd
+    (64, "f32", [2000, 7], None, 2),                            # row of 16 vectors
+    (1536, "bf16", [20000] + [1] * 40, [0] * 41, 1),            # one long, many tiny
+]
+
+
+@pytest.mark.parametrize("case", range(len(SMALL)))
+def test_small_layouts_full(A, case):
+    D, dt, lengths, mods, nmod = SMALL[case]
+    _say(f"small case {case}: D={D} {dt} nseg={len(lengths)} "
+         f"T={sum(lengths)} nmod={nmod}")
+    inp = synth.make_packed(_wl(D, dt), lengths, mods, nmod=nmod, seed=case)
+    out = P.gpu_packed(inp, P.packed_to_device(inp))
+    torch.cuda.synchronize()
+    out = {k: v.cpu() for k, v in out.items()}
+    for r in P.compare_packed_full(inp, out, dt):
+        _say(f"  {r}")
+
+
+def test_128_segments_random_table(A):
+    """The largest table: 128 segments of 0..300 rows (some empty), random
+    modulation indices (some vectors unused), inside guard bytes."""
+    g = np.random.default_rng(3)
+    lengths = g.integers(0, 300, size=128)
+    lengths[[5, 17, 90]] = 0
+    mods = g.integers(0, 60, size=128).astype(np.int32)
+    D = 3072
+    _say(f"128 segments, T={lengths.sum()} D={D}")
+    inp = synth.make_packed(_wl(D, "bf16"), lengths, mods, nmod=64, seed=9)
+    dev = P.packed_to_device(inp)
+    T, nmod = int(lengths.sum()), 64
+    pad = 4096
+
+    def guarded(n, dtype):
+        buf = torch.full((n + 2 * pad,), -7.0, dtype=dtype, device="cuda")
+        return buf, buf[pad:pad + n]
+
+    yb, y = guarded(T * D, torch.bfloat16)
+    mb, mean = guarded(T, torch.float32)
+    rb, rstd = guarded(T, torch.float32)
+    xb, dx = guarded(T * D, torch.bfloat16)
+    sb, dscale = guarded(nmod * D, torch.float32)
+    hb, dshift = guarded(nmod * D, torch.float32)
+    need = A.bwd_segments_workspace_bytes(inp.seg_offsets, D, torch.bfloat16)
+    wb, ws = guarded(need // 4, torch.float32)
+    A.fwd_segments(dev["x"], dev["scale"], dev["shift"], inp.seg_offsets,
+                   inp.seg_mod, y=y.view(T, D), mean=mean, rstd=rstd)
+    A.bwd_segments(dev["dy"], dev["x"], dev["scale"], mean, rstd,
+                   inp.seg_offsets, inp.seg_mod, dx=dx.view(T, D),
+                   dscale=dscale.view(nmod, D), dshift=dshift.view(nmod, D),
+                   workspace=ws)
+    torch.cuda.synchronize()
+    for buf in (yb, mb, rb, xb, sb, hb, wb):
+        assert torch.all(buf[:pad] == -7.0) and torch.all(buf[-pad:] == -7.0)
+    out = dict(y=y.view(T, D).cpu(), mean=mean.cpu(), rstd=rstd.cpu(),
+               dx=dx.view(T, D).cpu(), dscale=dscale.view(nmod, D).cpu(),
+               dshift=dshift.view(nmod, D).cpu())
+    for r in P.compare_packed_full(inp, out, "bf16"):
+        _say(f"  {r}")
+    unused = sorted(set(range(nmod)) - set(int(m) for m in mods))
+    assert unused and not out["dscale"][unused].any()
+
+
+def test_uniform_layout_matches_batched_path(A):
+    """B equal segments with the identity table are the batched layout: the
+    per-row outputs are the same kernels' arithmetic, bit for bit; dscale
+    and dshift are sums in another grouping, so within tolerance."""
+    B, N, D = 6, 1000, 1536
+    _say(f"uniform layout B={B} N={N} D={D}")
+    inp = synth.make_packed(_wl(D, "bf16"), [N] * B, seed=4)
+    dev = P.packed_to_device(inp)
+    seg = P.gpu_packed(inp, dev)
+    bat = dict(x=dev["x"].view(B, N, D), scale=dev["scale"],
+               shift=dev["shift"], dy=dev["dy"].view(B, N, D))
+    ref = P.gpu_fwd_bwd(bat)
+    torch.cuda.synchronize()
+    assert torch.equal(seg["y"], ref["y"].view(B * N, D))
+    assert torch.equal(seg["mean"], ref["mean"].view(-1))
+    assert torch.equal(seg["rstd"], ref["rstd"].view(-1))
+    assert torch.equal(seg["dx"], ref["dx"].view(B * N, D))
+    P.check_dmod("dscale", seg["dscale"].cpu(), ref["dscale"].cpu().double())
+    P.check_dmod("dshift", seg["dshift"].cpu(), ref["dshift"].cpu().double())
+
+
+def test_deterministic(A):
+    lengths, mods = [700, 3, 4096, 0, 129], [3, 1, 0, 2, 1]
+    inp = synth.make_packed(_wl(3072, "bf16"), lengths, mods, nmod=4, seed=2)
+    dev = P.packed_to_device(inp)
+    a = P.gpu_packed(inp, dev)
+    b = P.gpu_packed(inp, dev)
+    torch.cuda.synchronize()
+    for k in a:
+        assert torch.equal(a[k], b[k]), k
+
+
+def test_wide_rows_rejected(A, oracle_mod):
+    inp = synth.make_packed(_wl(8192, "bf16"), [10, 20], seed=1)
+    dev = P.packed_to_device(inp)
+    y, mean, rstd = A.fwd_segments(dev["x"], dev["scale"], dev["shift"],
+                                   inp.seg_offsets)
+    torch.cuda.synchronize()
+    out = dict(y=y.cpu(), mean=mean.cpu(), rstd=rstd.cpu())
+    ref_y, ref_m, ref_r = oracle_mod.fwd_segments(inp.x, inp.scale,
+                                                  inp.shift, inp.seg_offsets)
+    P.check_out("y", out["y"], ref_y, "bf16")
+    P.check_stats(out["mean"], out["rstd"], ref_m, ref_r, inp.x)
+    with pytest.raises(A.AdalnError) as e:
+        A.bwd_segments(dev["dy"], dev["x"], dev["scale"], mean, rstd,
+                       inp.seg_offsets)
+    assert e.value.code == -6
+
+
+def _full_size(A, inp, name, k_rows):
+    T = int(inp.seg_offsets[-1])
+    D = inp.x.shape[1]
+    _say(f"{name}: nseg={len(inp.seg_offsets) - 1} T={T} D={D}")
+    dev = P.packed_to_device(inp)
+    out = P.gpu_packed(inp, dev)
+    rows = P.sample_rows(T, k_rows, seed=1)
+    # every segment's first and last row too
+    ends = np.r_[inp.seg_offsets[:-1], inp.seg_offsets[1:] - 1]
+    ends = ends[(ends >= 0) & (ends < T)]
+    rows = np.unique(np.r_[rows, ends])
+    idx = torch.from_numpy(rows).to("cuda")
+    got = dict(y=out["y"].index_select(0, idx).cpu(),
+               dx=out["dx"].index_select(0, idx).cpu(),
+               mean=out["mean"].index_select(0, idx).cpu(),
+               rstd=out["rstd"].index_select(0, idx).cpu(),
+               dscale=out["dscale"].cpu(), dshift=out["dshift"].cpu())
+    torch.cuda.synchronize()
+    del dev, out
+    for r in P.compare_packed_rows(inp, got, rows, "bf16"):
+        _say(f"  rows {r}")
+    for r in P.compare_packed_full(inp, got, "bf16", with_rows=False):
+        _say(f"  full {r}")
+
+
+def test_packed_mixed_full_size(A):
+    lengths = synth.pack_lengths(seed=0)
+    inp = synth.make_packed(synth.PACKED_MIXED, lengths, seed=0)
+    _full_size(A, inp, "packed mixed-length pack", 2048)
+
+
+def test_mmdit_layout_full_size(A):
+    wl = synth.MMDIT_PACKED
+    lengths, mods = synth.mmdit_layout(wl.B)
+    inp = synth.make_packed(wl, lengths, mods, nmod=2 * wl.B, seed=0)
+    _full_size(A, inp, "two-stream layout", 2048)
