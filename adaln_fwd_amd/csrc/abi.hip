@@ -3,6 +3,7 @@
 // include/adaln.h.  Every check runs on the host before any HIP call, so an
 // invalid call enqueues nothing.
 #include <stdarg.h>
+#include <algorithm>
 #include <stdio.h>
 #include <stdint.h>
 
@@ -217,10 +218,15 @@ bool choose_tile_plan(int64_t B, int64_t N, int64_t nvec, TilePlan *plan) {
   return true;
 }
 
-// Segment plans: segment s of N_s rows gets bps_s = max(1, floor(G * N_s /
-// T)) workgroups (none if it is empty), G = 256 * OCC for the kernel's
-// occupancy and T the total rows, so the grid is spread over the segments in
-// proportion to their rows.  Every (segment, workgroup) pair has one partial
+// Segment plans.  The G = 256 * OCC workgroups that are resident at once
+// (OCC for the kernel's occupancy) are shared out so that the most rows any
+// workgroup walks, R, is as small as possible: segment s of N_s rows gets
+// ceil(N_s / R) workgroups (none if it is empty), with R the smallest value
+// for which the total stays within G -- found by bisection, since the total
+// only falls as R grows.  Plain proportional shares (floor(G * N_s / T))
+// would leave a short segment, such as the text tokens of a two-stream
+// sample, one workgroup with twice the rows of the rest, and the whole
+// launch waiting for it.  Every (segment, workgroup) pair has one partial
 // row: the workspace holds [2][total workgroups][D] floats.
 bool plan_segments(const int64_t *off, const int32_t *mod, int64_t nseg,
                    int64_t nvec, bool bwd, SegMap *map, int *V_out) {
@@ -229,19 +235,31 @@ bool plan_segments(const int64_t *off, const int32_t *mod, int64_t nseg,
   const int occ = bwd ? bwd_stream_occ(sp.V) : fwd_stream_occ(sp.V);
   const int64_t G = (int64_t)kCUs * occ;
   const int64_t T = nseg > 0 ? off[nseg] : 0;
+  int64_t longest = 0;
+  for (int64_t s = 0; s < nseg; ++s)
+    longest = std::max(longest, off[s + 1] - off[s]);
+  auto workgroups = [&](int64_t R) {
+    int64_t n = 0;
+    for (int64_t s = 0; s < nseg; ++s) n += (off[s + 1] - off[s] + R - 1) / R;
+    return n;
+  };
+  // R = longest gives one workgroup per non-empty segment, at most 128 <= G
+  int64_t lo = std::max<int64_t>(1, (T + G - 1) / G), hi = std::max<int64_t>(1, longest);
+  while (lo < hi) {
+    const int64_t mid = lo + (hi - lo) / 2;
+    if (workgroups(mid) <= G)
+      hi = mid;
+    else
+      lo = mid + 1;
+  }
+  const int64_t R = lo;
   int64_t wg = 0;
   map->nseg = (int32_t)nseg;
   for (int64_t s = 0; s < nseg; ++s) {
-    const int64_t rows = off[s + 1] - off[s];
-    int64_t bps = 0;
-    if (rows > 0) {
-      bps = G * rows / T;
-      if (bps < 1) bps = 1;
-    }
     map->wg_start[s] = (int32_t)wg;
     map->row_start[s] = off[s];
     map->mod[s] = mod ? mod[s] : (int32_t)s;
-    wg += bps;
+    wg += (off[s + 1] - off[s] + R - 1) / R;
   }
   map->wg_start[nseg] = (int32_t)wg;
   map->row_start[nseg] = T;

@@ -243,11 +243,13 @@ def bwd_fused_plan(B: int, N: int, D: int, dtype: torch.dtype) -> dict:
                 partial_rows=out[3])
 
 
-class _SegTable:
-    """Host copies of a segment table in the ABI's layout (int64 offsets,
-    int32 modulation indices), kept alive for the duration of a call."""
+class SegTable:
+    """Host copy of a segment table in the ABI's layout (int64 offsets,
+    int32 modulation indices).  The segment functions accept one in place of
+    ``seg_offsets`` (with ``seg_mod`` left None) to skip the conversion in a
+    loop that reuses a layout."""
 
-    def __init__(self, seg_offsets, seg_mod):
+    def __init__(self, seg_offsets, seg_mod=None):
         offs = [int(v) for v in seg_offsets]
         if len(offs) < 1:
             raise ValueError("seg_offsets needs at least one entry (0)")
@@ -272,9 +274,17 @@ class _SegTable:
                                                          ctypes.c_void_p)
 
 
+def _table(seg_offsets, seg_mod) -> SegTable:
+    if isinstance(seg_offsets, SegTable):
+        if seg_mod is not None:
+            raise ValueError("pass seg_mod inside the SegTable")
+        return seg_offsets
+    return SegTable(seg_offsets, seg_mod)
+
+
 def bwd_segments_workspace_bytes(seg_offsets, D: int,
                                  dtype: torch.dtype) -> int:
-    tab = _SegTable(seg_offsets, None)
+    tab = _table(seg_offsets, None)
     return int(_lib.load().adaln_bwd_segments_workspace_bytes(
         tab.offsets_ptr, tab.nseg, D, _DTYPES.get(dtype, -1)))
 
@@ -287,7 +297,7 @@ def fwd_segments(x: torch.Tensor, scale: torch.Tensor, shift: torch.Tensor,
     seg_offsets[s] .. seg_offsets[s+1]-1 and modulated by
     scale/shift[seg_mod[s]] (row s if seg_mod is None); scale, shift:
     [nmod, D].  Returns (y, mean, rstd) with mean, rstd float32 [T]."""
-    tab = _SegTable(seg_offsets, seg_mod)
+    tab = _table(seg_offsets, seg_mod)
     if x.dim() != 2:
         raise ValueError(f"x must be [T, D], got shape {tuple(x.shape)}")
     T, D = x.shape
@@ -324,7 +334,7 @@ def bwd_segments(dy, x, scale, mean, rstd, seg_offsets, seg_mod=None, *,
     """Backward of :func:`fwd_segments`; returns (dx, dscale, dshift) with
     dscale, dshift float32 [nmod, D] summed over every segment that uses
     each modulation vector."""
-    tab = _SegTable(seg_offsets, seg_mod)
+    tab = _table(seg_offsets, seg_mod)
     if x.dim() != 2:
         raise ValueError(f"x must be [T, D], got shape {tuple(x.shape)}")
     T, D = x.shape

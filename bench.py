@@ -7,7 +7,12 @@ resident in HBM: adaln_fwd, then the backward pass as adaln_bwd enqueues it
 For --workload mixed_schedule a step is one pass over all 64 buckets of the
 mixed-length schedule in schedule order (each bucket a forward and a
 backward); one input set per bucket shape is drawn and kept resident, since
-the kernels' time does not depend on the values.  W untimed warm-up steps
+the kernels' time does not depend on the values.  For the packed layouts
+(--workload packed_mixed: one pack of mixed-length samples up to the
+131072-token budget; mmdit_packed: text and video segments of 4 samples) a
+step is adaln_fwd_segments then adaln_bwd_segments over the whole pack;
+--unpacked runs the same samples as batched calls instead, one per run of
+equal-length segments.  W untimed warm-up steps
 run first; then exactly K steps are timed between two device
 synchronisations.  HIP events recorded on the same stream between the
 calls give each kernel's average duration inside the timed region.
@@ -52,6 +57,7 @@ KERNEL_SOURCES = {
     "fwd": ("fwd.hip",) + _SHARED,
     "bwd_fused": ("bwd_fused.hip",) + _SHARED,
     "bwd_finish": ("dmod.hip",) + _SHARED,
+    "bwd": ("bwd_fused.hip", "dmod.hip") + _SHARED,
 }
 # rocprofv3 kernel-name prefixes of each step component
 KERNEL_SYMBOLS = {
@@ -222,6 +228,73 @@ def copy_probe(nbytes: int, steps: int, warmup: int) -> int:
     return 0
 
 
+def segment_bytes(T, D, esize, nmod, part_bytes):
+    """Algorithmic bytes of the packed calls (partial sums written by the
+    stream kernel and read back by the finishing kernel)."""
+    act = T * D * esize
+    stats = 4 * T
+    mod = nmod * D * esize
+    return {
+        "fwd": 2 * act + 2 * mod + 2 * stats,
+        "bwd": 3 * act + mod + 2 * stats + 2 * part_bytes + 2 * nmod * D * 4,
+    }
+
+
+def packed_layout(synth, wl, seed):
+    if wl.name == "mmdit_packed":
+        lengths, mods = synth.mmdit_layout(wl.B)
+        return lengths, mods, 2 * wl.B
+    lengths = synth.pack_lengths(seed)
+    return lengths, None, len(lengths)
+
+
+def make_packed_job(A, torch, inp, dev, esize):
+    job = {k: getattr(inp, k).to(dev) for k in ("x", "scale", "shift", "dy")}
+    T, D = inp.x.shape
+    nmod = inp.scale.shape[0]
+    job["table"] = A.SegTable(inp.seg_offsets, inp.seg_mod)
+    job["y"] = torch.empty_like(job["x"])
+    job["dx"] = torch.empty_like(job["x"])
+    job["mean"] = torch.empty(T, dtype=torch.float32, device=dev)
+    job["rstd"] = torch.empty(T, dtype=torch.float32, device=dev)
+    job["dscale"] = torch.empty(nmod, D, dtype=torch.float32, device=dev)
+    job["dshift"] = torch.empty(nmod, D, dtype=torch.float32, device=dev)
+    wbytes = A.bwd_segments_workspace_bytes(job["table"], D, inp.x.dtype)
+    job["ws"] = torch.empty(max(wbytes, 1), dtype=torch.uint8, device=dev)
+    job["tokens"] = T
+    job["bytes"] = segment_bytes(T, D, esize, nmod, wbytes)
+    return job
+
+
+class _Batch:
+    """x, scale, shift, dy of one batched call (host tensors)."""
+
+    def __init__(self, x, scale, shift, dy):
+        self.x, self.scale, self.shift, self.dy = x, scale, shift, dy
+
+
+def unpacked_batches(inp):
+    """The samples of a packed layout as batched calls: each run of
+    consecutive segments of one length becomes one [B, L, D] call with the
+    segments' modulation vectors gathered."""
+    import torch
+    off = [int(v) for v in inp.seg_offsets]
+    mods = (list(range(len(off) - 1)) if inp.seg_mod is None
+            else [int(m) for m in inp.seg_mod])
+    by_len = {}
+    for s in range(len(off) - 1):
+        by_len.setdefault(off[s + 1] - off[s], []).append(s)
+    out = []
+    for L, segs in sorted(by_len.items()):
+        if L == 0:
+            continue
+        x = torch.stack([inp.x[off[s]:off[s + 1]] for s in segs])
+        dy = torch.stack([inp.dy[off[s]:off[s + 1]] for s in segs])
+        idx = torch.tensor([mods[s] for s in segs])
+        out.append(_Batch(x, inp.scale[idx], inp.shift[idx], dy))
+    return out
+
+
 def make_job(A, torch, inp, dev, esize):
     """Device buffers of one batch shape, plus its algorithmic bytes."""
     B, N, D = inp.x.shape
@@ -254,6 +327,9 @@ def main(argv=None) -> int:
     ap.add_argument("--traffic-from", metavar="DIR",
                     help="print per-kernel HBM traffic computed from the "
                          "rocprofv3 --pmc CSVs under DIR and exit")
+    ap.add_argument("--unpacked", action="store_true",
+                    help="packed workloads: run the samples as batched "
+                         "calls, one per segment length, instead")
     ap.add_argument("--copy-probe", action="store_true",
                     help="time torch's device copy of one workload-sized "
                          "tensor instead (achievable-bandwidth reference and "
@@ -294,7 +370,25 @@ def main(argv=None) -> int:
     dt = synth.torch_dtype(wl.dtype)
     esize = torch.empty((), dtype=dt).element_size()
 
-    if wl.B is None:
+    packed = wl in synth.PACKED
+    first_inp = None
+    if packed:
+        lengths, mods, nmod = packed_layout(synth, wl, args.seed)
+        D = wl.D
+        if args.copy_probe:
+            return copy_probe(sum(lengths) * D * esize, args.steps,
+                              args.warmup)
+        log(f"packed workload {wl.name}: {len(lengths)} segments, "
+            f"{sum(lengths)} tokens, D={D}, {nmod} modulation vectors")
+        pinp = synth.make_packed(wl, lengths, mods, nmod=nmod, seed=args.seed)
+        if args.unpacked:
+            order = [make_job(A, torch, b, dev, esize)
+                     for b in unpacked_batches(pinp)]
+            packed = False
+        else:
+            order = [make_packed_job(A, torch, pinp, dev, esize)]
+        del pinp
+    elif wl.B is None:
         # the mixed-length schedule: one step = every bucket, in order
         sched = synth.mixed_schedule(args.seed)
         shapes = {S: A.bshape(S, synth.MIXED_M_MEM, synth.MIXED_M_COMP,
@@ -311,7 +405,6 @@ def main(argv=None) -> int:
                                     bucket=sched.index(S))
             jobs[S] = make_job(A, torch, inp, dev, esize)
         order = [jobs[S] for S in sched]
-        first_inp = None
     else:
         B, N, D = wl.shape
         if args.copy_probe:
@@ -320,9 +413,28 @@ def main(argv=None) -> int:
         first_inp = synth.make_inputs(wl, seed=args.seed)
         order = [make_job(A, torch, first_inp, dev, esize)]
 
-    names = ("fwd", "bwd_fused", "bwd_finish")
+    names = ("fwd", "bwd") if packed else ("fwd", "bwd_fused", "bwd_finish")
+
+    def packed_step(ev=None):
+        for j, job in enumerate(order):
+            e = ev[j] if ev is not None else None
+            if e is not None:
+                e[0].record(stream)
+            A.fwd_segments(job["x"], job["scale"], job["shift"], job["table"],
+                           y=job["y"], mean=job["mean"], rstd=job["rstd"],
+                           stream=stream)
+            if e is not None:
+                e[1].record(stream)
+            A.bwd_segments(job["dy"], job["x"], job["scale"], job["mean"],
+                           job["rstd"], job["table"], dx=job["dx"],
+                           dscale=job["dscale"], dshift=job["dshift"],
+                           workspace=job["ws"], stream=stream)
+            if e is not None:
+                e[2].record(stream)
 
     def step(ev=None):
+        if packed:
+            return packed_step(ev)
         for j, job in enumerate(order):
             e = ev[j] if ev is not None else None
             if e is not None:
@@ -345,7 +457,8 @@ def main(argv=None) -> int:
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    events = [[[torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    events = [[[torch.cuda.Event(enable_timing=True)
+                for _ in range(len(names) + 1)]
                for _ in order] for _ in range(args.steps)]
     log(f"timing {args.steps} steps")
     torch.cuda.synchronize()
@@ -388,7 +501,14 @@ def main(argv=None) -> int:
         "algorithmic_bytes_per_launch": int(tot_bytes[dom] / launches),
         "avg_launch_ms": round(tot_ms[dom] / launches, 5),
     }
-    if wl.B is None:
+    if wl in synth.PACKED:
+        config = {"workload": wl.name, "layout": "batched per length"
+                  if args.unpacked else "packed", "segments": len(lengths),
+                  "calls": len(order), "D": D, "tokens": tokens,
+                  "dtype": wl.dtype, "modulation_vectors": nmod,
+                  "lengths": {str(L): lengths.count(L)
+                              for L in sorted(set(lengths))}}
+    elif wl.B is None:
         config = {"workload": wl.name, "buckets": len(order), "D": D,
                   "tokens": tokens, "dtype": wl.dtype,
                   "bucket_batch": {str(S): b for S, b in shapes.items()}}
