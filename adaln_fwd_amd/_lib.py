@@ -48,6 +48,10 @@ SIGNATURES = {
                                   _SZ, _VP, _VP, _I64, _I64, _I64, _INT,
                                   _VP]),
     "adaln_bshape": (_I64, [_I64, _I64, _I64, ctypes.c_int32]),
+    "adaln_bshape_real": (_I64, [_I64, _I64, ctypes.c_double,
+                                 ctypes.c_double]),
+    "adaln_costfit": (_INT, [_VP, _VP, _VP, _I64, ctypes.c_double,
+                             ctypes.c_double, _VP]),
     "adaln_max_d": (_I64, [_INT]),
     "adaln_strerror": (ctypes.c_char_p, [_INT]),
     "adaln_last_error": (ctypes.c_char_p, []),

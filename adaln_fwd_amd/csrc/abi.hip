@@ -14,8 +14,8 @@
 
 namespace adaln {
 namespace {
-
 thread_local char g_msg[256] = "";
+}  // namespace
 
 int fail(int code, const char *fmt, ...) {
   va_list ap;
@@ -29,6 +29,8 @@ int ok() {
   g_msg[0] = '\0';
   return ADALN_OK;
 }
+
+namespace {
 
 int hip_fail(hipError_t e, const char *what) {
   return fail(ADALN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));

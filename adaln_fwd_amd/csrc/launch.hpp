@@ -10,6 +10,11 @@
 
 namespace adaln {
 
+// Error reporting of the C ABI: fail() records a message for
+// adaln_last_error() and returns `code`; ok() clears it.
+int fail(int code, const char *fmt, ...);
+int ok();
+
 // How a token row is spread over a workgroup: W wavefronts share one row and
 // each lane holds V 16-byte vectors of it (vector k of wave w, lane l is the
 // row's vector (k*W + w)*64 + l).  A 256-thread workgroup works on 4/W rows.

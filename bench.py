@@ -315,6 +315,122 @@ def make_job(A, torch, inp, dev, esize):
     return job
 
 
+# Latent token counts of the pixel scan: 1, 3, 8, 15 and 21 frames of 30x52
+# patches, and the schedule's 8190 and 16380 (all of them, like the
+# schedule's lengths, not multiples of 128).
+SWEEP_LENGTHS = (1560, 4680, 8190, 12480, 16380, 23400, 32760)
+DP_GPUS = 8
+REF_LENGTH = 16380
+
+
+def cost_model(args) -> int:
+    """Shape benchmark of the synthetic step, the cost-model fit and the
+    bucket policies it implies; prints one JSON line."""
+    import torch
+    import adaln_fwd_amd as A
+    from adaln_fwd_amd import sched
+    import synth
+    A.load()
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        return 1
+    m_mem, m_comp, p_int = synth.MIXED_M_MEM, synth.MIXED_M_COMP, synth.MIXED_P
+    D = synth.MIXED_SCHEDULE.D
+    step = sched.SyntheticStep(D=D, heads=24)
+    times = {}
+
+    def measure(B, S):
+        if (B, S) not in times:
+            ms = step.run(B, S, iters=args.steps, warmup=args.warmup)
+            times[(B, S)] = sorted(ms)[len(ms) // 2]
+            log(f"B={B:3d} S={S:6d}: {times[(B, S)]:.3f} ms")
+        return times[(B, S)]
+
+    shapes = sched.sweep_shapes(SWEEP_LENGTHS, m_mem)
+    log(f"shape benchmark: {len(shapes)} shapes, D={D}, 24 heads")
+    for B, S in shapes:
+        measure(B, S)
+    Bs = [B for B, _ in shapes]
+    Ss = [S for _, S in shapes]
+    ts = [times[k] for k in shapes]
+    model = sched.costfit(Bs, Ss, ts)
+    mc = sched.m_comp_for(model.p, m_mem, REF_LENGTH)
+    policies = {
+        "token_equal": {S: max(1, m_mem // S) for S in synth.MIXED_LENGTHS},
+        "dual_pages_constants": {S: A.bshape(S, m_mem, m_comp, p_int)
+                                 for S in synth.MIXED_LENGTHS},
+        "dual_fitted": sched.buckets(synth.MIXED_LENGTHS, m_mem, mc,
+                                     model.p),
+    }
+    sched_draws = synth.mixed_schedule(args.seed)
+    pol_out = {}
+    for name, table in policies.items():
+        # data-parallel estimate: the 64 draws dealt to DP_GPUS GPUs in
+        # order, DP_GPUS buckets per step; a step lasts as long as its
+        # slowest bucket
+        steps_ms, steps_tok = [], []
+        for i in range(0, len(sched_draws), DP_GPUS):
+            group = sched_draws[i:i + DP_GPUS]
+            steps_ms.append(max(measure(table[S], S) for S in group))
+            steps_tok.append(sum(table[S] * S for S in group))
+        t = [measure(B, S) for S, B in table.items()]
+        tok = [B * S for S, B in table.items()]
+        pol_out[name] = {
+            "bucket_batch": {str(S): B for S, B in table.items()},
+            "step_ms": {str(S): round(measure(B, S), 4)
+                        for S, B in table.items()},
+            "predicted_ms": {str(S): round(model.predict(B, S), 4)
+                             for S, B in table.items()},
+            "cv_step_time": round(sched.cv(t), 4),
+            "dp_estimate": {
+                "gpus": DP_GPUS,
+                "tokens_per_s": round(sum(steps_tok) / (sum(steps_ms) * 1e-3),
+                                      1),
+                "busy_fraction": round(
+                    sum(measure(table[S], S) for S in sched_draws)
+                    / (DP_GPUS * sum(steps_ms)), 4),
+            },
+        }
+    # attention's sensitivity to lengths that are multiples of 128
+    aligned = {str(S): {"ms": round(measure(1, S), 4),
+                        "ms_at_S-2": round(measure(1, S - 2), 4)}
+               for S in (8192, 16384, 32768)}
+    rec = {
+        "metric": "cost model of the synthetic step (AdaLN fwd + fused "
+                  "attention fwd + AdaLN bwd), 1 MI355X",
+        "model": "t_ms = a + b * B * S^p",
+        "fit": {"a": model.a, "b": model.b, "p": model.p, "rss": model.rss,
+                "r2": model.r2},
+        "samples": [{"B": B, "S": S, "ms": round(times[(B, S)], 4)}
+                    for B, S in shapes],
+        "pearson_r_token_equal_buckets": {
+            "tokens": round(sched.pearson([m_mem // S * S for S in
+                                           SWEEP_LENGTHS],
+                                          [times[(m_mem // S, S)] for S in
+                                           SWEEP_LENGTHS]), 4),
+            "S^2": round(sched.pearson([S * S for S in SWEEP_LENGTHS],
+                                       [times[(m_mem // S, S)] for S in
+                                        SWEEP_LENGTHS]), 4),
+        },
+        "pearson_r": {
+            "tokens": round(sched.pearson([B * S for B, S in shapes], ts), 4),
+            "S^2": round(sched.pearson([S * S for S in Ss], ts), 4),
+            "B*S^2": round(sched.pearson([B * S * S for B, S in shapes], ts),
+                           4),
+        },
+        "m_comp": {"reference_length": REF_LENGTH, "fitted": mc,
+                   "pages": m_comp,
+                   "by_reference_length": {str(S): sched.m_comp_for(
+                       model.p, m_mem, S) for S in synth.MIXED_LENGTHS}},
+        "policies": pol_out,
+        "alignment_probe_B1": aligned,
+        "config": {"D": D, "heads": 24, "dtype": "bf16", "m_mem": m_mem,
+                   "steps": args.steps, "warmup": args.warmup},
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -330,6 +446,9 @@ def main(argv=None) -> int:
     ap.add_argument("--unpacked", action="store_true",
                     help="packed workloads: run the samples as batched "
                          "calls, one per segment length, instead")
+    ap.add_argument("--cost-model", action="store_true",
+                    help="shape benchmark of the synthetic step, cost-model "
+                         "fit and bucket policies (--steps/--warmup per shape)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="time torch's device copy of one workload-sized "
                          "tensor instead (achievable-bandwidth reference and "
@@ -354,6 +473,8 @@ def main(argv=None) -> int:
     if args.steps < 1 or args.warmup < 0:
         print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
         return 2
+    if args.cost_model:
+        return cost_model(args)
 
     import torch
     import adaln_fwd_amd as A

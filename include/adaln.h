@@ -210,6 +210,28 @@ int adaln_bwd_segments(const void *dy, const void *x, const void *scale,
  */
 int64_t adaln_bshape(int64_t S, int64_t m_mem, int64_t m_comp, int32_t p);
 
+/*
+ * The same rule with a fitted, real exponent and compute bound (section 2.A,
+ * cost-fitting system): max(1, min(floor(m_mem / S), floor(m_comp / S^p))),
+ * the compute bound taken as floor of the double quotient m_comp / pow(S, p).
+ * Returns ADALN_ERR_INVALID for S <= 0, a negative or non-finite bound or
+ * exponent.  Host-only.
+ */
+int64_t adaln_bshape_real(int64_t S, int64_t m_mem, double m_comp, double p);
+
+/*
+ * Step-time cost model of section 2.A: fits t ~ a + b * B * S^p to n >= 3
+ * measured samples (B[i], S[i], t[i]) (host arrays of double; B, S > 0) by
+ * least squares over a, b and p in [p_lo, p_hi].  For each p the best (a, b)
+ * is the closed-form linear fit; the residual is then minimised over p by a
+ * 400-interval grid scan followed by golden-section search.  Writes
+ * out[0..3] = a, b, p, residual sum of squares.  Returns ADALN_OK or
+ * ADALN_ERR_INVALID (NULL array, n < 3, a non-positive B or S, a non-finite
+ * value, p_lo >= p_hi).  Host-only.
+ */
+int adaln_costfit(const double *B, const double *S, const double *t,
+                  int64_t n, double p_lo, double p_hi, double *out);
+
 /* Largest D the row kernels accept for `dtype` (0 for an unknown dtype). */
 int64_t adaln_max_d(int dtype);
 
