@@ -231,7 +231,7 @@ bool choose_stream_plan(int64_t B, int64_t N, int64_t nvec, bool bwd,
                         StreamPlan *plan);
 bool choose_tile_plan(int64_t B, int64_t N, int64_t nvec, TilePlan *plan);
 
-// Launchers: enqueue on `stream`, return hipGetLastError() of the launch.
+// Launchers: enqueue on `stream` and return the launch's own status.
 hipError_t launch_fwd_tiles(int dtype, const TilePlan &plan, const void *x,
                             const void *scale, const void *shift, void *y,
                             float *mean, float *rstd, int32_t B, int32_t N,

@@ -431,6 +431,94 @@ def cost_model(args) -> int:
     return 0
 
 
+def eager_reference(args) -> int:
+    """PyTorch's own unfused chain for the same workload -- layer_norm, then
+    the modulation as separate elementwise ops, and its autograd backward --
+    timed beside this library's calls (the analogue of the pages' unfused
+    baseline); prints one JSON line."""
+    import torch
+    import torch.nn.functional as F
+    import adaln_fwd_amd as A
+    import synth
+    A.load()
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        return 1
+    wl = synth.BY_NAME[args.workload]
+    if wl.B is None or wl in synth.PACKED:
+        print("--eager-reference takes a batched workload", file=sys.stderr)
+        return 2
+    B, N, D = wl.shape
+    inp = synth.make_inputs(wl, seed=args.seed)
+    dev = torch.device("cuda", 0)
+    x = inp.x.to(dev)
+    dy = inp.dy.to(dev)
+    scale = inp.scale.to(dev)
+    shift = inp.shift.to(dev)
+
+    def chain(x_, s_, h_):
+        return (F.layer_norm(x_, (D,), eps=synth.EPS) * (1 + s_[:, None, :])
+                + h_[:, None, :])
+
+    def timed(fn, n):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3 * n)]
+        for i in range(n):
+            fn(ev[3 * i:3 * i + 3])
+        torch.cuda.synchronize()
+        fwd = [ev[3 * i].elapsed_time(ev[3 * i + 1]) for i in range(n)]
+        bwd = [ev[3 * i + 1].elapsed_time(ev[3 * i + 2]) for i in range(n)]
+        return sorted(fwd)[n // 2], sorted(bwd)[n // 2]
+
+    xg = x.clone().requires_grad_(True)
+    sg = scale.clone().requires_grad_(True)
+    hg = shift.clone().requires_grad_(True)
+
+    def torch_step(ev):
+        ev[0].record()
+        y = chain(xg, sg, hg)
+        ev[1].record()
+        torch.autograd.grad(y, (xg, sg, hg), dy)
+        ev[2].record()
+
+    y = torch.empty_like(x)
+    dx = torch.empty_like(x)
+    mean = torch.empty(B, N, device=dev)
+    rstd = torch.empty(B, N, device=dev)
+    ds = torch.empty(B, D, device=dev)
+    dh = torch.empty(B, D, device=dev)
+    ws = torch.empty(max(1, A.bwd_workspace_bytes(B, N, D, x.dtype)),
+                     dtype=torch.uint8, device=dev)
+
+    def lib_step(ev):
+        ev[0].record()
+        A.fwd(x, scale, shift, y=y, mean=mean, rstd=rstd)
+        ev[1].record()
+        A.bwd(dy, x, scale, mean, rstd, dx=dx, dscale=ds, dshift=dh,
+              workspace=ws)
+        ev[2].record()
+
+    log(f"eager reference on {wl.name}: warm-up")
+    timed(torch_step, args.warmup or 1)
+    timed(lib_step, args.warmup or 1)
+    log(f"timing {args.steps} steps each")
+    t_fwd, t_bwd = timed(torch_step, args.steps)
+    l_fwd, l_bwd = timed(lib_step, args.steps)
+    rec = {
+        "metric": "median ms per call, PyTorch eager unfused chain vs this "
+                  "library, 1 MI355X",
+        "config": {"workload": wl.name, "B": B, "N": N, "D": D,
+                   "dtype": wl.dtype},
+        "torch_eager": {"fwd_ms": round(t_fwd, 4), "bwd_ms": round(t_bwd, 4)},
+        "library": {"fwd_ms": round(l_fwd, 4), "bwd_ms": round(l_bwd, 4)},
+        "speedup": {"fwd": round(t_fwd / l_fwd, 3),
+                    "bwd": round(t_bwd / l_bwd, 3),
+                    "fwd+bwd": round((t_fwd + t_bwd) / (l_fwd + l_bwd), 3)},
+        "torch": torch.__version__,
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -449,6 +537,10 @@ def main(argv=None) -> int:
     ap.add_argument("--cost-model", action="store_true",
                     help="shape benchmark of the synthetic step, cost-model "
                          "fit and bucket policies (--steps/--warmup per shape)")
+    ap.add_argument("--eager-reference", action="store_true",
+                    help="time PyTorch's unfused eager chain (layer_norm, "
+                         "modulation, autograd backward) beside this library "
+                         "on the workload")
     ap.add_argument("--copy-probe", action="store_true",
                     help="time torch's device copy of one workload-sized "
                          "tensor instead (achievable-bandwidth reference and "
@@ -475,6 +567,8 @@ def main(argv=None) -> int:
         return 2
     if args.cost_model:
         return cost_model(args)
+    if args.eager_reference:
+        return eager_reference(args)
 
     import torch
     import adaln_fwd_amd as A
