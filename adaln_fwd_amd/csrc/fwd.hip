@@ -96,6 +96,15 @@ __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void fwd_stream_kernel(
       }
 #pragma unroll
       for (int k = 0; k < V; ++k) opaque(xv[k]);
+      // Rows of 3 and of 10 or more vectors: widen scale and shift to float
+      // again for every row.  Kept widened across the loop they do not fit
+      // the register budget of the occupancy these rows run at, and the
+      // spills cost more than the conversions (measured: 3-vector bf16 rows
+      // 52 -> 32 us for 77 MB).
+      if constexpr (V == 3 || V >= 10) {
+#pragma unroll
+        for (int k = 0; k < V; ++k) opaque(sv[k]), opaque(hv[k]);
+      }
       const int64_t off = (row0 + n) * D;
 #pragma unroll
       for (int k = 0; k < V; ++k) {
@@ -237,6 +246,12 @@ __attribute__((amdgpu_waves_per_eu(fwd_waves_per_simd(V)))) void fwd_tile_kernel
 
 #pragma unroll
       for (int k = 0; k < V; ++k) opaque(xv[k]);
+      // as in the stream kernel: re-widen scale and shift per row where
+      // keeping them widened would spill
+      if constexpr (V >= 4) {
+#pragma unroll
+        for (int k = 0; k < V; ++k) opaque(sv[k]), opaque(hv[k]);
+      }
       const int64_t off = (row0 + n) * D;
 #pragma unroll
       for (int k = 0; k < V; ++k) {
