@@ -133,7 +133,7 @@ constexpr int kMaxStreamVectors = 16 * 64;
 #define ADALN_BWD_OCC_LONG 1
 #endif
 #ifndef ADALN_BWD_SHORT_V
-#define ADALN_BWD_SHORT_V 2
+#define ADALN_BWD_SHORT_V 3
 #endif
 constexpr int fwd_stream_pf(int V) {
   return V <= 8 ? ADALN_FWD_PF_SHORT : V <= 12 ? ADALN_FWD_PF_LONG : 1;
