@@ -26,6 +26,11 @@ Prints one JSON line:
                 on the current kernel sources, else null
   cpu_baseline  the float64 CPU oracle on a bounded sample of the same
                 workload, on this host's cores
+  cold          with --cold: each call timed alone after a 1 GiB write that
+                evicts the caches (median, p10, p90)
+Other modes print their own JSON line: --cost-model (shape benchmark and
+cost-model fit of the bucket scheduler), --eager-reference (PyTorch's unfused
+chain beside this library), --copy-probe, --traffic-from.
 """
 
 from __future__ import annotations
@@ -534,6 +539,9 @@ def main(argv=None) -> int:
     ap.add_argument("--unpacked", action="store_true",
                     help="packed workloads: run the samples as batched "
                          "calls, one per segment length, instead")
+    ap.add_argument("--cold", action="store_true",
+                    help="also time each call after evicting the caches "
+                         "(reported under 'cold'; single-call workloads)")
     ap.add_argument("--cost-model", action="store_true",
                     help="shape benchmark of the synthetic step, cost-model "
                          "fit and bucket policies (--steps/--warmup per shape)")
@@ -668,6 +676,28 @@ def main(argv=None) -> int:
             if e is not None:
                 e[3].record(stream)
 
+    calls = {}
+    if len(order) == 1:
+        job = order[0]
+        if packed:
+            calls["fwd"] = lambda: A.fwd_segments(
+                job["x"], job["scale"], job["shift"], job["table"],
+                y=job["y"], mean=job["mean"], rstd=job["rstd"], stream=stream)
+            calls["bwd"] = lambda: A.bwd_segments(
+                job["dy"], job["x"], job["scale"], job["mean"], job["rstd"],
+                job["table"], dx=job["dx"], dscale=job["dscale"],
+                dshift=job["dshift"], workspace=job["ws"], stream=stream)
+        else:
+            calls["fwd"] = lambda: A.fwd(
+                job["x"], job["scale"], job["shift"], y=job["y"],
+                mean=job["mean"], rstd=job["rstd"], stream=stream)
+            calls["bwd_fused"] = lambda: A.bwd_fused(
+                job["dy"], job["x"], job["scale"], job["mean"], job["rstd"],
+                dx=job["dx"], workspace=job["ws"], stream=stream)
+            calls["bwd_finish"] = lambda: A.bwd_finish(
+                job["ws"], *job["shape"], dt, dscale=job["dscale"],
+                dshift=job["dshift"], stream=stream)
+
     log(f"warm-up {args.warmup} steps")
     for _ in range(args.warmup):
         step()
@@ -697,6 +727,38 @@ def main(argv=None) -> int:
                    "bytes": int(tot_bytes[n] / launches),
                    "gbps": round(tot_bytes[n] / (tot_ms[n] * 1e-3) / 1e9, 1)}
                for n in names}
+    if launches == 1:
+        # spread over the timed steps (one launch of each per step)
+        for i, n in enumerate(names):
+            d = sorted(ev[0][i].elapsed_time(ev[0][i + 1]) for ev in events)
+            kernels[n]["p10_ms"] = round(d[len(d) // 10], 5)
+            kernels[n]["median_ms"] = round(d[len(d) // 2], 5)
+            kernels[n]["p90_ms"] = round(d[(9 * len(d)) // 10], 5)
+
+    cold = None
+    if args.cold and launches == 1:
+        # each call after a 1 GiB write that evicts the caches (L2 and the
+        # 256 MB memory-side cache), outside the timed region above
+        scrub = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        per = {n: [] for n in names}
+        cev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        for _ in range(args.steps):
+            for i, n in enumerate(names):
+                scrub.fill_(1.0)
+                cev[0].record(stream)
+                calls[n]()
+                cev[1].record(stream)
+                torch.cuda.synchronize()
+                per[n].append(cev[0].elapsed_time(cev[1]))
+        del scrub
+        cold = {}
+        for n in names:
+            d = sorted(per[n])
+            b = order[0]["bytes"][n]
+            cold[n] = {"median_ms": round(d[len(d) // 2], 5),
+                       "p10_ms": round(d[len(d) // 10], 5),
+                       "p90_ms": round(d[(9 * len(d)) // 10], 5),
+                       "gbps": round(b / (d[len(d) // 2] * 1e-3) / 1e9, 1)}
     step_bytes = sum(tot_bytes.values())
     tokens = sum(job["tokens"] for job in order)
     gbps = step_bytes / (ms_step * 1e-3) / 1e9
@@ -755,6 +817,7 @@ def main(argv=None) -> int:
         "kernels": kernels,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "cold": cold,
         "kernel_source_hash": src_hash,
     }
     print(json.dumps(rec), flush=True)
