@@ -73,6 +73,8 @@ def test_video_bucket_full(A):
     (2, 17, 8192, "f32", "normal"),        # two wavefronts per row, f32
     (1, 5, 16384, "f32", "normal"),        # largest f32 row
     (3, 257, 1024, "f32", "offset"),
+    (2, 333, 2560, "f32", "offset"),       # widest fused f32 backward
+    (1, 100, 4096, "f32", "normal"),       # f32 stream forward, unfused bwd
     (600, 5, 1536, "bf16", "offset"),      # more samples than workgroups
     (1100, 1, 5120, "bf16", "outliers"),   # several samples per workgroup
     (2000, 3, 64, "f32", "normal"),
@@ -284,3 +286,53 @@ def test_abi_errors_on_device_buffers(A):
                        ws.data_ptr(), need - 1, B, N, D, 1, None)
     assert rc == -4
     torch.cuda.synchronize()
+
+
+def test_threads_and_streams(A):
+    """Two host threads, each on its own stream with its own buffers and
+    workspace, run forward + backward concurrently; every result equals the
+    serial one bit for bit, and an invalid call in one thread leaves the
+    other thread's error message untouched."""
+    import threading
+    from adaln_fwd_amd import _lib
+    _say("two threads, two streams")
+    wls = [W.custom(4, 900, 3072, "bf16", x_kind="offset", dy_std=1e-2),
+           W.custom(1, 5000, 5120, "bf16", x_kind="outliers", dy_std=1e-2)]
+    devs = [P.to_device(synth.make_inputs(w, seed=i)) for i, w in
+            enumerate(wls)]
+    serial = [P.gpu_fwd_bwd(d) for d in devs]
+    torch.cuda.synchronize()
+    results = [None, None]
+    errors = []
+    lib = A.load()
+
+    def work(i):
+        try:
+            s = torch.cuda.Stream()
+            outs = []
+            with torch.cuda.stream(s):
+                for _ in range(5):
+                    outs.append(P.gpu_fwd_bwd(devs[i], stream=s))
+                    if i == 0:
+                        # a failing call: only this thread sees its message
+                        rc = lib.adaln_fwd(None, None, None, None, None, None,
+                                           1, 1, 64, 9, None)
+                        assert rc == _lib.ERR_DTYPE
+                        assert b"dtype" in lib.adaln_last_error()
+                    else:
+                        assert lib.adaln_last_error() == b""
+            s.synchronize()
+            results[i] = outs
+        except BaseException as e:  # reported by the main thread
+            errors.append(e)
+
+    ts = [threading.Thread(target=work, args=(i,)) for i in range(2)]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    assert not errors, errors
+    for i in range(2):
+        for out in results[i]:
+            for k in serial[i]:
+                assert torch.equal(out[k], serial[i][k]), (i, k)
