@@ -14,8 +14,11 @@ step is adaln_fwd_segments then adaln_bwd_segments over the whole pack;
 --unpacked runs the same samples as batched calls instead, one per run of
 equal-length segments.  W untimed warm-up steps
 run first; then exactly K steps are timed between two device
-synchronisations.  HIP events recorded on the same stream between the
-calls give each kernel's average duration inside the timed region.
+synchronisations.  Inside the timed region, HIP events recorded on the same
+stream just before and after the backward's main kernel give that kernel's
+average duration (the roofline line).  Events between every pair of calls
+cost about 2% of the step, so the per-kernel breakdown comes from K further
+steps with an event at every boundary, after the timed region.
 
 Prints one JSON line:
   value         tokens/s over the timed steps (wall clock)
@@ -638,81 +641,73 @@ def main(argv=None) -> int:
 
     names = ("fwd", "bwd") if packed else ("fwd", "bwd_fused", "bwd_finish")
 
-    def packed_step(ev=None):
-        for j, job in enumerate(order):
-            e = ev[j] if ev is not None else None
-            if e is not None:
-                e[0].record(stream)
-            A.fwd_segments(job["x"], job["scale"], job["shift"], job["table"],
-                           y=job["y"], mean=job["mean"], rstd=job["rstd"],
-                           stream=stream)
-            if e is not None:
-                e[1].record(stream)
-            A.bwd_segments(job["dy"], job["x"], job["scale"], job["mean"],
-                           job["rstd"], job["table"], dx=job["dx"],
-                           dscale=job["dscale"], dshift=job["dshift"],
-                           workspace=job["ws"], stream=stream)
-            if e is not None:
-                e[2].record(stream)
-
-    def step(ev=None):
+    def job_calls(job):
+        """The calls of one job's forward + backward, in order."""
         if packed:
-            return packed_step(ev)
-        for j, job in enumerate(order):
-            e = ev[j] if ev is not None else None
-            if e is not None:
-                e[0].record(stream)
-            A.fwd(job["x"], job["scale"], job["shift"], y=job["y"],
-                  mean=job["mean"], rstd=job["rstd"], stream=stream)
-            if e is not None:
-                e[1].record(stream)
-            A.bwd_fused(job["dy"], job["x"], job["scale"], job["mean"],
-                        job["rstd"], dx=job["dx"], workspace=job["ws"],
-                        stream=stream)
-            if e is not None:
-                e[2].record(stream)
-            A.bwd_finish(job["ws"], *job["shape"], dt, dscale=job["dscale"],
-                         dshift=job["dshift"], stream=stream)
-            if e is not None:
-                e[3].record(stream)
+            return [
+                lambda: A.fwd_segments(
+                    job["x"], job["scale"], job["shift"], job["table"],
+                    y=job["y"], mean=job["mean"], rstd=job["rstd"],
+                    stream=stream),
+                lambda: A.bwd_segments(
+                    job["dy"], job["x"], job["scale"], job["mean"],
+                    job["rstd"], job["table"], dx=job["dx"],
+                    dscale=job["dscale"], dshift=job["dshift"],
+                    workspace=job["ws"], stream=stream)]
+        return [
+            lambda: A.fwd(job["x"], job["scale"], job["shift"], y=job["y"],
+                          mean=job["mean"], rstd=job["rstd"], stream=stream),
+            lambda: A.bwd_fused(job["dy"], job["x"], job["scale"],
+                                job["mean"], job["rstd"], dx=job["dx"],
+                                workspace=job["ws"], stream=stream),
+            lambda: A.bwd_finish(job["ws"], *job["shape"], dt,
+                                 dscale=job["dscale"], dshift=job["dshift"],
+                                 stream=stream)]
 
-    calls = {}
-    if len(order) == 1:
-        job = order[0]
-        if packed:
-            calls["fwd"] = lambda: A.fwd_segments(
-                job["x"], job["scale"], job["shift"], job["table"],
-                y=job["y"], mean=job["mean"], rstd=job["rstd"], stream=stream)
-            calls["bwd"] = lambda: A.bwd_segments(
-                job["dy"], job["x"], job["scale"], job["mean"], job["rstd"],
-                job["table"], dx=job["dx"], dscale=job["dscale"],
-                dshift=job["dshift"], workspace=job["ws"], stream=stream)
-        else:
-            calls["fwd"] = lambda: A.fwd(
-                job["x"], job["scale"], job["shift"], y=job["y"],
-                mean=job["mean"], rstd=job["rstd"], stream=stream)
-            calls["bwd_fused"] = lambda: A.bwd_fused(
-                job["dy"], job["x"], job["scale"], job["mean"], job["rstd"],
-                dx=job["dx"], workspace=job["ws"], stream=stream)
-            calls["bwd_finish"] = lambda: A.bwd_finish(
-                job["ws"], *job["shape"], dt, dscale=job["dscale"],
-                dshift=job["dshift"], stream=stream)
+    plan = [job_calls(job) for job in order]
+    nk = len(names)
+
+    def step(ev=None, at=()):
+        """One step; ev[j][b] is recorded before call b of job j (b = nk:
+        after its last call) for every boundary b in `at`."""
+        for j, calls in enumerate(plan):
+            for b, call in enumerate(calls):
+                if ev is not None and b in at:
+                    ev[j][b].record(stream)
+                call()
+            if ev is not None and nk in at:
+                ev[j][nk].record(stream)
+
+    calls = dict(zip(names, plan[0])) if len(order) == 1 else {}
+    # The roofline's kernel: the backward's main pass (the largest), timed
+    # inside the timed region with one event on each side; events on every
+    # kernel boundary cost about 2% of the step (each record is a marker with
+    # a cache flush), so the full per-kernel breakdown runs after it.
+    dom = names.index("bwd" if packed else "bwd_fused")
+
+    def new_events():
+        return [[[torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)]
+                 for _ in order] for _ in range(args.steps)]
 
     log(f"warm-up {args.warmup} steps")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    events = [[[torch.cuda.Event(enable_timing=True)
-                for _ in range(len(names) + 1)]
-               for _ in order] for _ in range(args.steps)]
+    dom_events = new_events()
     log(f"timing {args.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(events[i])
+        step(dom_events[i], at=(dom, dom + 1))
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_step = 1e3 * elapsed / args.steps
+
+    log(f"per-kernel breakdown: {args.steps} more steps")
+    events = new_events()
+    for i in range(args.steps):
+        step(events[i], at=tuple(range(nk + 1)))
+    torch.cuda.synchronize()
 
     # per-kernel time and algorithmic bytes, summed over the jobs of a step
     tot_ms = {n: 0.0 for n in names}
@@ -764,19 +759,21 @@ def main(argv=None) -> int:
     gbps = step_bytes / (ms_step * 1e-3) / 1e9
     tokens_s = tokens / (ms_step * 1e-3)
 
-    dom = max(names, key=lambda n: tot_ms[n])
+    dname = names[dom]
+    dom_ms = sum(ev[j][dom].elapsed_time(ev[j][dom + 1])
+                 for ev in dom_events for j in range(len(order))) / args.steps
     src_hash = kernel_source_hash()
-    achieved = tot_bytes[dom] / (tot_ms[dom] * 1e-3) / 1e9
+    achieved = tot_bytes[dname] / (dom_ms * 1e-3) / 1e9
     roofline = {
-        "kernel": dom,
+        "kernel": dname,
         "bound": "hbm",
         "achieved": round(achieved, 1),
         "peak": HBM_PEAK_GBPS,
         "unit": "GB/s",
         "frac": round(achieved / HBM_PEAK_GBPS, 4),
-        "traffic": load_traffic(dom, wl.name, kernel_source_hash(dom)),
-        "algorithmic_bytes_per_launch": int(tot_bytes[dom] / launches),
-        "avg_launch_ms": round(tot_ms[dom] / launches, 5),
+        "traffic": load_traffic(dname, wl.name, kernel_source_hash(dname)),
+        "algorithmic_bytes_per_launch": int(tot_bytes[dname] / launches),
+        "avg_launch_ms": round(dom_ms / launches, 5),
     }
     if wl in synth.PACKED:
         config = {"workload": wl.name, "layout": "batched per length"
