@@ -47,6 +47,27 @@ def test_bshape_mixed_schedule_by_hand(oracle_mod, S, expect):
     assert oracle_mod.bshape(S, 131072, 2_200_000_000, 2) == expect
 
 
+def _golden_buckets():
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden",
+                        "bucket_sizes.txt")
+    rows = []
+    for line in open(path):
+        line = line.split("#", 1)[0].split()
+        if line:
+            rows.append(tuple(int(v) for v in line))
+    return rows
+
+
+def test_bshape_golden_table(oracle_mod):
+    """The hand-evaluated table in tests/golden/bucket_sizes.txt."""
+    rows = _golden_buckets()
+    assert len(rows) == 6
+    for S, m_mem, m_comp, p, mem_b, comp_b, b in rows:
+        assert m_mem // S == mem_b and m_comp // S ** p == comp_b
+        assert oracle_mod.bshape(S, m_mem, m_comp, p) == b
+
+
 def test_bshape_tokens_per_bucket(oracle_mod):
     toks = {S: S * oracle_mod.bshape(S, 131072, 2_200_000_000, 2)
             for S in (1560, 8190, 16380, 32760)}
