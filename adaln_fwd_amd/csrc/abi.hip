@@ -163,6 +163,12 @@ DmodPlan choose_dmod_plan(int64_t B, int64_t N, int64_t nvec) {
 #define ADALN_BWD_MIN_BPS 1
 #endif
 
+// Waves per SIMD (and so workgroups per CU) a stream plan's kernel runs at.
+int stream_occ(const StreamPlan &p, bool bwd) {
+  if (!bwd) return fwd_stream_occ(p.V);
+  return p.W > 1 ? 1 : bwd_stream_occ(p.V);
+}
+
 bool choose_stream_plan(int64_t B, int64_t N, int64_t nvec, bool bwd,
                         StreamPlan *plan) {
   StreamPlan p;
@@ -170,9 +176,18 @@ bool choose_stream_plan(int64_t B, int64_t N, int64_t nvec, bool bwd,
   if (p.V == 0 && 64 * V_ >= nvec) p.V = V_;
   ADALN_STREAM_V(ADALN_STREAM_PLAN_CASE)
 #undef ADALN_STREAM_PLAN_CASE
-  if (p.V == 0 || (bwd && p.V > kMaxBwdStreamV)) return false;
+  if (bwd && (p.V == 0 || p.V > kMaxBwdStreamV)) {
+    // too wide for one wavefront's registers: a pair of wavefronts per row
+    p.V = 0;
+#define ADALN_WIDE_PLAN_CASE(V_) \
+  if (p.V == 0 && (int64_t)kWideWaves * 64 * V_ >= nvec) p.V = V_;
+    ADALN_BWD_WIDE_V(ADALN_WIDE_PLAN_CASE)
+#undef ADALN_WIDE_PLAN_CASE
+    p.W = kWideWaves;
+  }
+  if (p.V == 0) return false;
   if (B > 0 && N > 0) {
-    const int occ = bwd ? bwd_stream_occ(p.V) : fwd_stream_occ(p.V);
+    const int occ = stream_occ(p, bwd);
     const int64_t G = (int64_t)kCUs * occ;
     const int64_t min_bps = bwd ? ADALN_BWD_MIN_BPS : ADALN_FWD_MIN_BPS;
     int64_t bps = G / B > 1 ? G / B : 1;
@@ -231,10 +246,10 @@ bool choose_tile_plan(int64_t B, int64_t N, int64_t nvec, TilePlan *plan) {
 // launch waiting for it.  Every (segment, workgroup) pair has one partial
 // row: the workspace holds [2][total workgroups][D] floats.
 bool plan_segments(const int64_t *off, const int32_t *mod, int64_t nseg,
-                   int64_t nvec, bool bwd, SegMap *map, int *V_out) {
+                   int64_t nvec, bool bwd, SegMap *map, StreamPlan *plan) {
   StreamPlan sp;
   if (!choose_stream_plan(1, 1, nvec, bwd, &sp)) return false;
-  const int occ = bwd ? bwd_stream_occ(sp.V) : fwd_stream_occ(sp.V);
+  const int occ = stream_occ(sp, bwd);
   const int64_t G = (int64_t)kCUs * occ;
   const int64_t T = nseg > 0 ? off[nseg] : 0;
   int64_t longest = 0;
@@ -265,7 +280,7 @@ bool plan_segments(const int64_t *off, const int32_t *mod, int64_t nseg,
   }
   map->wg_start[nseg] = (int32_t)wg;
   map->row_start[nseg] = T;
-  *V_out = sp.V;
+  *plan = sp;
   return true;
 }
 
@@ -449,9 +464,14 @@ ADALN_API int adaln_bwd_fused(const void *dy, const void *x, const void *scale,
   if (!rows) return ok();
   float *part_scale = static_cast<float *>(workspace);
   float *part_shift = part_scale + (size_t)B * plan.bps * D;
-  const hipError_t e = launch_bwd_fused(
-      dtype, plan, dy, x, scale, mean, rstd, dx, part_scale, part_shift,
-      (int32_t)B, (int32_t)N, (int32_t)D, (hipStream_t)stream);
+  const hipError_t e =
+      plan.W > 1
+          ? launch_bwd_wide(dtype, plan, dy, x, scale, mean, rstd, dx,
+                            part_scale, part_shift, (int32_t)B, (int32_t)N,
+                            (int32_t)D, (hipStream_t)stream)
+          : launch_bwd_fused(dtype, plan, dy, x, scale, mean, rstd, dx,
+                             part_scale, part_shift, (int32_t)B, (int32_t)N,
+                             (int32_t)D, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "adaln_bwd_fused launch");
   return ok();
 }
@@ -465,7 +485,7 @@ ADALN_API int adaln_bwd_fused_plan(int64_t B, int64_t N, int64_t D,
     return fail(ADALN_ERR_UNSUPPORTED,
                 "D=%lld is too wide for the fused backward", (long long)D);
   out[0] = plan.V;
-  out[1] = 1;
+  out[1] = plan.W;
   out[2] = plan.grid;
   out[3] = plan.bps;
   return ok();
@@ -567,9 +587,9 @@ ADALN_API size_t adaln_bwd_segments_workspace_bytes(const int64_t *seg_offsets,
                      dtype) != ADALN_OK)
     return 0;
   SegMap map;
-  int V = 0;
+  StreamPlan sp;
   if (!plan_segments(seg_offsets, nullptr, nseg, D / elems_per_vec(dtype),
-                     true, &map, &V))
+                     true, &map, &sp))
     return 0;
   ok();
   return partial_bytes(map.wg_start[nseg], 1, D);
@@ -591,14 +611,14 @@ ADALN_API int adaln_fwd_segments(const void *x, const void *scale,
   ADALN_TRY(check_ptr(mean, rows, "mean"));
   ADALN_TRY(check_ptr(rstd, rows, "rstd"));
   SegMap map;
-  int V = 0;
+  StreamPlan sp;
   if (!plan_segments(seg_offsets, seg_mod, nseg, D / elems_per_vec(dtype),
-                     false, &map, &V))
+                     false, &map, &sp))
     return fail(ADALN_ERR_UNSUPPORTED,
                 "D=%lld is too wide for the segment kernels", (long long)D);
   if (!rows) return ok();
   const hipError_t e =
-      launch_fwd_segments(dtype, V, map, x, scale, shift, y, mean, rstd,
+      launch_fwd_segments(dtype, sp.V, map, x, scale, shift, y, mean, rstd,
                           (int32_t)D, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "adaln_fwd_segments launch");
   return ok();
@@ -625,9 +645,9 @@ ADALN_API int adaln_bwd_segments(const void *dy, const void *x,
   ADALN_TRY(check_ptr(dscale, nmod > 0, "dscale"));
   ADALN_TRY(check_ptr(dshift, nmod > 0, "dshift"));
   SegMap map;
-  int V = 0;
+  StreamPlan sp;
   if (!plan_segments(seg_offsets, seg_mod, nseg, D / elems_per_vec(dtype),
-                     true, &map, &V))
+                     true, &map, &sp))
     return fail(ADALN_ERR_UNSUPPORTED,
                 "D=%lld is too wide for the segment kernels", (long long)D);
   const size_t need = partial_bytes(map.wg_start[nseg], 1, D);
@@ -638,8 +658,12 @@ ADALN_API int adaln_bwd_segments(const void *dy, const void *x,
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = hipSuccess;
   if (rows)
-    e = launch_bwd_segments(dtype, V, map, dy, x, scale, mean, rstd, dx,
-                            part_scale, part_shift, (int32_t)D, s);
+    e = sp.W > 1 ? launch_bwd_wide_segments(dtype, sp.V, map, dy, x, scale,
+                                            mean, rstd, dx, part_scale,
+                                            part_shift, (int32_t)D, s)
+                 : launch_bwd_segments(dtype, sp.V, map, dy, x, scale, mean,
+                                       rstd, dx, part_scale, part_shift,
+                                       (int32_t)D, s);
   if (e == hipSuccess)
     e = launch_finish_segments(part_scale, part_shift, dscale, dshift, map,
                                (int32_t)nmod, (int32_t)D, s);

@@ -45,7 +45,8 @@ struct DmodPlan {
 // are processed `groups` at a time, with `bps` workgroups per sample, and
 // each wavefront walks its sample's rows with a stride of 4*bps.
 struct StreamPlan {
-  int V = 0;
+  int V = 0;       // vectors per lane
+  int W = 1;       // wavefronts per row (2: the backward's wide rows)
   int grid = 0;
   int bps = 0;     // workgroups per sample (partial rows per sample)
   int groups = 0;  // samples in flight
@@ -157,6 +158,10 @@ constexpr int bwd_stream_occ(int V) {
 // register file beyond V = 10; wider rows take the separate dx and D-tile
 // kernels.
 constexpr int kMaxBwdStreamV = 10;
+// Wider rows (up to 2 * 640 vectors) split between the two wavefronts of a
+// pair (bwd_wide_kernel), V vectors per lane each, at one wavefront per SIMD.
+constexpr int kWideWaves = 2;
+#define ADALN_BWD_WIDE_V(X) X(6) X(8) X(10)
 
 // Tile kernel of the forward for rows wider than 1024 vectors: a workgroup
 // of W wavefronts owns n_tile consecutive token rows of one sample, and lane
@@ -266,6 +271,19 @@ hipError_t launch_fwd_segments(int dtype, int V, const SegMap &map,
                                const void *x, const void *scale,
                                const void *shift, void *y, float *mean,
                                float *rstd, int32_t D, hipStream_t stream);
+
+hipError_t launch_bwd_wide(int dtype, const StreamPlan &plan, const void *dy,
+                           const void *x, const void *scale,
+                           const float *mean, const float *rstd, void *dx,
+                           float *part_scale, float *part_shift, int32_t B,
+                           int32_t N, int32_t D, hipStream_t stream);
+
+hipError_t launch_bwd_wide_segments(int dtype, int V, const SegMap &map,
+                                    const void *dy, const void *x,
+                                    const void *scale, const float *mean,
+                                    const float *rstd, void *dx,
+                                    float *part_scale, float *part_shift,
+                                    int32_t D, hipStream_t stream);
 
 hipError_t launch_bwd_segments(int dtype, int V, const SegMap &map,
                                const void *dy, const void *x,

@@ -19,13 +19,13 @@ HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 
 @pytest.fixture(scope="module")
 def usage(tmp_path_factory):
-    """Spilled VGPRs per kernel of fwd.hip and bwd_fused.hip (compiled in
-    parallel)."""
+    """Spilled VGPRs per kernel of fwd.hip, bwd_fused.hip and bwd_wide.hip
+    (compiled in parallel)."""
     if not os.path.exists(HIPCC):
         pytest.skip("hipcc not available")
     tmp = tmp_path_factory.mktemp("res")
     procs = {}
-    for src in ("fwd.hip", "bwd_fused.hip"):
+    for src in ("fwd.hip", "bwd_fused.hip", "bwd_wide.hip"):
         procs[src] = subprocess.Popen(
             [HIPCC, "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -60,3 +60,11 @@ def test_backward_stream_kernels_spill_at_most_a_few(usage):
     assert len(stream) >= 32
     worst = max(stream.values())
     assert worst <= 8, {k: v for k, v in stream.items() if v}
+
+
+def test_wide_backward_kernels_do_not_spill(usage):
+    wide = {k: v for k, v in usage["bwd_wide.hip"].items()
+            if "bwd_wide_kernel" in k}
+    assert len(wide) >= 24
+    spills = {k: v for k, v in wide.items() if v}
+    assert not spills, spills

@@ -79,6 +79,12 @@ def test_video_bucket_full(A):
     (1100, 1, 5120, "bf16", "outliers"),   # several samples per workgroup
     (2000, 3, 64, "f32", "normal"),
     (300, 17, 520, "bf16", "normal"),      # many samples, ragged row
+    # backward rows split between two wavefronts (641..1280 vectors)
+    (3, 333, 5128, "bf16", "outliers"),    # narrowest, ragged last vector
+    (2, 1001, 10240, "bf16", "offset"),    # widest
+    (1, 777, 7000, "bf16", "normal"),      # ragged half
+    (5, 64, 4096, "f32", "normal"),
+    (600, 3, 6144, "bf16", "offset"),      # odd rows per workgroup
 ])
 def test_shapes(A, B, N, D, dtype, kind):
     wl = W.custom(B, N, D, dtype, x_kind=kind, dy_std=1e-2 if dtype ==
@@ -86,24 +92,38 @@ def test_shapes(A, B, N, D, dtype, kind):
     _run_full(A, wl, seed=B + N + D)
 
 
-def test_large_model_sampled(A):
-    """D=5120, N=75600 at full size: sampled rows plus full dscale/dshift."""
-    wl = synth.LARGE_MODEL
-    _say(f"{wl.name} full size, sampled rows")
+def _run_sampled(A, wl, k):
     inp = synth.make_inputs(wl)
     dev = P.to_device(inp)
     out = P.gpu_fwd_bwd(dev)
     torch.cuda.synchronize()
     out = {k: v.cpu() for k, v in out.items()}
     del dev
-    rows = P.sample_rows(wl.rows, 1500)
+    rows = P.sample_rows(wl.rows, k)
     for r in P.compare_rows(inp, out, rows, wl.dtype):
         _say(f"  {r}")
     for r in P.compare_full(inp, out, wl.dtype, with_rows=False):
         _say(f"  {r}")
     # every output is finite
-    for k in ("y", "dx", "mean", "rstd"):
-        assert torch.isfinite(out[k].float()).all(), k
+    for name in ("y", "dx", "mean", "rstd"):
+        assert torch.isfinite(out[name].float()).all(), name
+
+
+def test_large_model_sampled(A):
+    """D=5120, N=75600 at full size: sampled rows plus full dscale/dshift."""
+    wl = synth.LARGE_MODEL
+    _say(f"{wl.name} full size, sampled rows")
+    _run_sampled(A, wl, 1500)
+
+
+def test_wide_rows_sampled(A):
+    """D=8192 (rows split between two wavefronts in the backward) at the
+    large model's activation size: sampled rows plus full dscale/dshift."""
+    wl = W.custom(1, 49152, 8192, "bf16", x_kind="outliers", dy_std=1e-2,
+                  name="wide_rows")
+    _say(f"{wl.name} {wl.shape}, sampled rows")
+    assert A.bwd_fused_plan(*wl.shape, torch.bfloat16)["waves_per_row"] == 2
+    _run_sampled(A, wl, 1024)
 
 
 def test_constant_and_extreme_rows(A):
@@ -226,9 +246,9 @@ def test_unfused_entry_points(A, wl):
         _say(f"  {r}")
 
 
-@pytest.mark.parametrize("D", [5128, 8192, 32768])
+@pytest.mark.parametrize("D", [10248, 16384, 32768])
 def test_fused_unsupported_for_wide_rows(A, D):
-    """Rows wider than 640 vectors have no fused plan; adaln_bwd falls back
+    """Rows wider than 1280 vectors have no fused plan; adaln_bwd falls back
     to the unfused kernels and gives the same bits as calling them."""
     wl = W.custom(1, 9, D, "bf16", dy_std=1e-2)
     _say("wide rows: bwd falls back to bwd_dx + bwd_dmod")

@@ -44,6 +44,9 @@ SMALL = [
     (5120, "bf16", [40, 1, 333], None, 3),                      # widest bf16 bwd
     (64, "f32", [2000, 7], None, 2),                            # row of 16 vectors
     (1536, "bf16", [20000] + [1] * 40, [0] * 41, 1),            # one long, many tiny
+    (8192, "bf16", [300, 0, 17, 1001], [1, 0, 1, 2], 3),        # two-wavefront rows
+    (7000, "bf16", [5, 64, 3], None, 3),                        # ragged two-wavefront
+    (4096, "f32", [100, 257], [0, 0], 1),
 ]
 
 
@@ -136,19 +139,17 @@ def test_deterministic(A):
         assert torch.equal(a[k], b[k]), k
 
 
-def test_wide_rows_rejected(A, oracle_mod):
-    inp = synth.make_packed(_wl(8192, "bf16"), [10, 20], seed=1)
+def test_wide_rows_rejected(A):
+    """Rows past the packed kernels' widths (1024 vectors forward, 1280
+    backward) are refused before anything is enqueued."""
+    inp = synth.make_packed(_wl(16384, "bf16"), [10, 20], seed=1)
     dev = P.packed_to_device(inp)
-    y, mean, rstd = A.fwd_segments(dev["x"], dev["scale"], dev["shift"],
-                                   inp.seg_offsets)
-    torch.cuda.synchronize()
-    out = dict(y=y.cpu(), mean=mean.cpu(), rstd=rstd.cpu())
-    ref_y, ref_m, ref_r = oracle_mod.fwd_segments(inp.x, inp.scale,
-                                                  inp.shift, inp.seg_offsets)
-    P.check_out("y", out["y"], ref_y, "bf16")
-    P.check_stats(out["mean"], out["rstd"], ref_m, ref_r, inp.x)
     with pytest.raises(A.AdalnError) as e:
-        A.bwd_segments(dev["dy"], dev["x"], dev["scale"], mean, rstd,
+        A.fwd_segments(dev["x"], dev["scale"], dev["shift"], inp.seg_offsets)
+    assert e.value.code == -6
+    mean = torch.zeros(30, device="cuda")
+    with pytest.raises(A.AdalnError) as e:
+        A.bwd_segments(dev["dy"], dev["x"], dev["scale"], mean, mean,
                        inp.seg_offsets)
     assert e.value.code == -6
 
