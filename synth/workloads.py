@@ -116,9 +116,18 @@ MMDIT_PACKED = Workload(
          "tokens have their own modulation vectors, laid out [2, B, D] "
          "(text of every sample, then video)")
 
+# Rows wider than one wavefront's registers in the backward (8192 features,
+# split between two wavefronts), at the large model's activation size.
+WIDE_ROWS = Workload(
+    name="wide_rows", index=7, B=1, N=49152, D=8192, dtype="bf16",
+    x_kind="outliers", mod_std=0.1, dy_std=1e-2,
+    note="one sequence of 49152 tokens at D=8192 (805 MB per activation "
+         "tensor), the large model's distributions")
+
 ALL = (TINY_F32, IMAGE_BUCKET, VIDEO_BUCKET, LARGE_MODEL, MIXED_SCHEDULE)
 PACKED = (PACKED_MIXED, MMDIT_PACKED)
-BY_NAME = {w.name: w for w in ALL + PACKED}
+EXTRA = (WIDE_ROWS,)
+BY_NAME = {w.name: w for w in ALL + PACKED + EXTRA}
 
 
 def custom(B: int, N: int, D: int, dtype: str, x_kind: str = "normal",

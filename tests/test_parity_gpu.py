@@ -119,8 +119,7 @@ def test_large_model_sampled(A):
 def test_wide_rows_sampled(A):
     """D=8192 (rows split between two wavefronts in the backward) at the
     large model's activation size: sampled rows plus full dscale/dshift."""
-    wl = W.custom(1, 49152, 8192, "bf16", x_kind="outliers", dy_std=1e-2,
-                  name="wide_rows")
+    wl = synth.WIDE_ROWS
     _say(f"{wl.name} {wl.shape}, sampled rows")
     assert A.bwd_fused_plan(*wl.shape, torch.bfloat16)["waves_per_row"] == 2
     _run_sampled(A, wl, 1024)
