@@ -36,7 +36,10 @@
  *   between calls, so calls on different streams may run concurrently as long
  *   as they use distinct output and workspace buffers.
  * Streams.  `stream` is a hipStream_t passed as void* (NULL = the default
- *   stream).  Calls enqueue kernels and return without synchronising.
+ *   stream).  Calls enqueue kernels on the calling thread's current HIP
+ *   device, which must own the stream and every buffer, and return without
+ *   synchronising.  Nothing is allocated, no memory is set with memset
+ *   nodes and nothing waits, so the calls can be captured in a HIP graph.
  * Errors.  Arguments are validated on the host before any HIP call; a failing
  *   check returns a negative code and enqueues nothing.  A launch failure
  *   returns ADALN_ERR_HIP.  adaln_strerror() names a code; adaln_last_error()
