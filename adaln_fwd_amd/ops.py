@@ -376,6 +376,26 @@ def bwd_segments(dy, x, scale, mean, rstd, seg_offsets, seg_mod=None, *,
     return dx, dscale, dshift
 
 
+def stream_probe(kind: int, a: torch.Tensor, dst: torch.Tensor,
+                 b: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Diagnostic streaming probe: kind 0 copies a into dst, kind 1 writes
+    a XOR b into dst (byte buffers of equal size, a multiple of 10240)."""
+    for t, name in ((a, "a"), (dst, "dst"), (b, "b")):
+        if t is None:
+            continue
+        if t.device.type != "cuda" or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    n = a.numel() * a.element_size()
+    if dst.numel() * dst.element_size() != n or (
+            b is not None and b.numel() * b.element_size() != n):
+        raise ValueError("probe buffers must have the same size")
+    with torch.cuda.device(a.device):
+        rc = _lib.load().adaln_stream_probe(int(kind), _ptr(a), _ptr(b),
+                                            _ptr(dst), n,
+                                            _stream(a.device, stream))
+    _lib.check(rc, "adaln_stream_probe")
+
+
 def bshape(S: int, m_mem: int, m_comp: int, p: int) -> int:
     """Dual-constraint bucket batch size (host integer arithmetic in the
     library); raises on invalid arguments."""

@@ -527,6 +527,46 @@ def eager_reference(args) -> int:
     return 0
 
 
+def stream_probe(args) -> int:
+    """The library's streaming probes on buffers of the workload's activation
+    size; prints one JSON line."""
+    import torch
+    import adaln_fwd_amd as A
+    import synth
+    A.load()
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        return 1
+    wl = synth.BY_NAME[args.workload]
+    if wl.B is None:
+        print("--probe takes a workload with one shape", file=sys.stderr)
+        return 2
+    esize = 4 if wl.dtype == "f32" else 2
+    n = wl.B * wl.N * wl.D * esize // 10240 * 10240
+    a = torch.empty(n, dtype=torch.uint8, device="cuda").random_()
+    b = torch.empty_like(a).random_()
+    d = torch.empty_like(a)
+    out = {"probe": "adaln_stream_probe", "workload": wl.name,
+           "buffer_bytes": n}
+    for kind, name, streams in ((0, "copy", 2), (1, "read2_write1", 3)):
+        for _ in range(args.warmup or 1):
+            A.stream_probe(kind, a, d, b=b)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        ev[0].record()
+        for _ in range(args.steps):
+            A.stream_probe(kind, a, d, b=b)
+        ev[1].record()
+        torch.cuda.synchronize()
+        ms = ev[0].elapsed_time(ev[1]) / args.steps
+        out[name] = {"avg_ms": round(ms, 5),
+                     "gbps": round(streams * n / (ms * 1e-3) / 1e9, 1)}
+    ok = bool(torch.equal(d, a ^ b))
+    out["read2_write1"]["result_ok"] = ok
+    print(json.dumps(out), flush=True)
+    return 0 if ok else 1
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -552,6 +592,10 @@ def main(argv=None) -> int:
                     help="time PyTorch's unfused eager chain (layer_norm, "
                          "modulation, autograd backward) beside this library "
                          "on the workload")
+    ap.add_argument("--probe", action="store_true",
+                    help="time the library's streaming probes (copy; 2 reads "
+                         "+ 1 write) on buffers of the workload's activation "
+                         "size")
     ap.add_argument("--copy-probe", action="store_true",
                     help="time torch's device copy of one workload-sized "
                          "tensor instead (achievable-bandwidth reference and "
@@ -580,6 +624,8 @@ def main(argv=None) -> int:
         return cost_model(args)
     if args.eager_reference:
         return eager_reference(args)
+    if args.probe:
+        return stream_probe(args)
 
     import torch
     import adaln_fwd_amd as A
@@ -754,6 +800,32 @@ def main(argv=None) -> int:
                        "p10_ms": round(d[len(d) // 10], 5),
                        "p90_ms": round(d[(9 * len(d)) // 10], 5),
                        "gbps": round(b / (d[len(d) // 2] * 1e-3) / 1e9, 1)}
+    probe = None
+    if launches == 1:
+        # what HBM sustains for the dominant kernel's access pattern (two
+        # read streams, one write stream) with no arithmetic, on buffers of
+        # the workload's size; after the timed region, not part of `value`
+        job = order[0]
+        row = 10240
+        n = (job["x"].numel() * job["x"].element_size()) // row * row
+        if n > 0:
+            a = job["x"].view(-1).view(torch.uint8)[:n]
+            b = job["dy"].view(-1).view(torch.uint8)[:n]
+            d = job["y"].view(-1).view(torch.uint8)[:n]
+            for _ in range(3):
+                A.stream_probe(1, a, d, b=b, stream=stream)
+            pev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            pev[0].record(stream)
+            reps = 10
+            for _ in range(reps):
+                A.stream_probe(1, a, d, b=b, stream=stream)
+            pev[1].record(stream)
+            torch.cuda.synchronize()
+            pms = pev[0].elapsed_time(pev[1]) / reps
+            probe = {"pattern": "2 reads + 1 write, nontemporal, no "
+                                "arithmetic (adaln_stream_probe kind 1)",
+                     "bytes": 3 * n, "avg_ms": round(pms, 5),
+                     "gbps": round(3 * n / (pms * 1e-3) / 1e9, 1)}
     step_bytes = sum(tot_bytes.values())
     tokens = sum(job["tokens"] for job in order)
     gbps = step_bytes / (ms_step * 1e-3) / 1e9
@@ -775,6 +847,9 @@ def main(argv=None) -> int:
         "algorithmic_bytes_per_launch": int(tot_bytes[dname] / launches),
         "avg_launch_ms": round(dom_ms / launches, 5),
     }
+    if probe is not None:
+        probe["kernel_frac_of_probe"] = round(achieved / probe["gbps"], 4)
+        roofline["achievable_probe"] = probe
     if wl in synth.PACKED:
         config = {"workload": wl.name, "layout": "batched per length"
                   if args.unpacked else "packed", "segments": len(lengths),

@@ -209,6 +209,19 @@ int adaln_bwd_segments(const void *dy, const void *x, const void *scale,
                        int64_t D, int dtype, void *stream);
 
 /*
+ * Streaming-bandwidth probe (diagnostic): the access pattern of the
+ * row-stream kernels without their arithmetic, to measure what HBM sustains
+ * for it.  kind 0 copies a to dst; kind 1 writes dst = a XOR b (two read
+ * streams and one write stream, the fused backward's pattern).  a, b, dst:
+ * device buffers of `bytes` bytes, 16-byte aligned, not overlapping (b is
+ * unused for kind 0); bytes a multiple of 10240 (one 10 KiB row per
+ * wavefront per step).  Returns ADALN_ERR_INVALID / ADALN_ERR_ALIGN for
+ * other arguments.
+ */
+int adaln_stream_probe(int kind, const void *a, const void *b, void *dst,
+                       int64_t bytes, void *stream);
+
+/*
  * Dual-constraint bucket batch size of section 2.A:
  *     max(1, min(floor(m_mem / S), floor(m_comp / S^p)))
  * in exact integer arithmetic.  When S^p exceeds the int64 range the compute

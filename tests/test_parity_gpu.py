@@ -355,3 +355,23 @@ def test_threads_and_streams(A):
         for out in results[i]:
             for k in serial[i]:
                 assert torch.equal(out[k], serial[i][k]), (i, k)
+
+
+def test_stream_probe(A):
+    """The streaming probe copies (kind 0) and XORs (kind 1) whole buffers,
+    and refuses sizes that are not whole 10 KiB rows."""
+    _say("stream probe")
+    n = 10240 * 37
+    a = torch.randint(0, 256, (n,), dtype=torch.uint8, device="cuda")
+    b = torch.randint(0, 256, (n,), dtype=torch.uint8, device="cuda")
+    d = torch.zeros_like(a)
+    A.stream_probe(0, a, d)
+    torch.cuda.synchronize()
+    assert torch.equal(d, a)
+    A.stream_probe(1, a, d, b=b)
+    torch.cuda.synchronize()
+    assert torch.equal(d, a ^ b)
+    with pytest.raises(A.AdalnError):
+        A.stream_probe(0, a[:10000], d[:10000])
+    with pytest.raises(A.AdalnError):
+        A.stream_probe(5, a, d)
