@@ -375,3 +375,56 @@ def test_stream_probe(A):
         A.stream_probe(0, a[:10000], d[:10000])
     with pytest.raises(A.AdalnError):
         A.stream_probe(5, a, d)
+
+
+def _random_shapes(seed, count):
+    g = np.random.default_rng(seed)
+    out = []
+    for _ in range(count):
+        dtype = "bf16" if g.random() < 0.7 else "f32"
+        E = 8 if dtype == "bf16" else 4
+        # widths across every kernel family: one wavefront, a pair in the
+        # backward, several wavefronts in the forward
+        nvec = int(g.choice([g.integers(1, 65), g.integers(65, 641),
+                             g.integers(641, 1281), g.integers(1281, 2049)],
+                            p=[0.3, 0.4, 0.2, 0.1]))
+        B = int(g.integers(1, 9))
+        N = int(g.integers(1, max(2, 60000 // (B * nvec))))
+        out.append((B, N, nvec * E, dtype))
+    return out
+
+
+@pytest.mark.parametrize("B,N,D,dtype", _random_shapes(2024, 24))
+def test_random_shapes(A, B, N, D, dtype):
+    """Seeded random shapes over every kernel family, compared in full."""
+    wl = W.custom(B, N, D, dtype, x_kind="offset",
+                  dy_std=1e-2 if dtype == "bf16" else 1.0)
+    _run_full(A, wl, seed=B * 7 + N * 3 + D)
+
+
+def test_non_finite_rows_stay_local(A):
+    """A row holding NaN or Inf gives non-finite outputs in that row (and in
+    its sample's dscale/dshift) only; every other row and sample is
+    unchanged, bit for bit."""
+    B, N, D = 3, 40, 1536
+    wl = W.custom(B, N, D, "bf16", x_kind="offset", dy_std=1e-2)
+    _say("non-finite rows")
+    inp = synth.make_inputs(wl)
+    dev = P.to_device(inp)
+    clean = P.gpu_fwd_bwd(dev)
+    bad = dict(dev)
+    bad["x"] = dev["x"].clone()
+    bad["x"][1, 7, 100] = float("nan")
+    bad["x"][1, 9, 5] = float("inf")
+    out = P.gpu_fwd_bwd(bad)
+    torch.cuda.synchronize()
+    for n in (7, 9):
+        assert not torch.isfinite(out["y"][1, n].float()).all()
+    keep = torch.ones(B, N, dtype=torch.bool, device="cuda")
+    keep[1, 7] = keep[1, 9] = False
+    assert torch.equal(out["y"][keep], clean["y"][keep])
+    assert torch.equal(out["dx"][keep], clean["dx"][keep])
+    assert torch.equal(out["mean"][keep], clean["mean"][keep])
+    for b in (0, 2):
+        assert torch.equal(out["dscale"][b], clean["dscale"][b])
+        assert torch.equal(out["dshift"][b], clean["dshift"][b])
