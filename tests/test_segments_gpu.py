@@ -190,3 +190,33 @@ def test_mmdit_layout_full_size(A):
     lengths, mods = synth.mmdit_layout(wl.B)
     inp = synth.make_packed(wl, lengths, mods, nmod=2 * wl.B, seed=0)
     _full_size(A, inp, "two-stream layout", 2048)
+
+
+def _random_tables(seed, count):
+    g = np.random.default_rng(seed)
+    out = []
+    for _ in range(count):
+        dtype = "bf16" if g.random() < 0.75 else "f32"
+        E = 8 if dtype == "bf16" else 4
+        nvec = int(g.choice([g.integers(1, 65), g.integers(65, 641),
+                             g.integers(641, 1025)], p=[0.3, 0.5, 0.2]))
+        nseg = int(g.integers(1, 129))
+        lengths = g.integers(0, max(2, 40000 // (nseg * nvec)), size=nseg)
+        nmod = int(g.integers(1, nseg + 1))
+        mods = g.integers(0, nmod, size=nseg).tolist()
+        out.append((nvec * E, dtype, lengths.tolist(), mods, nmod))
+    return out
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_random_tables(A, case):
+    """Seeded random segment tables (1-128 segments, empty ones, shared and
+    unused vectors) at widths of every kernel family, compared in full."""
+    D, dt, lengths, mods, nmod = _random_tables(77, 8)[case]
+    _say(f"random table {case}: D={D} {dt} nseg={len(lengths)} "
+         f"T={sum(lengths)} nmod={nmod}")
+    inp = synth.make_packed(_wl(D, dt), lengths, mods, nmod=nmod, seed=case)
+    out = P.gpu_packed(inp, P.packed_to_device(inp))
+    torch.cuda.synchronize()
+    out = {k: v.cpu() for k, v in out.items()}
+    P.compare_packed_full(inp, out, dt)
