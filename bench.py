@@ -511,6 +511,24 @@ def eager_reference(args) -> int:
     log(f"timing {args.steps} steps each")
     t_fwd, t_bwd = timed(torch_step, args.steps)
     l_fwd, l_bwd = timed(lib_step, args.steps)
+
+    # device memory a forward leaves allocated for its backward, beyond its
+    # output y: autograd's saved tensors for the unfused chain, the saved
+    # statistics (mean, rstd) for this library
+    torch.cuda.synchronize()
+    m0 = torch.cuda.memory_allocated()
+    ye = chain(xg, sg, hg)
+    torch.cuda.synchronize()
+    eager_saved = torch.cuda.memory_allocated() - m0 - ye.numel() * \
+        ye.element_size()
+    del ye
+    torch.cuda.synchronize()
+    m0 = torch.cuda.memory_allocated()
+    yl, ml, rl = A.fwd(x, scale, shift)
+    torch.cuda.synchronize()
+    lib_saved = torch.cuda.memory_allocated() - m0 - yl.numel() * \
+        yl.element_size()
+    del yl, ml, rl
     rec = {
         "metric": "median ms per call, PyTorch eager unfused chain vs this "
                   "library, 1 MI355X",
@@ -521,6 +539,12 @@ def eager_reference(args) -> int:
         "speedup": {"fwd": round(t_fwd / l_fwd, 3),
                     "bwd": round(t_bwd / l_bwd, 3),
                     "fwd+bwd": round((t_fwd + t_bwd) / (l_fwd + l_bwd), 3)},
+        "saved_for_backward_bytes": {"torch_eager": int(eager_saved),
+                                     "library": int(lib_saved),
+                                     "per_token_eager": round(
+                                         eager_saved / (B * N), 2),
+                                     "per_token_library": round(
+                                         lib_saved / (B * N), 2)},
         "torch": torch.__version__,
     }
     print(json.dumps(rec), flush=True)
