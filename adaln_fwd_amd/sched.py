@@ -8,11 +8,11 @@ The arithmetic (the least-squares fit and the bucket rule) runs in
 marshals arrays and times the synthetic step.
 
 The synthetic step of a [B, S, D] bucket is the AdaLN forward (this
-library), attention over the normalised tokens (PyTorch's fused
-scaled-dot-product attention, flash or memory-efficient kernel only -- no
-fallback to the unfused path) and the AdaLN backward (this library): the
-operator the pages fuse plus the O(S^2) part whose cost the compute
-constraint accounts for.
+library), self-attention over the normalised tokens, forward and backward
+(PyTorch's fused scaled-dot-product attention, flash or memory-efficient
+kernels only -- no fallback to the unfused path), and the AdaLN backward
+(this library): the operator the pages fuse plus the O(S^2) part whose cost
+the compute constraint accounts for, both directions of a training step.
 """
 
 from __future__ import annotations
@@ -103,11 +103,13 @@ def cv(values: Sequence[float], weights: Sequence[float] = None) -> float:
 class SyntheticStep:
     """Times the synthetic step of one bucket shape on the current GPU."""
 
-    def __init__(self, D: int = 3072, heads: int = 24, device="cuda"):
+    def __init__(self, D: int = 3072, heads: int = 24, device="cuda",
+                 attention_backward: bool = True):
         import torch
         if D % heads:
             raise ValueError("D must be a multiple of heads")
         self.D, self.heads, self.device = D, heads, torch.device(device)
+        self.attention_backward = attention_backward
 
     def run(self, B: int, S: int, iters: int = 5, warmup: int = 2
             ) -> List[float]:
@@ -137,13 +139,23 @@ class SyntheticStep:
         ws = torch.empty(max(1, ops.bwd_workspace_bytes(B, S, D,
                                                         torch.bfloat16)),
                          dtype=torch.uint8, device=dev)
-        qkv = y.view(B, S, H, D // H).transpose(1, 2)
+        # q = k = v: the normalised tokens as H heads (a view of y); the
+        # attention's own gradient input is a fixed random tensor
+        qkv = y.view(B, S, H, D // H).transpose(1, 2).detach()
+        back = self.attention_backward
+        if back:
+            qkv.requires_grad_(True)
+            d_out = torch.randn(B, H, S, D // H, device=dev,
+                                dtype=torch.bfloat16, generator=g)
 
         def step():
             ops.fwd(x, scale, shift, y=y, mean=mean, rstd=rstd)
             with sdpa_kernel([SDPBackend.FLASH_ATTENTION,
                               SDPBackend.EFFICIENT_ATTENTION]):
-                F.scaled_dot_product_attention(qkv, qkv, qkv)
+                out = F.scaled_dot_product_attention(qkv, qkv, qkv)
+                if back:
+                    out.backward(d_out)
+                    qkv.grad = None
             ops.bwd(dy, x, scale, mean, rstd, dx=dx, dscale=dscale,
                     dshift=dshift, workspace=ws)
 

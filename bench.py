@@ -405,7 +405,7 @@ def cost_model(args) -> int:
                for S in (8192, 16384, 32768)}
     rec = {
         "metric": "cost model of the synthetic step (AdaLN fwd + fused "
-                  "attention fwd + AdaLN bwd), 1 MI355X",
+                  "attention fwd and bwd + AdaLN bwd), 1 MI355X",
         "model": "t_ms = a + b * B * S^p",
         "fit": {"a": model.a, "b": model.b, "p": model.p, "rss": model.rss,
                 "r2": model.r2},
