@@ -147,15 +147,19 @@ DmodPlan choose_dmod_plan(int64_t B, int64_t N, int64_t nvec) {
   return p;
 }
 
-// Row-stream plans (rows of up to 1024 vectors for the forward, 640 for the
-// backward).  V is the smallest
-// instantiated count that holds the row.  The kernel's occupancy OCC fixes a
-// persistent grid of G = 256 * OCC workgroups (OCC per CU on a 256-CU
-// MI355X), spread over the samples: bps = max(1, G / B) workgroups per
-// sample, `groups` = G / bps samples in flight.  The plan depends only on the
-// shape, so the workspace size ([B, bps, D] partial sums of the backward) is
-// a pure function of it; on a part with another CU count the kernels remain
-// correct and only use the GPU less evenly.
+// Row-stream plans (rows of up to 1024 vectors for the forward, 1280 for the
+// backward, which takes a pair of wavefronts per row past 320).  V is the
+// smallest instantiated count that holds the row.  The kernel's occupancy OCC
+// fixes a persistent grid of G = 256 * OCC workgroups (OCC per CU on a
+// 256-CU MI355X), spread over the samples: up to G / B workgroups per sample
+// (at least one), `groups` = G / bps samples in flight.  Of the counts that
+// keep the most rows any row walker (a wavefront, or a pair of them) visits
+// as low as G / B does, bps is the smallest, so that all walkers finish
+// together rather than a few walking one row more (measured on MI355X: the
+// 16 x 1560-token, D = 1536 backward 1% faster).  The plan depends only on
+// the shape, so the workspace size ([B, bps, D] partial sums of the
+// backward) is a pure function of it; on a part with another CU count the
+// kernels remain correct and only use the GPU less evenly.
 #ifndef ADALN_FWD_MIN_BPS
 #define ADALN_FWD_MIN_BPS 1
 #endif
@@ -166,7 +170,7 @@ DmodPlan choose_dmod_plan(int64_t B, int64_t N, int64_t nvec) {
 // Waves per SIMD (and so workgroups per CU) a stream plan's kernel runs at.
 int stream_occ(const StreamPlan &p, bool bwd) {
   if (!bwd) return fwd_stream_occ(p.V);
-  return p.W > 1 ? 1 : bwd_stream_occ(p.V);
+  return p.W > 1 ? bwd_wide_occ(p.V) : bwd_stream_occ(p.V);
 }
 
 bool choose_stream_plan(int64_t B, int64_t N, int64_t nvec, bool bwd,
@@ -192,6 +196,10 @@ bool choose_stream_plan(int64_t B, int64_t N, int64_t nvec, bool bwd,
     const int64_t min_bps = bwd ? ADALN_BWD_MIN_BPS : ADALN_FWD_MIN_BPS;
     int64_t bps = G / B > 1 ? G / B : 1;
     if (bps < min_bps) bps = min_bps < G ? min_bps : G;
+    const int64_t walkers = p.W > 1 ? 2 : 4;  // row walkers per workgroup
+    const int64_t most = (N + walkers * bps - 1) / (walkers * bps);
+    const int64_t even = (N + walkers * most - 1) / (walkers * most);
+    if (even >= min_bps && even < bps) bps = even;
     const int64_t groups = G / bps;
     p.bps = (int)bps;
     p.groups = (int)groups;

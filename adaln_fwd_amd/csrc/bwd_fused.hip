@@ -1,6 +1,7 @@
 // Fused backward of the AdaLN operator: dx and the D-tile partial sums of
-// dscale/dshift in one pass over x and dy (rows of up to 640 16-byte
-// vectors; wider rows use the separate dx and D-tile kernels).
+// dscale/dshift in one pass over x and dy, for rows of up to 320 16-byte
+// vectors (wider rows: bwd_wide_kernel, then the separate dx and D-tile
+// kernels).
 //
 // The D-tile coalesced reduction of the AdaptiveLoad technical summary
 // (section 2.B, backward pass) pins each thread to a feature and accumulates

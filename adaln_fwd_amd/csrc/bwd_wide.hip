@@ -1,14 +1,17 @@
-// Fused backward for rows of 641 to 1280 16-byte vectors (bf16 D of 5128 to
-// 10240, f32 D of 2564 to 5120): dx and the D-tile partial sums of
+// Fused backward for rows of 321 to 1280 16-byte vectors (bf16 D of 2568 to
+// 10240, f32 D of 1284 to 5120): dx and the D-tile partial sums of
 // dscale/dshift in one pass over x and dy, like bwd_stream_kernel, with each
 // row split between two wavefronts.
 //
-// One wavefront cannot hold such a row together with its per-lane
-// accumulators (2 floats per element it owns): past 640 vectors they
-// outgrow the register file.  Here the four wavefronts of a workgroup form
-// two pairs; a pair shares a row, wavefront h of the pair owning the
-// contiguous vectors [h*V*64, (h+1)*V*64) (lane l: vector (h*V + k)*64 + l),
-// so each keeps the registers of a 640-vector row.  The two row sums of dx
+// A row held in one wavefront together with its per-lane accumulators (2
+// floats per element it owns) takes the whole register file from 640
+// vectors up, and outgrows it past that; from 321 vectors up it already
+// leaves room for one wavefront per SIMD only, with nothing to cover memory
+// latency.  Here the four wavefronts of a workgroup form two pairs; a pair
+// shares a row, wavefront h of the pair owning the contiguous vectors
+// [h*V*64, (h+1)*V*64) (lane l: vector (h*V + k)*64 + l), so each keeps the
+// registers of half the row: two wavefronts per SIMD for rows of up to 640
+// vectors, one for wider ones.  The two row sums of dx
 // (of g and of g*xhat) are combined through LDS: each wavefront reduces its
 // half with DPP, lane 0 stores the two values, one barrier, and both read the
 // pair's two halves and add them in half order.  The store area is
@@ -36,7 +39,8 @@ constexpr int kPairs = 2;  // rows a workgroup works on at a time
 
 template <typename T, int V, bool FULL, class Map>
 __global__ __launch_bounds__(kBlock)
-__attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_wide_kernel(
+__attribute__((amdgpu_waves_per_eu(bwd_wide_occ(V), bwd_wide_occ(V)))) void
+bwd_wide_kernel(
     const T *__restrict__ dy, const T *__restrict__ x,
     const T *__restrict__ scale, const float *__restrict__ mean,
     const float *__restrict__ rstd, T *__restrict__ dx,

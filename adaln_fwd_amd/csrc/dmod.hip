@@ -106,40 +106,55 @@ __global__ __launch_bounds__(kBlock) void dmod_partial_kernel(
 }
 
 // dscale[b, d] = sum over t = 0 .. n_tiles-1 of part_scale[b, t, d] (and the
-// same for dshift).  A workgroup of 16 wavefronts covers 64 features of one
-// sample, one per lane; wavefront w sums the contiguous range of tiles
-// [w*n_tiles/16, (w+1)*n_tiles/16) in index order, issuing up to 16 loads
-// per array before adding them, and the 16 wavefront sums are added in
-// wavefront order.  One feature per lane (rather than four) spreads a
-// 5120-feature sample over 80 workgroups, so enough CUs stream the partials.
+// same for dshift).  One lane per feature.  A workgroup of 16 wavefronts
+// covers 16 / wpc column blocks of 64 features; the wpc wavefronts of a
+// column block split the tiles into wpc contiguous ranges, each summed in
+// index order with all its loads in flight, and the range sums are added in
+// range order.  wpc is the smallest power of two with n_tiles <= 16 * wpc (at
+// most 16), so every wavefront has work and issues one batch of loads: one
+// feature per lane spreads a 5120-feature sample with 256 tiles over 80
+// workgroups, and a few tiles per sample take 16 column blocks a workgroup.
 // With n_tiles == 0 the outputs are zero.
 constexpr int kFinishWaves = 16;
 constexpr int kFinishBatch = 16;
 
+// log2 of the wavefronts per column block that sum `rows` partial rows at
+// most `batch` rows each (at most 16 wavefronts).
+static int finish_wpc_log2(int64_t rows, int batch) {
+  int l = 0;
+  while (l < 4 && rows > (int64_t)batch << l) ++l;
+  return l;
+}
+
 __global__ __launch_bounds__(kFinishWaves * kWave) void dmod_finish_kernel(
     const float *__restrict__ part_scale, const float *__restrict__ part_shift,
     float *__restrict__ dscale, float *__restrict__ dshift, int32_t D,
-    int32_t n_tiles, int32_t col_blocks, int64_t total_blocks) {
-  __shared__ float stage[kFinishWaves - 1][2][kWave];
+    int32_t n_tiles, int32_t col_blocks, int32_t wpc_log2, int64_t total_cols) {
+  __shared__ float stage[kFinishWaves][2][kWave];
   const int lane = lane_id();
   const int wave = wave_id();
-  const int t0 = (int)((int64_t)wave * n_tiles / kFinishWaves);
-  const int t1 = (int)((int64_t)(wave + 1) * n_tiles / kFinishWaves);
+  const int wpc = 1 << wpc_log2;
+  const int cpb = kFinishWaves >> wpc_log2;  // column blocks per workgroup
+  const int slice = wave & (wpc - 1);
+  const int t0 = (int)((int64_t)slice * n_tiles / wpc);
+  const int t1 = (int)((int64_t)(slice + 1) * n_tiles / wpc);
 
-  for (int64_t blk = blockIdx.x; blk < total_blocks; blk += gridDim.x) {
-    const int cb = (int)(blk % col_blocks);
-    const int b = (int)(blk / col_blocks);
+  for (int64_t blk = blockIdx.x; blk * cpb < total_cols; blk += gridDim.x) {
+    const int64_t col = blk * cpb + (wave >> wpc_log2);  // (b, column block)
+    const bool live = col < total_cols;
+    const int cb = live ? (int)(col % col_blocks) : 0;
+    const int b = live ? (int)(col / col_blocks) : 0;
     const int c = cb * kWave + lane;
-    const bool ok = c < D;
+    const bool ok = live && c < D;
     const int64_t base = (int64_t)b * n_tiles * D + c;
     float as = 0.f, ah = 0.f;
     for (int t = t0; t < t1; t += kFinishBatch) {
       float vs[kFinishBatch], vh[kFinishBatch];
 #pragma unroll
       for (int i = 0; i < kFinishBatch; ++i) {
-        const bool live = ok && t + i < t1;
-        vs[i] = live ? part_scale[base + (int64_t)(t + i) * D] : 0.f;
-        vh[i] = live ? part_shift[base + (int64_t)(t + i) * D] : 0.f;
+        const bool in = ok && t + i < t1;
+        vs[i] = in ? part_scale[base + (int64_t)(t + i) * D] : 0.f;
+        vh[i] = in ? part_shift[base + (int64_t)(t + i) * D] : 0.f;
       }
 #pragma unroll
       for (int i = 0; i < kFinishBatch; ++i) {
@@ -147,16 +162,15 @@ __global__ __launch_bounds__(kFinishWaves * kWave) void dmod_finish_kernel(
         ah += vh[i];
       }
     }
-    if (wave > 0) {
-      stage[wave - 1][0][lane] = as;
-      stage[wave - 1][1][lane] = ah;
+    if (slice > 0) {
+      stage[wave][0][lane] = as;
+      stage[wave][1][lane] = ah;
     }
     __syncthreads();
-    if (wave == 0 && ok) {
-#pragma unroll
-      for (int w = 0; w < kFinishWaves - 1; ++w) {
-        as += stage[w][0][lane];
-        ah += stage[w][1][lane];
+    if (slice == 0 && ok) {
+      for (int w = 1; w < wpc; ++w) {
+        as += stage[wave + w][0][lane];
+        ah += stage[wave + w][1][lane];
       }
       dscale[(int64_t)b * D + c] = as;
       dshift[(int64_t)b * D + c] = ah;
@@ -167,37 +181,42 @@ __global__ __launch_bounds__(kFinishWaves * kWave) void dmod_finish_kernel(
 
 // Segment variant: dscale[m, d] = sum over the segments s with mod[s] == m,
 // in index order, of the partial rows of their workgroups
-// [wg_start[s], wg_start[s+1]).  Wavefront w takes rows wg_start[s] + w,
-// + 16, ... of each such segment (up to 8 loads per array in flight), and
-// the 16 wavefront sums are added in wavefront order.
+// [wg_start[s], wg_start[s+1]).  As above, wpc wavefronts share a column
+// block (wpc from the most partial rows any modulation vector has); slice j
+// takes rows wg_start[s] + j, + wpc, ... of each such segment (up to 8 loads
+// per array in flight), and the slice sums are added in slice order.
 constexpr int kSegBatch = 8;
 
 __global__ __launch_bounds__(kFinishWaves * kWave) void finish_segments_kernel(
     const float *__restrict__ part_scale, const float *__restrict__ part_shift,
     float *__restrict__ dscale, float *__restrict__ dshift, int32_t D,
-    int32_t col_blocks, int64_t total_blocks, SegMap map) {
-  __shared__ float stage[kFinishWaves - 1][2][kWave];
+    int32_t col_blocks, int32_t wpc_log2, int64_t total_cols, SegMap map) {
+  __shared__ float stage[kFinishWaves][2][kWave];
   const int lane = lane_id();
   const int wave = wave_id();
+  const int wpc = 1 << wpc_log2;
+  const int cpb = kFinishWaves >> wpc_log2;
+  const int slice = wave & (wpc - 1);
 
-  for (int64_t blk = blockIdx.x; blk < total_blocks; blk += gridDim.x) {
-    const int cb = (int)(blk % col_blocks);
-    const int m = (int)(blk / col_blocks);
+  for (int64_t blk = blockIdx.x; blk * cpb < total_cols; blk += gridDim.x) {
+    const int64_t col = blk * cpb + (wave >> wpc_log2);  // (m, column block)
+    const bool live = col < total_cols;
+    const int cb = live ? (int)(col % col_blocks) : 0;
+    const int m = live ? (int)(col / col_blocks) : -1;
     const int c = cb * kWave + lane;
-    const bool ok = c < D;
+    const bool ok = live && c < D;
     float as = 0.f, ah = 0.f;
     for (int s = 0; s < map.nseg; ++s) {
       if (map.mod[s] != m) continue;
       const int end = map.wg_start[s + 1];
-      for (int w0 = map.wg_start[s] + wave; w0 < end;
-           w0 += kFinishWaves * kSegBatch) {
+      for (int w0 = map.wg_start[s] + slice; w0 < end; w0 += wpc * kSegBatch) {
         float vs[kSegBatch], vh[kSegBatch];
 #pragma unroll
         for (int i = 0; i < kSegBatch; ++i) {
-          const int w = w0 + i * kFinishWaves;
-          const bool live = ok && w < end;
-          vs[i] = live ? part_scale[(int64_t)w * D + c] : 0.f;
-          vh[i] = live ? part_shift[(int64_t)w * D + c] : 0.f;
+          const int w = w0 + i * wpc;
+          const bool in = ok && w < end;
+          vs[i] = in ? part_scale[(int64_t)w * D + c] : 0.f;
+          vh[i] = in ? part_shift[(int64_t)w * D + c] : 0.f;
         }
 #pragma unroll
         for (int i = 0; i < kSegBatch; ++i) {
@@ -206,16 +225,15 @@ __global__ __launch_bounds__(kFinishWaves * kWave) void finish_segments_kernel(
         }
       }
     }
-    if (wave > 0) {
-      stage[wave - 1][0][lane] = as;
-      stage[wave - 1][1][lane] = ah;
+    if (slice > 0) {
+      stage[wave][0][lane] = as;
+      stage[wave][1][lane] = ah;
     }
     __syncthreads();
-    if (wave == 0 && ok) {
-#pragma unroll
-      for (int w = 0; w < kFinishWaves - 1; ++w) {
-        as += stage[w][0][lane];
-        ah += stage[w][1][lane];
+    if (slice == 0 && ok) {
+      for (int w = 1; w < wpc; ++w) {
+        as += stage[wave + w][0][lane];
+        ah += stage[wave + w][1][lane];
       }
       dscale[(int64_t)m * D + c] = as;
       dshift[(int64_t)m * D + c] = ah;
@@ -229,12 +247,23 @@ hipError_t launch_finish_segments(const float *part_scale,
                                   float *dshift, const SegMap &map,
                                   int32_t nmod, int32_t D,
                                   hipStream_t stream) {
+  // the most partial rows any modulation vector sums
+  int64_t most = 0;
+  for (int32_t m = 0; m < nmod; ++m) {
+    int64_t rows = 0;
+    for (int s = 0; s < map.nseg; ++s)
+      if (map.mod[s] == m) rows += map.wg_start[s + 1] - map.wg_start[s];
+    most = rows > most ? rows : most;
+  }
+  const int wl = finish_wpc_log2(most, kSegBatch);
   const int32_t col_blocks = (D + kWave - 1) / kWave;
-  const int64_t total_blocks = (int64_t)col_blocks * nmod;
-  return launch_kernel_threads(finish_segments_kernel, total_blocks,
+  const int64_t total_cols = (int64_t)col_blocks * nmod;
+  const int64_t cpb = kFinishWaves >> wl;
+  return launch_kernel_threads(finish_segments_kernel,
+                               (total_cols + cpb - 1) / cpb,
                                kFinishWaves * kWave, stream, part_scale,
                                part_shift, dscale, dshift, D, col_blocks,
-                               total_blocks, map);
+                               (int32_t)wl, total_cols, map);
 }
 
 hipError_t launch_dmod_partial(int dtype, const DmodPlan &plan,
@@ -261,12 +290,15 @@ hipError_t launch_dmod_finish(const float *part_scale,
                               const float *part_shift, float *dscale,
                               float *dshift, int32_t B, int32_t D,
                               int32_t n_tiles, hipStream_t stream) {
+  const int wl = finish_wpc_log2(n_tiles, kFinishBatch);
   const int32_t col_blocks = (D + kWave - 1) / kWave;
-  const int64_t total_blocks = (int64_t)col_blocks * B;
-  return launch_kernel_threads(dmod_finish_kernel, total_blocks,
+  const int64_t total_cols = (int64_t)col_blocks * B;
+  const int64_t cpb = kFinishWaves >> wl;
+  return launch_kernel_threads(dmod_finish_kernel,
+                               (total_cols + cpb - 1) / cpb,
                                kFinishWaves * kWave, stream, part_scale,
                                part_shift, dscale, dshift, D, n_tiles,
-                               col_blocks, total_blocks);
+                               col_blocks, (int32_t)wl, total_cols);
 }
 
 }  // namespace adaln

@@ -107,7 +107,7 @@ __device__ __forceinline__ void for_each_segment(const SegMap &m, F &&f) {
 }
 
 #define ADALN_STREAM_V(X) X(1) X(2) X(3) X(4) X(5) X(6) X(8) X(10) X(12) X(16)
-#define ADALN_BWD_STREAM_V(X) X(1) X(2) X(3) X(4) X(5) X(6) X(8) X(10)
+#define ADALN_BWD_STREAM_V(X) X(1) X(2) X(3) X(4) X(5)
 constexpr int kMaxStreamVectors = 16 * 64;
 
 // Rows in flight per wavefront (PF) and waves per SIMD (OCC) of each stream
@@ -154,14 +154,20 @@ constexpr int bwd_stream_pf(int V) {
 constexpr int bwd_stream_occ(int V) {
   return V <= ADALN_BWD_SHORT_V ? ADALN_BWD_OCC_SHORT : ADALN_BWD_OCC_LONG;
 }
-// The backward's per-lane accumulators (2*V*E floats) outgrow even the full
-// register file beyond V = 10; wider rows take the separate dx and D-tile
-// kernels.
-constexpr int kMaxBwdStreamV = 10;
-// Wider rows (up to 2 * 640 vectors) split between the two wavefronts of a
-// pair (bwd_wide_kernel), V vectors per lane each, at one wavefront per SIMD.
+// The fused backward keeps per-lane accumulators (2*V*E floats) next to the
+// row.  One wavefront per row (bwd_stream_kernel) holds rows of up to 320
+// vectors.  Wider rows, up to 2 * 640 vectors, split between the two
+// wavefronts of a pair (bwd_wide_kernel), V vectors per lane each; past 1280
+// vectors the accumulators outgrow the register file and the separate dx and
+// D-tile kernels take over.  A whole 640-vector row in one wavefront needs
+// the full register file at one wavefront per SIMD, so nothing covers its
+// memory latency while it computes; as halves, rows of up to 640 vectors run
+// at two wavefronts per SIMD (measured on MI355X: the D = 5120 bf16 backward
+// 411 -> 400 us, D = 3072 1-3% faster).
+constexpr int kMaxBwdStreamV = 5;
 constexpr int kWideWaves = 2;
-#define ADALN_BWD_WIDE_V(X) X(6) X(8) X(10)
+#define ADALN_BWD_WIDE_V(X) X(3) X(4) X(5) X(6) X(8) X(10)
+constexpr int bwd_wide_occ(int V) { return V <= 5 ? 2 : 1; }
 
 // Tile kernel of the forward for rows wider than 1024 vectors: a workgroup
 // of W wavefronts owns n_tile consecutive token rows of one sample, and lane

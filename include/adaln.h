@@ -116,7 +116,7 @@ int adaln_bwd(const void *dy, const void *x, const void *scale,
 /*
  * The two launches adaln_bwd makes for rows of at most 1280 vectors
  * (D <= 10240 bf16 / 5120 f32), exposed so callers can schedule or time them
- * separately.  Rows of up to 640 vectors are owned by one wavefront each,
+ * separately.  Rows of up to 320 vectors are owned by one wavefront each,
  * wider ones by a pair of wavefronts that combine their row sums through
  * LDS.  adaln_bwd_fused reads x and dy once: it writes dx and, per
  * (sample, n_tile), float32 partial sums of dscale and dshift into the

@@ -45,8 +45,10 @@ int main(void)
     CHECK(adaln_bwd_workspace_bytes(2, 3, 60, ADALN_BF16) == 0);
     {
         int64_t plan[4];
-        CHECK(adaln_bwd_fused_plan(1, 75600, 5120, ADALN_BF16, plan) == ADALN_OK);
+        CHECK(adaln_bwd_fused_plan(1, 75600, 2048, ADALN_BF16, plan) == ADALN_OK);
         CHECK(plan[1] == 1 && plan[3] > 0);
+        CHECK(adaln_bwd_fused_plan(1, 75600, 5120, ADALN_BF16, plan) == ADALN_OK);
+        CHECK(plan[1] == 2 && plan[3] > 0);
         CHECK(adaln_bwd_fused_plan(1, 1000, 8192, ADALN_BF16, plan) == ADALN_OK);
         CHECK(plan[1] == 2);
     }

@@ -79,8 +79,13 @@ def test_video_bucket_full(A):
     (1100, 1, 5120, "bf16", "outliers"),   # several samples per workgroup
     (2000, 3, 64, "f32", "normal"),
     (300, 17, 520, "bf16", "normal"),      # many samples, ragged row
-    # backward rows split between two wavefronts (641..1280 vectors)
-    (3, 333, 5128, "bf16", "outliers"),    # narrowest, ragged last vector
+    # backward rows split between two wavefronts (321..1280 vectors; two
+    # wavefronts per SIMD up to 640)
+    (3, 123, 2568, "bf16", "offset"),      # narrowest, ragged half
+    (2, 150, 4000, "bf16", "normal"),      # 4 vectors per lane, ragged
+    (4, 100, 1288, "f32", "normal"),       # f32, ragged
+    (700, 2, 3072, "bf16", "offset"),      # more samples than workgroups
+    (3, 333, 5128, "bf16", "outliers"),    # one wavefront per SIMD, ragged
     (2, 1001, 10240, "bf16", "offset"),    # widest
     (1, 777, 7000, "bf16", "normal"),      # ragged half
     (5, 64, 4096, "f32", "normal"),
