@@ -110,13 +110,14 @@ __global__ __launch_bounds__(kBlock) void dmod_partial_kernel(
 // covers 16 / wpc column blocks of 64 features; the wpc wavefronts of a
 // column block split the tiles into wpc contiguous ranges, each summed in
 // index order with all its loads in flight, and the range sums are added in
-// range order.  wpc is the smallest power of two with n_tiles <= 16 * wpc (at
-// most 16), so every wavefront has work and issues one batch of loads: one
-// feature per lane spreads a 5120-feature sample with 256 tiles over 80
-// workgroups, and a few tiles per sample take 16 column blocks a workgroup.
-// With n_tiles == 0 the outputs are zero.
+// range order.  wpc is the smallest power of two with n_tiles <= 32 * wpc (at
+// most 16), so every wavefront has work and, up to 512 tiles, issues all its
+// loads in one batch (one round trip to memory): one feature per lane
+// spreads a 5120-feature sample with 512 tiles over 80 workgroups, and a few
+// tiles per sample take 16 column blocks a workgroup.  With n_tiles == 0 the
+// outputs are zero.
 constexpr int kFinishWaves = 16;
-constexpr int kFinishBatch = 16;
+constexpr int kFinishBatch = 32;
 
 // log2 of the wavefronts per column block that sum `rows` partial rows at
 // most `batch` rows each (at most 16 wavefronts).

@@ -63,15 +63,17 @@ def log(msg: str) -> None:
 _SHARED = ("common.hpp", "launch.hpp", "abi.hip")
 KERNEL_SOURCES = {
     "fwd": ("fwd.hip",) + _SHARED,
-    "bwd_fused": ("bwd_fused.hip",) + _SHARED,
+    "bwd_fused": ("bwd_fused.hip", "bwd_wide.hip") + _SHARED,
     "bwd_finish": ("dmod.hip",) + _SHARED,
-    "bwd": ("bwd_fused.hip", "dmod.hip") + _SHARED,
+    "bwd": ("bwd_fused.hip", "bwd_wide.hip", "dmod.hip") + _SHARED,
 }
-# rocprofv3 kernel-name prefixes of each step component
+# rocprofv3 kernel-name prefixes of each step component (the fused backward
+# runs one wavefront per row or, for wider rows, pairs of them)
 KERNEL_SYMBOLS = {
-    "fwd": "void adaln::fwd_stream_kernel",
-    "bwd_fused": "void adaln::bwd_stream_kernel",
-    "bwd_finish": "adaln::dmod_finish_kernel",
+    "fwd": ("void adaln::fwd_stream_kernel",),
+    "bwd_fused": ("void adaln::bwd_stream_kernel",
+                  "void adaln::bwd_wide_kernel"),
+    "bwd_finish": ("adaln::dmod_finish_kernel",),
 }
 
 
