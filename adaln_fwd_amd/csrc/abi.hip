@@ -209,10 +209,17 @@ bool choose_stream_plan(int64_t B, int64_t N, int64_t nvec, bool bwd,
   return true;
 }
 
+// Workgroups per CU of a tile plan: 4 SIMDs times the kernel's waves per
+// SIMD, over the W wavefronts of a workgroup (at least one).
+int64_t tile_wgs_per_cu(const TilePlan &p) {
+  const int64_t n = 4 * fwd_waves_per_simd(p.V) / p.W;
+  return n > 1 ? n : 1;
+}
+
 // Forward rows wider than 1024 vectors: W wavefronts share a row; the V (of
 // the instantiated ones) that wastes the fewest vector slots, the smallest
-// such V among equals.  Tiles: about two rounds of the workgroups 256 CUs
-// hold at the kernel's occupancy, spread over the samples.
+// such V among equals.  Rows are dealt out as in the stream plans, over the
+// G = 256 * tile_wgs_per_cu resident workgroups (one row walker each).
 bool choose_tile_plan(int64_t B, int64_t N, int64_t nvec, TilePlan *plan) {
   TilePlan p;
   int64_t best_waste = -1;
@@ -230,14 +237,15 @@ bool choose_tile_plan(int64_t B, int64_t N, int64_t nvec, TilePlan *plan) {
 #undef ADALN_FWD_PLAN_CASE
   if (p.V == 0) return false;
   if (B > 0 && N > 0) {
-    int64_t per_cu = 4 * fwd_waves_per_simd(p.V) / p.W;
-    if (per_cu < 1) per_cu = 1;
-    const int64_t target = (int64_t)kCUs * per_cu * 2;
-    const int64_t tiles_per_sample = target > B ? (target + B - 1) / B : 1;
-    int64_t n_tile = (N + tiles_per_sample - 1) / tiles_per_sample;
-    if (n_tile < 2) n_tile = 2;
-    p.n_tile = (int)n_tile;
-    p.n_tiles = (int)((N + n_tile - 1) / n_tile);
+    const int64_t G = (int64_t)kCUs * tile_wgs_per_cu(p);
+    int64_t bps = G / B > 1 ? G / B : 1;
+    const int64_t most = (N + bps - 1) / bps;
+    const int64_t even = (N + most - 1) / most;
+    if (even < bps) bps = even;
+    const int64_t groups = G / bps;
+    p.bps = (int)bps;
+    p.groups = (int)groups;
+    p.grid = (int)(bps * (groups < B ? groups : B));
   }
   *plan = p;
   return true;
@@ -253,12 +261,8 @@ bool choose_tile_plan(int64_t B, int64_t N, int64_t nvec, TilePlan *plan) {
 // sample, one workgroup with twice the rows of the rest, and the whole
 // launch waiting for it.  Every (segment, workgroup) pair has one partial
 // row: the workspace holds [2][total workgroups][D] floats.
-bool plan_segments(const int64_t *off, const int32_t *mod, int64_t nseg,
-                   int64_t nvec, bool bwd, SegMap *map, StreamPlan *plan) {
-  StreamPlan sp;
-  if (!choose_stream_plan(1, 1, nvec, bwd, &sp)) return false;
-  const int occ = stream_occ(sp, bwd);
-  const int64_t G = (int64_t)kCUs * occ;
+void build_segment_map(const int64_t *off, const int32_t *mod, int64_t nseg,
+                       int64_t G, SegMap *map) {
   const int64_t T = nseg > 0 ? off[nseg] : 0;
   int64_t longest = 0;
   for (int64_t s = 0; s < nseg; ++s)
@@ -288,6 +292,13 @@ bool plan_segments(const int64_t *off, const int32_t *mod, int64_t nseg,
   }
   map->wg_start[nseg] = (int32_t)wg;
   map->row_start[nseg] = T;
+}
+
+bool plan_segments(const int64_t *off, const int32_t *mod, int64_t nseg,
+                   int64_t nvec, bool bwd, SegMap *map, StreamPlan *plan) {
+  StreamPlan sp;
+  if (!choose_stream_plan(1, 1, nvec, bwd, &sp)) return false;
+  build_segment_map(off, mod, nseg, (int64_t)kCUs * stream_occ(sp, bwd), map);
   *plan = sp;
   return true;
 }
@@ -618,16 +629,25 @@ ADALN_API int adaln_fwd_segments(const void *x, const void *scale,
   ADALN_TRY(check_ptr(y, rows, "y"));
   ADALN_TRY(check_ptr(mean, rows, "mean"));
   ADALN_TRY(check_ptr(rstd, rows, "rstd"));
+  const int64_t nvec = D / elems_per_vec(dtype);
   SegMap map;
   StreamPlan sp;
-  if (!plan_segments(seg_offsets, seg_mod, nseg, D / elems_per_vec(dtype),
-                     false, &map, &sp))
+  TilePlan tp;
+  hipError_t e = hipSuccess;
+  if (plan_segments(seg_offsets, seg_mod, nseg, nvec, false, &map, &sp)) {
+    if (!rows) return ok();
+    e = launch_fwd_segments(dtype, sp.V, map, x, scale, shift, y, mean, rstd,
+                            (int32_t)D, (hipStream_t)stream);
+  } else if (choose_tile_plan(1, 1, nvec, &tp)) {
+    if (!rows) return ok();
+    build_segment_map(seg_offsets, seg_mod, nseg,
+                      (int64_t)kCUs * tile_wgs_per_cu(tp), &map);
+    e = launch_fwd_tiles_segments(dtype, tp, map, x, scale, shift, y, mean,
+                                  rstd, (int32_t)D, (hipStream_t)stream);
+  } else {
     return fail(ADALN_ERR_UNSUPPORTED,
                 "D=%lld is too wide for the segment kernels", (long long)D);
-  if (!rows) return ok();
-  const hipError_t e =
-      launch_fwd_segments(dtype, sp.V, map, x, scale, shift, y, mean, rstd,
-                          (int32_t)D, (hipStream_t)stream);
+  }
   if (e != hipSuccess) return hip_fail(e, "adaln_fwd_segments launch");
   return ok();
 }

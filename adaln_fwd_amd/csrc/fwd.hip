@@ -14,11 +14,13 @@
 // sample's scale and shift stay in registers.  Mean and variance are
 // two-pass over the register-resident row (DPP reductions).
 //
-// fwd_tile_kernel (wider rows): W wavefronts share each row, lane l of
-// wavefront w holding vectors (k*W + w)*64 + l, for a tile of n_tile rows per
-// workgroup.  Each wavefront computes the mean of its own elements and the
-// centred sum of squares around it; the W results are combined through LDS
-// with the pairwise update of Chan, Golub and LeVeque (1979),
+// fwd_tile_kernel (wider rows): the W wavefronts of a workgroup share each
+// row, lane l of wavefront w holding vectors (k*W + w)*64 + l.  Rows are
+// dealt out as in the stream kernel (workgroup k_in of a sample's bps walks
+// rows k_in, k_in + bps, ...), with the next row in flight.  Each wavefront
+// computes the mean of its own elements and the centred sum of squares
+// around it; the W results are combined through LDS with the pairwise update
+// of Chan, Golub and LeVeque (1979),
 //     M2 = sum_w M2_w + sum_w n_w * (mean_w - mean)^2,
 // one barrier per row, keeping the accuracy of a two-pass variance.
 //
@@ -149,13 +151,12 @@ __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void fwd_stream_kernel(
   });
 }
 
-template <typename T, int V, bool FULL>
+template <typename T, int V, bool FULL, class Map>
 __global__ __launch_bounds__(kMaxRowWaves * kWave)
 __attribute__((amdgpu_waves_per_eu(fwd_waves_per_simd(V)))) void fwd_tile_kernel(
     const T *__restrict__ x, const T *__restrict__ scale,
     const T *__restrict__ shift, T *__restrict__ y, float *__restrict__ mean,
-    float *__restrict__ rstd, int32_t N, int32_t D, int32_t n_tile,
-    int32_t n_tiles, int32_t total_tiles) {
+    float *__restrict__ rstd, int32_t D, Map map) {
   constexpr int E = Elems<T>::value;
   __shared__ float red[2][3][kMaxRowWaves];  // [parity][sum, m2, count][wave]
   const int lane = lane_id();
@@ -177,17 +178,12 @@ __attribute__((amdgpu_waves_per_eu(fwd_waves_per_simd(V)))) void fwd_tile_kernel
   const float cnt_w = (float)(nvalid * E);
   int parity = 0;
 
-  for (int tile = blockIdx.x; tile < total_tiles; tile += gridDim.x) {
-    const int b = tile / n_tiles;
-    const int t = tile - b * n_tiles;
-    const int n0 = t * n_tile;
-    const int n1 = min(N, n0 + n_tile);
-    const int64_t row0 = (int64_t)b * N;
-
+  for_each_segment(map, [&](int64_t row0, int N, int mod, int k_in, int bps,
+                            int) {
     Vec sv[V], hv[V];
 #pragma unroll
     for (int k = 0; k < V; ++k) {
-      const int64_t c = (int64_t)b * D + (int64_t)jv[k] * E;
+      const int64_t c = (int64_t)mod * D + (int64_t)jv[k] * E;
       sv[k] = ok[k] ? load_vec(scale + c) : vzero();
       hv[k] = ok[k] ? load_vec(shift + c) : vzero();
     }
@@ -269,36 +265,37 @@ __attribute__((amdgpu_waves_per_eu(fwd_waves_per_simd(V)))) void fwd_tile_kernel
 
     // Steady state: A holds row n and rows n+1, n+2 exist, so every load in
     // the loop body is unconditional; the last one or two rows follow it.
-    Vec xa[V], xb[V];
-    load_row(xa, n0);
-    int n = n0;
-    for (; n + 2 < n1; n += 2) {
-      load_row(xb, n + 1);
-      do_row(xa, n);
-      load_row(xa, n + 2);
-      do_row(xb, n + 1);
+    int n = k_in;
+    if (n < N) {
+      const int stride = bps;
+      Vec xa[V], xb[V];
+      load_row(xa, n);
+      for (; n + 2 * stride < N; n += 2 * stride) {
+        load_row(xb, n + stride);
+        do_row(xa, n);
+        load_row(xa, n + 2 * stride);
+        do_row(xb, n + stride);
+      }
+      if (n + stride < N) {
+        load_row(xb, n + stride);
+        do_row(xa, n);
+        do_row(xb, n + stride);
+      } else {
+        do_row(xa, n);
+      }
     }
-    if (n + 1 < n1) {
-      load_row(xb, n + 1);
-      do_row(xa, n);
-      do_row(xb, n + 1);
-    } else {
-      do_row(xa, n);
-    }
-  }
+  });
 }
 
 namespace {
 
-template <typename T, int V, bool FULL>
-hipError_t fwd_v(const TilePlan &plan, const void *x, const void *scale,
-                 const void *shift, void *y, float *mean, float *rstd,
-                 int32_t B, int32_t N, int32_t D, hipStream_t s) {
-  const int32_t total = B * plan.n_tiles;
-  return launch_kernel_threads(
-      fwd_tile_kernel<T, V, FULL>, total, plan.W * kWave, s, (const T *)x,
-      (const T *)scale, (const T *)shift, (T *)y, mean, rstd, N, D,
-      (int32_t)plan.n_tile, (int32_t)plan.n_tiles, total);
+template <typename T, int V, bool FULL, class Map>
+hipError_t fwd_tile_v(int64_t grid, int W, const Map &map, const void *x,
+                      const void *scale, const void *shift, void *y,
+                      float *mean, float *rstd, int32_t D, hipStream_t s) {
+  return launch_kernel_threads(fwd_tile_kernel<T, V, FULL, Map>, grid,
+                               W * kWave, s, (const T *)x, (const T *)scale,
+                               (const T *)shift, (T *)y, mean, rstd, D, map);
 }
 
 template <typename T, int V, bool FULL, class Map>
@@ -362,28 +359,56 @@ hipError_t launch_fwd_segments(int dtype, int V, const SegMap &map,
                              shift, y, mean, rstd, D, stream);
 }
 
-#define ADALN_FWD_TILE_CASE(V_)                                                \
-  if (plan.V == V_) {                                                          \
-    if (full)                                                                  \
-      return dtype == 1 ? fwd_v<bf16, V_, true>(plan, x, scale, shift, y,      \
-                                                mean, rstd, B, N, D, stream)   \
-                        : fwd_v<float, V_, true>(plan, x, scale, shift, y,     \
-                                                 mean, rstd, B, N, D, stream); \
-    return dtype == 1 ? fwd_v<bf16, V_, false>(plan, x, scale, shift, y, mean, \
-                                               rstd, B, N, D, stream)          \
-                      : fwd_v<float, V_, false>(plan, x, scale, shift, y,      \
-                                                mean, rstd, B, N, D, stream);  \
+#define ADALN_FWD_TILE_CASE(V_)                                             \
+  if (V == V_) {                                                            \
+    if (full)                                                               \
+      return dtype == 1 ? fwd_tile_v<bf16, V_, true>(grid, W, map, x, scale, \
+                                                     shift, y, mean, rstd,  \
+                                                     D, stream)             \
+                        : fwd_tile_v<float, V_, true>(grid, W, map, x,      \
+                                                      scale, shift, y,      \
+                                                      mean, rstd, D,        \
+                                                      stream);              \
+    return dtype == 1 ? fwd_tile_v<bf16, V_, false>(grid, W, map, x, scale,  \
+                                                    shift, y, mean, rstd, D, \
+                                                    stream)                  \
+                      : fwd_tile_v<float, V_, false>(grid, W, map, x, scale, \
+                                                     shift, y, mean, rstd,  \
+                                                     D, stream);            \
   }
+
+namespace {
+
+template <class Map>
+hipError_t fwd_tile_dispatch(int dtype, int V, int W, int64_t grid,
+                             const Map &map, const void *x, const void *scale,
+                             const void *shift, void *y, float *mean,
+                             float *rstd, int32_t D, hipStream_t stream) {
+  if (W < 1 || W > kMaxRowWaves) return hipErrorInvalidValue;
+  const int E = dtype == 1 ? 8 : 4;
+  const bool full = (int64_t)V * W * kWave * E == D;
+  ADALN_FWD_V(ADALN_FWD_TILE_CASE)
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
 
 hipError_t launch_fwd_tiles(int dtype, const TilePlan &plan, const void *x,
                             const void *scale, const void *shift, void *y,
                             float *mean, float *rstd, int32_t B, int32_t N,
                             int32_t D, hipStream_t stream) {
-  if (plan.W < 1 || plan.W > kMaxRowWaves) return hipErrorInvalidValue;
-  const int E = dtype == 1 ? 8 : 4;
-  const bool full = (int64_t)plan.V * plan.W * kWave * E == D;
-  ADALN_FWD_V(ADALN_FWD_TILE_CASE)
-  return hipErrorInvalidValue;
+  const UniformMap map{B, N, plan.bps, plan.groups};
+  return fwd_tile_dispatch(dtype, plan.V, plan.W, plan.grid, map, x, scale,
+                           shift, y, mean, rstd, D, stream);
+}
+
+hipError_t launch_fwd_tiles_segments(int dtype, const TilePlan &plan,
+                                     const SegMap &map, const void *x,
+                                     const void *scale, const void *shift,
+                                     void *y, float *mean, float *rstd,
+                                     int32_t D, hipStream_t stream) {
+  return fwd_tile_dispatch(dtype, plan.V, plan.W, map.wg_start[map.nseg],
+                           map, x, scale, shift, y, mean, rstd, D, stream);
 }
 
 }  // namespace adaln

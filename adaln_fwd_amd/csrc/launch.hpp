@@ -169,18 +169,22 @@ constexpr int kWideWaves = 2;
 #define ADALN_BWD_WIDE_V(X) X(3) X(4) X(5) X(6) X(8) X(10)
 constexpr int bwd_wide_occ(int V) { return V <= 5 ? 2 : 1; }
 
-// Tile kernel of the forward for rows wider than 1024 vectors: a workgroup
-// of W wavefronts owns n_tile consecutive token rows of one sample, and lane
-// l of wavefront w holds vectors (k*W + w)*64 + l, k < V, of each row.
+// Tile kernel of the forward for rows wider than 1024 vectors: the W
+// wavefronts of a workgroup share each row, lane l of wavefront w holding
+// vectors (k*W + w)*64 + l, k < V.  Rows are dealt out like the stream
+// kernels' (bps workgroups per sample, `groups` samples in flight, `grid`
+// workgroups).
 struct TilePlan {
   int V = 0;
   int W = 0;
-  int n_tile = 0;
-  int n_tiles = 0;  // tiles per sample
+  int grid = 0;
+  int bps = 0;
+  int groups = 0;
 };
 
 constexpr int kMaxRowWaves = 8;  // at most 512 threads per tile workgroup
-#define ADALN_FWD_V(X) X(1) X(2) X(3) X(4) X(5) X(6) X(8)
+// (V <= 2 would need W > 8 for a row past 1024 vectors: never chosen)
+#define ADALN_FWD_V(X) X(3) X(4) X(5) X(6) X(8)
 constexpr int kCUs = 256;
 constexpr int fwd_waves_per_simd(int V) {
   return V <= 1 ? 8 : V == 2 ? 4 : V <= 4 ? 3 : 2;
@@ -247,6 +251,11 @@ hipError_t launch_fwd_tiles(int dtype, const TilePlan &plan, const void *x,
                             const void *scale, const void *shift, void *y,
                             float *mean, float *rstd, int32_t B, int32_t N,
                             int32_t D, hipStream_t stream);
+hipError_t launch_fwd_tiles_segments(int dtype, const TilePlan &plan,
+                                     const SegMap &map, const void *x,
+                                     const void *scale, const void *shift,
+                                     void *y, float *mean, float *rstd,
+                                     int32_t D, hipStream_t stream);
 
 hipError_t launch_bwd_dx(int dtype, const RowPlan &plan, const void *dy,
                          const void *x, const void *scale, const float *mean,

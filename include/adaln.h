@@ -186,9 +186,9 @@ int adaln_bwd_dmod(const void *dy, const void *x, const float *mean,
  *   scale, shift [nmod, D] dtype;  dscale, dshift [nmod, D] f32, where
  *                dscale[m] sums dy*xhat over every row of every segment
  *                with seg_mod[s] == m (zero for an unused m)
- * The per-row math is that of adaln_fwd / adaln_bwd.  Rows of up to 1024
- * (forward) / 1280 (backward) vectors; wider rows return
- * ADALN_ERR_UNSUPPORTED.  The workspace of adaln_bwd_segments is
+ * The per-row math is that of adaln_fwd / adaln_bwd.  The forward takes every
+ * row width adaln_fwd takes; the backward rows of up to 1280 vectors (D <=
+ * 10240 bf16 / 5120 f32), wider rows return ADALN_ERR_UNSUPPORTED.  The workspace of adaln_bwd_segments is
  * adaln_bwd_segments_workspace_bytes(seg_offsets, nseg, D, dtype) bytes; the
  * host arrays are read during the call only.
  */

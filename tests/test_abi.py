@@ -162,8 +162,11 @@ def test_segments_validation(lib):
     many, _, k4 = _table(list(range(130)))
     assert f(p, p, p, p, p, p, many, None, 129, 129, 1536, 1,
              None) == _lib.ERR_INVALID
-    # rows wider than the segment kernels take
-    assert f(p, p, p, p, p, p, off, mod, 2, 2, 16384, 1,
+    # rows wider than the segment kernels take (the forward takes every
+    # width adaln_fwd takes)
+    assert f(p, p, p, p, p, p, off, mod, 2, 2, 32776, 1,
+             None) == _lib.ERR_UNSUPPORTED
+    assert f(p, p, p, p, p, p, off, mod, 2, 2, 16388, 0,
              None) == _lib.ERR_UNSUPPORTED
     g = lib.adaln_bwd_segments
     need = lib.adaln_bwd_segments_workspace_bytes(off, 2, 1536, 1)

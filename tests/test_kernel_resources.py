@@ -68,3 +68,15 @@ def test_wide_backward_kernels_do_not_spill(usage):
     assert len(wide) >= 24
     spills = {k: v for k, v in wide.items() if v}
     assert not spills, spills
+
+
+def test_forward_tile_kernels_spill_only_at_the_widest_bf16(usage):
+    """The tile forward (rows past 1024 vectors) spills only in its 8-vector
+    bf16 instantiations, which serve the widest rows (3585-4096 vectors)
+    alone: two wavefronts per SIMD are the least its 8-wavefront workgroups
+    run at."""
+    tile = {k: v for k, v in usage["fwd.hip"].items()
+            if "fwd_tile_kernel" in k}
+    assert len(tile) >= 20
+    spills = {k: v for k, v in tile.items() if v and "4bf16ELi8E" not in k}
+    assert not spills, spills

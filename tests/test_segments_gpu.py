@@ -47,6 +47,7 @@ SMALL = [
     (8192, "bf16", [300, 0, 17, 1001], [1, 0, 1, 2], 3),        # two-wavefront rows
     (7000, "bf16", [5, 64, 3], None, 3),                        # ragged two-wavefront
     (4096, "f32", [100, 257], [0, 0], 1),
+    (10240, "bf16", [33, 0, 120], [0, 1, 0], 2),   # widest bwd; tile forward
 ]
 
 
@@ -139,18 +140,65 @@ def test_deterministic(A):
         assert torch.equal(a[k], b[k]), k
 
 
+WIDE_FORWARD = [
+    # D, dtype, lengths, seg_mod, nmod: rows past 1024 vectors (tile kernel)
+    (16384, "bf16", [10, 20, 0, 7], [1, 0, 1, 0], 2),
+    (32768, "bf16", [3, 5], None, 2),                 # widest row
+    (12288, "bf16", [1, 200, 31], [0, 0, 0], 1),
+    (16384, "f32", [4, 9], None, 2),                  # widest f32 row
+    (8200, "bf16", [64, 1], None, 2),                 # ragged, just past 1024
+]
+
+
+@pytest.mark.parametrize("case", range(len(WIDE_FORWARD)))
+def test_wide_forward_full(A, case):
+    """The forward of rows wider than one wavefront holds, packed, against
+    the oracle on every element."""
+    import oracle
+    D, dt, lengths, mods, nmod = WIDE_FORWARD[case]
+    _say(f"wide forward case {case}: D={D} {dt} lengths={lengths}")
+    inp = synth.make_packed(_wl(D, dt), lengths, mods, nmod=nmod, seed=case)
+    dev = P.packed_to_device(inp)
+    y, mean, rstd = A.fwd_segments(dev["x"], dev["scale"], dev["shift"],
+                                   inp.seg_offsets, inp.seg_mod)
+    torch.cuda.synchronize()
+    ry, rm, rr = oracle.fwd_segments(inp.x, inp.scale, inp.shift,
+                                     inp.seg_offsets, inp.seg_mod)
+    for r in P.check_out("y", y.cpu(), ry, dt):
+        _say(f"  {r}")
+    for r in P.check_stats(mean.cpu(), rstd.cpu(), rm, rr, inp.x):
+        _say(f"  {r}")
+
+
+def test_wide_forward_uniform_matches_batched(A):
+    """Equal segments with the identity table through the tile kernel equal
+    the batched forward bit for bit (same per-row arithmetic)."""
+    B, N, D = 3, 300, 16384
+    inp = synth.make_packed(_wl(D, "bf16"), [N] * B, seed=5)
+    dev = P.packed_to_device(inp)
+    y, mean, rstd = A.fwd_segments(dev["x"], dev["scale"], dev["shift"],
+                                   inp.seg_offsets)
+    ref = A.fwd(dev["x"].view(B, N, D), dev["scale"], dev["shift"])
+    torch.cuda.synchronize()
+    assert torch.equal(y, ref[0].view(B * N, D))
+    assert torch.equal(mean, ref[1].view(-1))
+    assert torch.equal(rstd, ref[2].view(-1))
+
+
 def test_wide_rows_rejected(A):
-    """Rows past the packed kernels' widths (1024 vectors forward, 1280
-    backward) are refused before anything is enqueued."""
+    """Rows past the packed backward's width (1280 vectors) are refused
+    before anything is enqueued; so are rows past the forward's (4096)."""
     inp = synth.make_packed(_wl(16384, "bf16"), [10, 20], seed=1)
     dev = P.packed_to_device(inp)
-    with pytest.raises(A.AdalnError) as e:
-        A.fwd_segments(dev["x"], dev["scale"], dev["shift"], inp.seg_offsets)
-    assert e.value.code == -6
     mean = torch.zeros(30, device="cuda")
     with pytest.raises(A.AdalnError) as e:
         A.bwd_segments(dev["dy"], dev["x"], dev["scale"], mean, mean,
                        inp.seg_offsets)
+    assert e.value.code == -6
+    x = torch.zeros(4, 32776, device="cuda", dtype=torch.bfloat16)
+    v = torch.zeros(1, 32776, device="cuda", dtype=torch.bfloat16)
+    with pytest.raises(A.AdalnError) as e:
+        A.fwd_segments(x, v, v, np.array([0, 4], dtype=np.int64))
     assert e.value.code == -6
 
 
