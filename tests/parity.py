@@ -15,6 +15,9 @@ Tolerances (per element; r = oracle value in float64, g = GPU value):
   1e-4 * rms, i.e. the stored value is the correctly rounded bfloat16 of a
   float32 result that lies within 1e-4 * rms of the exact one.  Without it
   the 2e-2 bound would be vacuous for dx, whose entries are about 1e-2.
+* bfloat16 outputs, also reported: the normwise relative error
+  ||g - r||_2 / ||r||_2, held to <= 1e-2 (bfloat16 rounding alone gives
+  about 2e-3).
 * dscale, dshift (float32 sums over N): |g - r| <= 1e-3 * max(|r|, rms).
 * mean: |g - r| <= 1e-5 * max(|r|, rms of the row's x);
   rstd: |g - r| <= 1e-5 * |r|.
@@ -35,6 +38,7 @@ STRICT_RTOL = 2.0 ** -8
 STRICT_RMS = 1e-4
 DMOD_RTOL = 1e-3
 STAT_RTOL = 1e-5
+NORMWISE_MAX = 1e-2
 
 
 def _np(t) -> np.ndarray:
@@ -54,12 +58,15 @@ class Report:
     max_ratio: float      # max over elements of err / allowed (<= 1 passes)
     over_plain: int = 0   # bf16: elements over the plain 2e-2 bound
     n: int = 0
+    normwise: Optional[float] = None  # bf16: ||g - r|| / ||r||
 
     def __str__(self):
         s = (f"{self.name}: n={self.n} max_err={self.max_err:.3e} "
              f"worst/allowed={self.max_ratio:.3f}")
         if self.over_plain:
             s += f" over_2e-2={self.over_plain}"
+        if self.normwise is not None:
+            s += f" normwise={self.normwise:.2e}"
         return s
 
 
@@ -83,6 +90,10 @@ def check_out(name: str, got, ref, dtype: str) -> Sequence[Report]:
     over = int(np.sum(np.abs(g - r) > BF16_ATOL))
     a = _judge(name + "[contract]", g, r, BF16_ATOL + BF16_RTOL * np.abs(r),
                over)
+    ref_norm = float(np.linalg.norm(r))
+    if ref_norm > 0:
+        a.normwise = float(np.linalg.norm(g - r)) / ref_norm
+        assert a.normwise <= NORMWISE_MAX, f"parity failure: {a}"
     b = _judge(name + "[strict]", g, r,
                STRICT_RTOL * np.abs(r) + STRICT_RMS * rms + 1e-30)
     return [a, b]
