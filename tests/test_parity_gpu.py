@@ -79,6 +79,8 @@ def test_video_bucket_full(A):
     (1100, 1, 5120, "bf16", "outliers"),   # several samples per workgroup
     (2000, 3, 64, "f32", "normal"),
     (300, 17, 520, "bf16", "normal"),      # many samples, ragged row
+    (6, 8192, 3072, "bf16", "offset"),     # long samples: 2 in flight (fwd)
+    (8, 6000, 2048, "f32", "normal"),      # long samples: 4 in flight (fwd)
     # backward rows split between two wavefronts (321..1280 vectors; two
     # wavefronts per SIMD up to 640)
     (3, 123, 2568, "bf16", "offset"),      # narrowest, ragged half
