@@ -37,6 +37,8 @@ SIGNATURES = {
                                 _VP]),
     "adaln_bwd_fused_plan": (_INT, [_I64, _I64, _I64, _INT,
                                     ctypes.POINTER(ctypes.c_int64)]),
+    "adaln_plan": (_INT, [_INT, _I64, _I64, _I64, _INT,
+                          ctypes.POINTER(ctypes.c_int64)]),
     "adaln_bwd_dx": (_INT, [_VP, _VP, _VP, _VP, _VP, _VP, _I64, _I64, _I64,
                             _INT, _VP]),
     "adaln_bwd_dmod": (_INT, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _I64,

@@ -528,6 +528,31 @@ ADALN_API int adaln_bwd_fused_plan(int64_t B, int64_t N, int64_t D,
   return ok();
 }
 
+ADALN_API int adaln_plan(int which, int64_t B, int64_t N, int64_t D,
+                         int dtype, int64_t *out) {
+  ADALN_TRY(check_shape(B, N, D, dtype));
+  if (out == nullptr) return fail(ADALN_ERR_INVALID, "out is NULL");
+  if (which != 0 && which != 1)
+    return fail(ADALN_ERR_INVALID,
+                "which must be 0 (forward) or 1 (fused backward), got %d",
+                which);
+  const int64_t nvec = D / elems_per_vec(dtype);
+  StreamPlan sp;
+  TilePlan tp;
+  if (choose_stream_plan(B, N, nvec, which == 1, &sp)) {
+    const int64_t walkers = 4 / sp.W;  // four-wavefront workgroups
+    const int64_t v[6] = {sp.V, sp.W, sp.grid, sp.bps, sp.groups, walkers};
+    std::copy(v, v + 6, out);
+  } else if (which == 0 && choose_tile_plan(B, N, nvec, &tp)) {
+    const int64_t v[6] = {tp.V, tp.W, tp.grid, tp.bps, tp.groups, 1};
+    std::copy(v, v + 6, out);
+  } else {
+    return fail(ADALN_ERR_UNSUPPORTED, "no %s plan for D=%lld",
+                which ? "fused backward" : "forward", (long long)D);
+  }
+  return ok();
+}
+
 ADALN_API int adaln_bwd_finish(const void *workspace,
                                size_t workspace_bytes_given, float *dscale,
                                float *dshift, int64_t B, int64_t N, int64_t D,

@@ -243,6 +243,21 @@ def bwd_fused_plan(B: int, N: int, D: int, dtype: torch.dtype) -> dict:
                 partial_rows=out[3])
 
 
+def plan(which: str, B: int, N: int, D: int, dtype: torch.dtype) -> dict:
+    """How :func:`fwd` (``which="fwd"``) or :func:`bwd_fused` (``"bwd"``)
+    splits a [B, N, D] batch into work (host-only): vectors per lane,
+    wavefronts per row, workgroups, workgroups per sample, samples in
+    flight, row walkers per workgroup."""
+    if which not in ("fwd", "bwd"):
+        raise ValueError(f"which must be 'fwd' or 'bwd', got {which!r}")
+    out = (ctypes.c_int64 * 6)()
+    rc = _lib.load().adaln_plan(0 if which == "fwd" else 1, B, N, D,
+                                _DTYPES.get(dtype, -1), out)
+    _lib.check(rc, "adaln_plan")
+    return dict(V=out[0], waves_per_row=out[1], workgroups=out[2],
+                bps=out[3], groups=out[4], walkers=out[5])
+
+
 class SegTable:
     """Host copy of a segment table in the ABI's layout (int64 offsets,
     int32 modulation indices).  The segment functions accept one in place of

@@ -150,6 +150,21 @@ int adaln_bwd_fused_plan(int64_t B, int64_t N, int64_t D, int dtype,
                          int64_t *out);
 
 /*
+ * How adaln_fwd (which = 0) or adaln_bwd_fused (which = 1) splits a batch
+ * into work, for callers that account for it and for tests of the planner.
+ * Fills out[0..5] with {vectors per lane V, wavefronts per row W, workgroups
+ * launched, workgroups per sample bps, samples in flight groups, row walkers
+ * per workgroup}.  Workgroup g with g / bps < groups works on samples
+ * g / bps, g / bps + groups, ... in turn; in each, its walker w visits rows
+ * (g % bps) * walkers + w, then every bps * walkers rows.  A walker is one
+ * wavefront (W = 1) or the W wavefronts that share a row.  Returns
+ * ADALN_ERR_UNSUPPORTED where the entry point would take another path (rows
+ * too wide for the fused backward).  Host-only; no HIP call.
+ */
+int adaln_plan(int which, int64_t B, int64_t N, int64_t D, int dtype,
+               int64_t *out);
+
+/*
  * Backward, input gradient only: dx from dy, x, scale and the saved
  * mean/rstd, one kernel launch (arguments as in adaln_bwd).  The pages give
  * no design for dx; it is the exact gradient of the formula above.

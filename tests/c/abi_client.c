@@ -52,6 +52,14 @@ int main(void)
         CHECK(adaln_bwd_fused_plan(1, 1000, 8192, ADALN_BF16, plan) == ADALN_OK);
         CHECK(plan[1] == 2);
     }
+    {
+        int64_t p[6];
+        CHECK(adaln_plan(0, 1, 75600, 5120, ADALN_BF16, p) == ADALN_OK);
+        CHECK(p[1] == 1 && p[2] == p[3] && p[5] == 4);
+        CHECK(adaln_plan(1, 1, 75600, 5120, ADALN_BF16, p) == ADALN_OK);
+        CHECK(p[1] == 2 && p[5] == 2);
+        CHECK(adaln_plan(2, 1, 75600, 5120, ADALN_BF16, p) == ADALN_ERR_INVALID);
+    }
     /* an invalid call enqueues nothing and explains itself */
     CHECK(adaln_fwd(NULL, NULL, NULL, NULL, NULL, NULL, 1, 1, 64, 9, NULL) ==
           ADALN_ERR_DTYPE);

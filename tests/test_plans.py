@@ -1,0 +1,116 @@
+"""The launch planner, on the host: for seeded random shapes over every
+kernel family, the plans adaln_plan reports, replayed through the work
+mapping the header documents (workgroup g -> samples g / bps, + groups, ...;
+walker w -> rows (g % bps) * walkers + w, + bps * walkers, ...), visit every
+token row exactly once, fit the resident grid, and for the fused backward
+give each (sample, workgroup) pair its own partial row inside the
+workspace.  The shape-dependent choices are pinned too: the wavefront
+pairs past 320 vectors, the fewest long samples in flight in the forward,
+and the balanced workgroups per sample.  CPU only."""
+
+import numpy as np
+import pytest
+import torch
+
+import adaln_fwd_amd as A
+
+BF16, F32 = torch.bfloat16, torch.float32
+D_BF16 = [8, 520, 1536, 2560, 2568, 3072, 4096, 5120, 5128, 7000, 8192,
+          10240, 12288, 16384, 32768]
+D_F32 = [4, 64, 1024, 1280, 1288, 2560, 4096, 8192, 16384]
+MAX_GRID = 256 * 8   # 256 CUs, at most 8 workgroups each
+
+
+def _shapes(seed, n):
+    g = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        dt = BF16 if g.random() < 0.6 else F32
+        D = int(g.choice(D_BF16 if dt is BF16 else D_F32))
+        B = int(np.exp(g.uniform(0, np.log(3000))))
+        N = int(np.exp(g.uniform(0, np.log(80000))))
+        N = max(1, min(N, 2_000_000 // B))
+        out.append((B, N, D, dt))
+    return out
+
+
+def _visits(p, B, N):
+    """Times each (sample, row) is visited under the documented mapping."""
+    count = np.zeros((B, N), dtype=np.int32)
+    bps, groups, walkers = p["bps"], p["groups"], p["walkers"]
+    stride = bps * walkers
+    for g in range(p["workgroups"]):
+        slot, k = divmod(g, bps)
+        if slot >= groups:
+            continue
+        for w in range(walkers):
+            count[slot::groups, k * walkers + w::stride] += 1
+    return count
+
+
+@pytest.mark.parametrize("B,N,D,dt", _shapes(7, 300))
+def test_every_row_once(B, N, D, dt):
+    for which in ("fwd", "bwd"):
+        try:
+            p = A.plan(which, B, N, D, dt)
+        except A.AdalnError as e:
+            assert which == "bwd" and e.code == -6
+            assert D // (8 if dt is BF16 else 4) > 1280
+            continue
+        assert 1 <= p["bps"] and 1 <= p["groups"]
+        assert p["workgroups"] == p["bps"] * min(p["groups"], B)
+        assert p["bps"] * p["groups"] <= MAX_GRID
+        # four-wavefront workgroups of row walkers, or one row at a time
+        # shared by all the workgroup's wavefronts (the tile forward)
+        assert p["walkers"] * p["waves_per_row"] == 4 or p["walkers"] == 1
+        assert np.all(_visits(p, B, N) == 1), (which, p)
+        if which == "bwd":
+            # partial row b * bps + (g % bps) of [B, bps, D], and room for it
+            q = A.bwd_fused_plan(B, N, D, dt)
+            assert q["partial_rows"] == p["bps"]
+            need = 2 * B * p["bps"] * D * 4
+            assert A.bwd_workspace_bytes(B, N, D, dt) >= need
+
+
+def test_rows_past_320_vectors_take_pairs():
+    assert A.plan("bwd", 1, 75600, 2560, BF16)["waves_per_row"] == 1
+    assert A.plan("bwd", 1, 75600, 2568, BF16)["waves_per_row"] == 2
+    assert A.plan("bwd", 1, 75600, 5120, BF16)["waves_per_row"] == 2
+    assert A.plan("bwd", 1, 75600, 1280, F32)["waves_per_row"] == 1
+    assert A.plan("bwd", 1, 75600, 1288, F32)["waves_per_row"] == 2
+    # the forward keeps one wavefront per row up to 1024 vectors
+    assert A.plan("fwd", 1, 75600, 8192, BF16)["waves_per_row"] == 1
+    assert A.plan("fwd", 1, 75600, 8200, BF16)["waves_per_row"] > 1
+
+
+def test_long_samples_fewer_in_flight_in_the_forward():
+    # 16 samples of 8190 rows at D = 3072: four in flight (4 each in turn);
+    # two would leave a wavefront 15.99 rows of a sample
+    p = A.plan("fwd", 16, 8190, 3072, BF16)
+    assert p["groups"] == 4
+    assert 8190 / (p["bps"] * p["walkers"]) >= 16
+    # 8 samples of 16380 rows: two in flight, 32 rows per wavefront each
+    p = A.plan("fwd", 8, 16380, 3072, BF16)
+    assert p["groups"] == 2 and 16380 / (p["bps"] * p["walkers"]) >= 16
+    # short samples keep one group each; the backward never changes
+    assert A.plan("fwd", 84, 1560, 3072, BF16)["groups"] >= 84
+    assert A.plan("bwd", 16, 8190, 3072, BF16)["groups"] >= 16
+
+
+def test_balanced_workgroups_per_sample():
+    # 16 x 1560 rows, D = 1536: 30 workgroups of 4 walkers give every walker
+    # 13 rows, as 32 would (12.2, rounded up) -- the fewest that do
+    p = A.plan("bwd", 16, 1560, 1536, BF16)
+    rows = -(-1560 // (p["bps"] * p["walkers"]))
+    assert rows == -(-1560 // (32 * p["walkers"]))
+    assert -(-1560 // ((p["bps"] - 1) * p["walkers"])) > rows
+
+
+def test_plan_validation():
+    with pytest.raises(A.AdalnError):
+        A.plan("fwd", 1, 1, 12, BF16)          # D not a multiple of 8
+    with pytest.raises(ValueError):
+        A.plan("both", 1, 1, 64, BF16)
+    with pytest.raises(A.AdalnError) as e:
+        A.plan("bwd", 1, 10, 16384, BF16)
+    assert e.value.code == -6
