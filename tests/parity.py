@@ -70,7 +70,7 @@ class Report:
         return s
 
 
-def _judge(name, g, r, allowed, over_plain=0) -> Report:
+def _grade(name, g, r, allowed, over_plain=0) -> Report:
     err = np.abs(g - r)
     ratio = np.max(err / allowed) if err.size else 0.0
     rep = Report(name, float(err.max()) if err.size else 0.0, float(ratio),
@@ -86,15 +86,15 @@ def check_out(name: str, got, ref, dtype: str) -> Sequence[Report]:
     assert np.all(np.isfinite(g)), f"{name}: non-finite GPU values"
     rms = _rms(r)
     if dtype == "f32":
-        return [_judge(name, g, r, F32_RTOL * np.maximum(np.abs(r), rms))]
+        return [_grade(name, g, r, F32_RTOL * np.maximum(np.abs(r), rms))]
     over = int(np.sum(np.abs(g - r) > BF16_ATOL))
-    a = _judge(name + "[contract]", g, r, BF16_ATOL + BF16_RTOL * np.abs(r),
+    a = _grade(name + "[contract]", g, r, BF16_ATOL + BF16_RTOL * np.abs(r),
                over)
     ref_norm = float(np.linalg.norm(r))
     if ref_norm > 0:
         a.normwise = float(np.linalg.norm(g - r)) / ref_norm
         assert a.normwise <= NORMWISE_MAX, f"parity failure: {a}"
-    b = _judge(name + "[strict]", g, r,
+    b = _grade(name + "[strict]", g, r,
                STRICT_RTOL * np.abs(r) + STRICT_RMS * rms + 1e-30)
     return [a, b]
 
@@ -103,7 +103,7 @@ def check_dmod(name: str, got, ref) -> Report:
     g, r = _np(got), _np(ref)
     assert g.shape == r.shape
     rms = _rms(r)
-    return _judge(name, g, r, DMOD_RTOL * np.maximum(np.abs(r), rms) + 1e-30)
+    return _grade(name, g, r, DMOD_RTOL * np.maximum(np.abs(r), rms) + 1e-30)
 
 
 def check_stats(got_mean, got_rstd, ref_mean, ref_rstd, x_rows) -> Sequence[Report]:
@@ -111,9 +111,9 @@ def check_stats(got_mean, got_rstd, ref_mean, ref_rstd, x_rows) -> Sequence[Repo
     gr, rr = _np(got_rstd), _np(ref_rstd)
     xr = _np(x_rows)
     row_rms = np.sqrt(np.mean(xr * xr, axis=-1))
-    a = _judge("mean", gm, rm, STAT_RTOL * np.maximum(np.abs(rm), row_rms)
+    a = _grade("mean", gm, rm, STAT_RTOL * np.maximum(np.abs(rm), row_rms)
                + 1e-30)
-    b = _judge("rstd", gr, rr, STAT_RTOL * np.abs(rr))
+    b = _grade("rstd", gr, rr, STAT_RTOL * np.abs(rr))
     return [a, b]
 
 
