@@ -1,12 +1,13 @@
 """The mixed-length batch schedule at full size: 64 buckets drawn uniformly
 from S in {1560, 8190, 16380, 32760}, each with the dual-constraint batch
 B_shape(S) (M_mem = 131072, M_comp = 2.2e9, p = 2), D = 3072, bf16, run
-through adaln_fwd and adaln_bwd exactly as the benchmark does.
+through adaln_fwd and adaln_bwd exactly as the benchmark does: one set of
+device buffers sized for the largest bucket, reused by every bucket.
 
-Per bucket: y, dx, mean and rstd on sampled token rows against the oracle,
-and dshift against its closed form (the float64 sum of dy over the tokens of
-each sample).  dscale and dshift in full against the oracle for the first
-bucket of each sequence length.
+One test per bucket: y, dx, mean and rstd on 48+ sampled token rows (the
+first and last 8 rows included) against the oracle; dscale and dshift in
+full against the oracle, and dshift also against its closed form (the
+float64 sum of dy over the tokens of each sample).
 """
 
 import numpy as np
@@ -33,63 +34,61 @@ def test_bucket_sizes_match_oracle_and_constraints(oracle_mod):
                           and b * S ** 2 <= synth.MIXED_M_COMP)
 
 
-def test_mixed_schedule_full_size(oracle_mod):
+@pytest.fixture(scope="module")
+def schedule():
+    """The schedule's lengths, batch sizes and the shared device buffers."""
     import adaln_fwd_amd as A
     sched = synth.mixed_schedule()
+    assert len(sched) == synth.MIXED_BUCKETS
     shapes = {S: A.bshape(S, synth.MIXED_M_MEM, synth.MIXED_M_COMP,
                           synth.MIXED_P) for S in set(sched)}
     D = synth.MIXED_SCHEDULE.D
     max_rows = max(b * S for S, b in shapes.items())
     dev = torch.device("cuda")
-    x_buf = torch.empty(max_rows * D, dtype=torch.bfloat16, device=dev)
-    dy_buf = torch.empty_like(x_buf)
-    y_buf = torch.empty_like(x_buf)
-    dx_buf = torch.empty_like(x_buf)
-    max_b = max(shapes.values())
-    ws = torch.empty(max(A.bwd_workspace_bytes(b, S, D, torch.bfloat16)
-                         for S, b in shapes.items()), dtype=torch.uint8,
-                     device=dev)
-    full_checked = set()
-    tokens = 0
-    for k, S in enumerate(sched):
-        B = shapes[S]
-        wl = synth.mixed_bucket(B, S)
-        _say(f"bucket {k}: B={B} S={S} D={D}")
-        inp = synth.make_inputs(wl, bucket=k)
-        n = B * S * D
-        x = x_buf[:n].view(B, S, D)
-        dy = dy_buf[:n].view(B, S, D)
-        y = y_buf[:n].view(B, S, D)
-        dx = dx_buf[:n].view(B, S, D)
-        x.copy_(inp.x)
-        dy.copy_(inp.dy)
-        scale = inp.scale.to(dev)
-        shift = inp.shift.to(dev)
-        _, mean, rstd = A.fwd(x, scale, shift, y=y)
-        _, dscale, dshift = A.bwd(dy, x, scale, mean, rstd, dx=dx,
-                                  workspace=ws)
-        rows = P.sample_rows(B * S, 48, seed=k)
-        idx = torch.from_numpy(rows).to(dev)
-        out = dict(y=y.view(B * S, D).index_select(0, idx).cpu(),
-                   dx=dx.view(B * S, D).index_select(0, idx).cpu(),
-                   mean=mean.view(-1).index_select(0, idx).cpu(),
-                   rstd=rstd.view(-1).index_select(0, idx).cpu(),
-                   dscale=dscale.cpu(), dshift=dshift.cpu())
-        torch.cuda.synchronize()
-        # the sampled rows, compared in the compact layout
-        compact = {key: out[key] for key in ("y", "dx")}
-        ref = P.oracle_rows(inp, rows)
-        P.check_out("y", compact["y"], ref["y"], "bf16")
-        P.check_out("dx", compact["dx"], ref["dx"], "bf16")
-        P.check_stats(out["mean"], out["rstd"], ref["mean"], ref["rstd"],
-                      ref["x"])
-        # dshift: the plain float64 sum of dy over each sample's tokens
-        P.check_dmod("dshift", out["dshift"],
-                     inp.dy.double().sum(dim=1).numpy())
-        if S not in full_checked:
-            full_checked.add(S)
-            for r in P.compare_full(inp, out, "bf16", with_rows=False):
-                _say(f"  full {r}")
-        tokens += B * S
-    _say(f"{len(sched)} buckets, {tokens} tokens checked")
-    assert full_checked == set(synth.MIXED_LENGTHS)
+    bufs = {k: torch.empty(max_rows * D, dtype=torch.bfloat16, device=dev)
+            for k in ("x", "dy", "y", "dx")}
+    bufs["ws"] = torch.empty(max(A.bwd_workspace_bytes(b, S, D, torch.bfloat16)
+                                 for S, b in shapes.items()),
+                             dtype=torch.uint8, device=dev)
+    yield sched, shapes, D, bufs
+    del bufs
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("k", range(synth.MIXED_BUCKETS))
+def test_mixed_bucket_full_size(schedule, k):
+    import adaln_fwd_amd as A
+    sched, shapes, D, bufs = schedule
+    S = sched[k]
+    B = shapes[S]
+    dev = bufs["x"].device
+    _say(f"bucket {k}: B={B} S={S} D={D}")
+    inp = synth.make_inputs(synth.mixed_bucket(B, S), bucket=k)
+    n = B * S * D
+    x, dy, y, dx = (bufs[key][:n].view(B, S, D) for key in ("x", "dy", "y",
+                                                             "dx"))
+    x.copy_(inp.x)
+    dy.copy_(inp.dy)
+    scale = inp.scale.to(dev)
+    shift = inp.shift.to(dev)
+    _, mean, rstd = A.fwd(x, scale, shift, y=y)
+    _, dscale, dshift = A.bwd(dy, x, scale, mean, rstd, dx=dx,
+                              workspace=bufs["ws"])
+    rows = P.sample_rows(B * S, 48, seed=k)
+    idx = torch.from_numpy(rows).to(dev)
+    got = dict(y=y.view(B * S, D).index_select(0, idx).cpu(),
+               dx=dx.view(B * S, D).index_select(0, idx).cpu(),
+               mean=mean.view(-1).index_select(0, idx).cpu(),
+               rstd=rstd.view(-1).index_select(0, idx).cpu(),
+               dscale=dscale.cpu(), dshift=dshift.cpu())
+    torch.cuda.synchronize()
+    ref = P.oracle_rows(inp, rows)
+    reps = []
+    reps += P.check_out("y", got["y"], ref["y"], "bf16")
+    reps += P.check_out("dx", got["dx"], ref["dx"], "bf16")
+    reps += P.check_stats(got["mean"], got["rstd"], ref["mean"], ref["rstd"],
+                          ref["x"])
+    reps += P.compare_full(inp, got, "bf16", with_rows=False)
+    reps.append(P.check_dmod("dshift[closed form]", got["dshift"],
+                             inp.dy.double().sum(dim=1).numpy()))
+    _say("; ".join(str(r) for r in reps))
