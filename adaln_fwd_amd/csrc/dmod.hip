@@ -105,19 +105,8 @@ __global__ __launch_bounds__(kBlock) void dmod_partial_kernel(
   }
 }
 
-// dscale[b, d] = sum over t = 0 .. n_tiles-1 of part_scale[b, t, d] (and the
-// same for dshift).  One lane per feature.  A workgroup of 16 wavefronts
-// covers 16 / wpc column blocks of 64 features; the wpc wavefronts of a
-// column block split the tiles into wpc contiguous ranges, each summed in
-// index order with all its loads in flight, and the range sums are added in
-// range order.  wpc is the smallest power of two with n_tiles <= 32 * wpc (at
-// most 16), so every wavefront has work and, up to 512 tiles, issues all its
-// loads in one batch (one round trip to memory): one feature per lane
-// spreads a 5120-feature sample with 512 tiles over 80 workgroups, and a few
-// tiles per sample take 16 column blocks a workgroup.  With n_tiles == 0 the
-// outputs are zero.
+// Waves per workgroup (at most) of the finishing kernels.
 constexpr int kFinishWaves = 16;
-constexpr int kFinishBatch = 32;
 
 // log2 of the wavefronts per column block that sum `rows` partial rows at
 // most `batch` rows each (at most 16 wavefronts).
@@ -127,35 +116,75 @@ static int finish_wpc_log2(int64_t rows, int batch) {
   return l;
 }
 
+// dscale[b, d] = sum over t = 0 .. n_tiles-1 of part_scale[b, t, d] (and the
+// same for dshift).  The partials are few megabytes at most, so the kernel's
+// time is the issue rate of the CUs it runs on: it is spread over as many
+// CUs as the shape allows.
+//
+// A column block is F consecutive features (F = 64, 32 or 16) of one sample.
+// A wavefront splits into R = 64 / F lane groups: lane l reads feature
+// l % F and its group g = l / F, so one load instruction covers R partial
+// rows of the block (R segments of 4F contiguous bytes).  The host picks F
+// so that the blocks cover the CUs (64 for 16 samples of 1536 features: 384
+// blocks; 32 for one sample of 5120: 160; 16 for one sample of 1536: 96).
+// wpc wavefronts (a power of two, at most 16) share a block and cut the
+// tiles into wpc contiguous slices; a workgroup holds cpb blocks (wpc * cpb
+// <= 16 wavefronts).
+//
+// Order of the sums, fixed by (n_tiles, F, wpc): in slice j, group g adds
+// the tiles t0 + g, t0 + g + R, ... in increasing order (up to kFinishBatch
+// loads per array in flight); the R group sums are added in group order
+// within the wavefront, and the slice sums in slice order through LDS.  No
+// atomics: the result is reproducible bit for bit.  With n_tiles == 0 the
+// outputs are zero.
+constexpr int kFinishBatch = 8;
+
+// Workgroups are dealt to the 8 XCDs of the part round robin (workgroup i to
+// XCD i % 8), and each XCD has its own L2.  This maps workgroup i to a
+// logical block so that each XCD takes a contiguous run of blocks: column
+// blocks that share a 128-byte line then meet in the same L2.  A bijection of
+// [0, grid): the last grid % 8 workgroups keep their own index.
+__device__ __forceinline__ int64_t xcd_block(int64_t id, int64_t grid) {
+  constexpr int64_t kXcds = 8;
+  const int64_t per = grid / kXcds;
+  return id < per * kXcds ? (id % kXcds) * per + id / kXcds : id;
+}
+
+template <int F>
 __global__ __launch_bounds__(kFinishWaves * kWave) void dmod_finish_kernel(
     const float *__restrict__ part_scale, const float *__restrict__ part_shift,
     float *__restrict__ dscale, float *__restrict__ dshift, int32_t D,
-    int32_t n_tiles, int32_t col_blocks, int32_t wpc_log2, int64_t total_cols) {
-  __shared__ float stage[kFinishWaves][2][kWave];
+    int32_t n_tiles, int32_t col_blocks, int32_t wpc_log2, int32_t cpb,
+    int64_t total_cols) {
+  constexpr int R = kWave / F;
+  __shared__ float stage[kFinishWaves][2][F];
   const int lane = lane_id();
   const int wave = wave_id();
+  const int f = lane % F;
+  const int g = lane / F;
   const int wpc = 1 << wpc_log2;
-  const int cpb = kFinishWaves >> wpc_log2;  // column blocks per workgroup
   const int slice = wave & (wpc - 1);
   const int t0 = (int)((int64_t)slice * n_tiles / wpc);
   const int t1 = (int)((int64_t)(slice + 1) * n_tiles / wpc);
 
-  for (int64_t blk = blockIdx.x; blk * cpb < total_cols; blk += gridDim.x) {
+  for (int64_t blk = xcd_block(blockIdx.x, gridDim.x); blk * cpb < total_cols;
+       blk += gridDim.x) {
     const int64_t col = blk * cpb + (wave >> wpc_log2);  // (b, column block)
     const bool live = col < total_cols;
     const int cb = live ? (int)(col % col_blocks) : 0;
     const int b = live ? (int)(col / col_blocks) : 0;
-    const int c = cb * kWave + lane;
+    const int c = cb * F + f;
     const bool ok = live && c < D;
     const int64_t base = (int64_t)b * n_tiles * D + c;
     float as = 0.f, ah = 0.f;
-    for (int t = t0; t < t1; t += kFinishBatch) {
+    for (int t = t0 + g; t < t1; t += R * kFinishBatch) {
       float vs[kFinishBatch], vh[kFinishBatch];
 #pragma unroll
       for (int i = 0; i < kFinishBatch; ++i) {
-        const bool in = ok && t + i < t1;
-        vs[i] = in ? part_scale[base + (int64_t)(t + i) * D] : 0.f;
-        vh[i] = in ? part_shift[base + (int64_t)(t + i) * D] : 0.f;
+        const int row = t + i * R;
+        const bool in = ok && row < t1;
+        vs[i] = in ? part_scale[base + (int64_t)row * D] : 0.f;
+        vh[i] = in ? part_shift[base + (int64_t)row * D] : 0.f;
       }
 #pragma unroll
       for (int i = 0; i < kFinishBatch; ++i) {
@@ -163,15 +192,26 @@ __global__ __launch_bounds__(kFinishWaves * kWave) void dmod_finish_kernel(
         ah += vh[i];
       }
     }
-    if (slice > 0) {
-      stage[wave][0][lane] = as;
-      stage[wave][1][lane] = ah;
+    // the R lane groups' sums, in group order (lanes of group 0 keep them)
+    if constexpr (R > 1) {
+      float ts = as, th = ah;
+#pragma unroll
+      for (int q = 1; q < R; ++q) {
+        ts += __shfl(as, lane + q * F);
+        th += __shfl(ah, lane + q * F);
+      }
+      as = ts;
+      ah = th;
+    }
+    if (slice > 0 && g == 0) {
+      stage[wave][0][f] = as;
+      stage[wave][1][f] = ah;
     }
     __syncthreads();
-    if (slice == 0 && ok) {
+    if (slice == 0 && g == 0 && ok) {
       for (int w = 1; w < wpc; ++w) {
-        as += stage[wave + w][0][lane];
-        ah += stage[wave + w][1][lane];
+        as += stage[wave + w][0][f];
+        ah += stage[wave + w][1][f];
       }
       dscale[(int64_t)b * D + c] = as;
       dshift[(int64_t)b * D + c] = ah;
@@ -291,15 +331,36 @@ hipError_t launch_dmod_finish(const float *part_scale,
                               const float *part_shift, float *dscale,
                               float *dshift, int32_t B, int32_t D,
                               int32_t n_tiles, hipStream_t stream) {
-  const int wl = finish_wpc_log2(n_tiles, kFinishBatch);
-  const int32_t col_blocks = (D + kWave - 1) / kWave;
+  // Column block width: 64 features when that gives every CU a block; else
+  // 32 when that still covers half the CUs (16-feature blocks would then
+  // put two workgroups on some CUs and split every 128-byte line between
+  // two blocks); else 16.  Measured on MI355X (finish alone): 1 x 5120
+  // features, 511 partial rows 5.9 -> 4.4 us; 1 x 1536, 512 rows
+  // 5.9 -> 3.8 us; 16 x 1536, 30 rows 5.5 -> 2.9 us.
+  constexpr int64_t kTargetCols = 256;
+  int F = 64;
+  if ((int64_t)B * ((D + 63) / 64) < kTargetCols)
+    F = (int64_t)B * ((D + 31) / 32) >= kTargetCols / 2 ? 32 : 16;
+  const int R = kWave / F;
+  const int wl = finish_wpc_log2(n_tiles, R * kFinishBatch);
+  const int wpc = 1 << wl;
+  const int32_t col_blocks = (D + F - 1) / F;
   const int64_t total_cols = (int64_t)col_blocks * B;
-  const int64_t cpb = kFinishWaves >> wl;
-  return launch_kernel_threads(dmod_finish_kernel,
-                               (total_cols + cpb - 1) / cpb,
-                               kFinishWaves * kWave, stream, part_scale,
-                               part_shift, dscale, dshift, D, n_tiles,
-                               col_blocks, (int32_t)wl, total_cols);
+  // column blocks per workgroup: as many as keep 256 workgroups or more
+  int64_t cpb = total_cols / kTargetCols;
+  if (cpb > kFinishWaves / wpc) cpb = kFinishWaves / wpc;
+  if (cpb < 1) cpb = 1;
+  const int threads = (int)(wpc * cpb) * kWave;
+  const int64_t blocks = (total_cols + cpb - 1) / cpb;
+  auto go = [&](auto kernel) {
+    return launch_kernel_threads(kernel, blocks, threads, stream, part_scale,
+                                 part_shift, dscale, dshift, D, n_tiles,
+                                 col_blocks, (int32_t)wl, (int32_t)cpb,
+                                 total_cols);
+  };
+  return F == 64 ? go(dmod_finish_kernel<64>)
+                 : F == 32 ? go(dmod_finish_kernel<32>)
+                           : go(dmod_finish_kernel<16>);
 }
 
 }  // namespace adaln

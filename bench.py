@@ -73,7 +73,7 @@ KERNEL_SYMBOLS = {
     "fwd": ("void adaln::fwd_stream_kernel",),
     "bwd_fused": ("void adaln::bwd_stream_kernel",
                   "void adaln::bwd_wide_kernel"),
-    "bwd_finish": ("adaln::dmod_finish_kernel",),
+    "bwd_finish": ("void adaln::dmod_finish_kernel",),
 }
 
 
