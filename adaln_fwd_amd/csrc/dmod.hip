@@ -222,65 +222,118 @@ __global__ __launch_bounds__(kFinishWaves * kWave) void dmod_finish_kernel(
 
 // Segment variant: dscale[m, d] = sum over the segments s with mod[s] == m,
 // in index order, of the partial rows of their workgroups
-// [wg_start[s], wg_start[s+1]).  As above, wpc wavefronts share a column
-// block (wpc from the most partial rows any modulation vector has); slice j
-// takes rows wg_start[s] + j, + wpc, ... of each such segment (up to 8 loads
-// per array in flight), and the slice sums are added in slice order.
-constexpr int kSegBatch = 8;
-
+// [wg_start[s], wg_start[s+1]).  Column blocks, lane groups, slices and
+// workgroups as in dmod_finish_kernel (blocks of F features of one
+// modulation vector m).  Order: slice j, group g adds, segment by segment in
+// index order, the rows wg_start[s] + j + g*wpc, then every R*wpc-th row
+// after it, in increasing order (up to kFinishBatch loads per array in
+// flight); the group sums are added in group order, the slice sums in slice
+// order.
+template <int F>
 __global__ __launch_bounds__(kFinishWaves * kWave) void finish_segments_kernel(
     const float *__restrict__ part_scale, const float *__restrict__ part_shift,
     float *__restrict__ dscale, float *__restrict__ dshift, int32_t D,
-    int32_t col_blocks, int32_t wpc_log2, int64_t total_cols, SegMap map) {
-  __shared__ float stage[kFinishWaves][2][kWave];
+    int32_t col_blocks, int32_t wpc_log2, int32_t cpb, int64_t total_cols,
+    SegMap map) {
+  constexpr int R = kWave / F;
+  __shared__ float stage[kFinishWaves][2][F];
   const int lane = lane_id();
   const int wave = wave_id();
+  const int f = lane % F;
+  const int g = lane / F;
   const int wpc = 1 << wpc_log2;
-  const int cpb = kFinishWaves >> wpc_log2;
   const int slice = wave & (wpc - 1);
+  const int step = wpc * R;  // rows between a group's consecutive rows
 
-  for (int64_t blk = blockIdx.x; blk * cpb < total_cols; blk += gridDim.x) {
+  for (int64_t blk = xcd_block(blockIdx.x, gridDim.x); blk * cpb < total_cols;
+       blk += gridDim.x) {
     const int64_t col = blk * cpb + (wave >> wpc_log2);  // (m, column block)
     const bool live = col < total_cols;
     const int cb = live ? (int)(col % col_blocks) : 0;
     const int m = live ? (int)(col / col_blocks) : -1;
-    const int c = cb * kWave + lane;
+    const int c = cb * F + f;
     const bool ok = live && c < D;
     float as = 0.f, ah = 0.f;
     for (int s = 0; s < map.nseg; ++s) {
       if (map.mod[s] != m) continue;
       const int end = map.wg_start[s + 1];
-      for (int w0 = map.wg_start[s] + slice; w0 < end; w0 += wpc * kSegBatch) {
-        float vs[kSegBatch], vh[kSegBatch];
+      for (int w0 = map.wg_start[s] + slice + g * wpc; w0 < end;
+           w0 += step * kFinishBatch) {
+        float vs[kFinishBatch], vh[kFinishBatch];
 #pragma unroll
-        for (int i = 0; i < kSegBatch; ++i) {
-          const int w = w0 + i * wpc;
+        for (int i = 0; i < kFinishBatch; ++i) {
+          const int w = w0 + i * step;
           const bool in = ok && w < end;
           vs[i] = in ? part_scale[(int64_t)w * D + c] : 0.f;
           vh[i] = in ? part_shift[(int64_t)w * D + c] : 0.f;
         }
 #pragma unroll
-        for (int i = 0; i < kSegBatch; ++i) {
+        for (int i = 0; i < kFinishBatch; ++i) {
           as += vs[i];
           ah += vh[i];
         }
       }
     }
-    if (slice > 0) {
-      stage[wave][0][lane] = as;
-      stage[wave][1][lane] = ah;
+    if constexpr (R > 1) {
+      float ts = as, th = ah;
+#pragma unroll
+      for (int q = 1; q < R; ++q) {
+        ts += __shfl(as, lane + q * F);
+        th += __shfl(ah, lane + q * F);
+      }
+      as = ts;
+      ah = th;
+    }
+    if (slice > 0 && g == 0) {
+      stage[wave][0][f] = as;
+      stage[wave][1][f] = ah;
     }
     __syncthreads();
-    if (slice == 0 && ok) {
+    if (slice == 0 && g == 0 && ok) {
       for (int w = 1; w < wpc; ++w) {
-        as += stage[wave + w][0][lane];
-        ah += stage[wave + w][1][lane];
+        as += stage[wave + w][0][f];
+        ah += stage[wave + w][1][f];
       }
       dscale[(int64_t)m * D + c] = as;
       dshift[(int64_t)m * D + c] = ah;
     }
     __syncthreads();
   }
+}
+
+// Launch shape of the finishing kernels for `vectors` modulation vectors
+// (samples) of D features whose largest sum has `rows` partial rows.
+struct FinishShape {
+  int F, wl, cpb, threads;
+  int32_t col_blocks;
+  int64_t total_cols, blocks;
+};
+
+static FinishShape finish_shape(int64_t vectors, int32_t D, int64_t rows) {
+  // Column block width: 64 features when that gives every CU a block; else
+  // 32 when that still covers half the CUs (16-feature blocks would then
+  // put two workgroups on some CUs and split every 128-byte line between
+  // two blocks); else 16.  Measured on MI355X (finish alone): 1 x 5120
+  // features, 511 partial rows 5.9 -> 4.5 us; 1 x 1536, 512 rows
+  // 5.9 -> 3.8 us; 16 x 1536, 30 rows 5.5 -> 2.9 us.
+  constexpr int64_t kTargetCols = 256;
+  FinishShape sh;
+  sh.F = 64;
+  if (vectors * ((D + 63) / 64) < kTargetCols)
+    sh.F = vectors * ((D + 31) / 32) >= kTargetCols / 2 ? 32 : 16;
+  const int R = kWave / sh.F;
+  sh.wl = finish_wpc_log2(rows, R * kFinishBatch);
+  const int wpc = 1 << sh.wl;
+  sh.col_blocks = (D + sh.F - 1) / sh.F;
+  sh.total_cols = (int64_t)sh.col_blocks * vectors;
+  // column blocks per workgroup: as many as keep 256 workgroups or more
+  int64_t cpb = sh.total_cols / kTargetCols;
+  if (cpb > kFinishWaves / wpc) cpb = kFinishWaves / wpc;
+  if (cpb < 1) cpb = 1;
+  sh.cpb = (int)cpb;
+  sh.threads = wpc * sh.cpb * kWave;
+  sh.blocks = (sh.total_cols + cpb - 1) / cpb;
+  return sh;
 }
 
 hipError_t launch_finish_segments(const float *part_scale,
@@ -296,15 +349,16 @@ hipError_t launch_finish_segments(const float *part_scale,
       if (map.mod[s] == m) rows += map.wg_start[s + 1] - map.wg_start[s];
     most = rows > most ? rows : most;
   }
-  const int wl = finish_wpc_log2(most, kSegBatch);
-  const int32_t col_blocks = (D + kWave - 1) / kWave;
-  const int64_t total_cols = (int64_t)col_blocks * nmod;
-  const int64_t cpb = kFinishWaves >> wl;
-  return launch_kernel_threads(finish_segments_kernel,
-                               (total_cols + cpb - 1) / cpb,
-                               kFinishWaves * kWave, stream, part_scale,
-                               part_shift, dscale, dshift, D, col_blocks,
-                               (int32_t)wl, total_cols, map);
+  const FinishShape sh = finish_shape(nmod, D, most);
+  auto go = [&](auto kernel) {
+    return launch_kernel_threads(kernel, sh.blocks, sh.threads, stream,
+                                 part_scale, part_shift, dscale, dshift, D,
+                                 sh.col_blocks, (int32_t)sh.wl,
+                                 (int32_t)sh.cpb, sh.total_cols, map);
+  };
+  return sh.F == 64 ? go(finish_segments_kernel<64>)
+                    : sh.F == 32 ? go(finish_segments_kernel<32>)
+                                 : go(finish_segments_kernel<16>);
 }
 
 hipError_t launch_dmod_partial(int dtype, const DmodPlan &plan,
@@ -331,36 +385,16 @@ hipError_t launch_dmod_finish(const float *part_scale,
                               const float *part_shift, float *dscale,
                               float *dshift, int32_t B, int32_t D,
                               int32_t n_tiles, hipStream_t stream) {
-  // Column block width: 64 features when that gives every CU a block; else
-  // 32 when that still covers half the CUs (16-feature blocks would then
-  // put two workgroups on some CUs and split every 128-byte line between
-  // two blocks); else 16.  Measured on MI355X (finish alone): 1 x 5120
-  // features, 511 partial rows 5.9 -> 4.4 us; 1 x 1536, 512 rows
-  // 5.9 -> 3.8 us; 16 x 1536, 30 rows 5.5 -> 2.9 us.
-  constexpr int64_t kTargetCols = 256;
-  int F = 64;
-  if ((int64_t)B * ((D + 63) / 64) < kTargetCols)
-    F = (int64_t)B * ((D + 31) / 32) >= kTargetCols / 2 ? 32 : 16;
-  const int R = kWave / F;
-  const int wl = finish_wpc_log2(n_tiles, R * kFinishBatch);
-  const int wpc = 1 << wl;
-  const int32_t col_blocks = (D + F - 1) / F;
-  const int64_t total_cols = (int64_t)col_blocks * B;
-  // column blocks per workgroup: as many as keep 256 workgroups or more
-  int64_t cpb = total_cols / kTargetCols;
-  if (cpb > kFinishWaves / wpc) cpb = kFinishWaves / wpc;
-  if (cpb < 1) cpb = 1;
-  const int threads = (int)(wpc * cpb) * kWave;
-  const int64_t blocks = (total_cols + cpb - 1) / cpb;
+  const FinishShape sh = finish_shape(B, D, n_tiles);
   auto go = [&](auto kernel) {
-    return launch_kernel_threads(kernel, blocks, threads, stream, part_scale,
-                                 part_shift, dscale, dshift, D, n_tiles,
-                                 col_blocks, (int32_t)wl, (int32_t)cpb,
-                                 total_cols);
+    return launch_kernel_threads(kernel, sh.blocks, sh.threads, stream,
+                                 part_scale, part_shift, dscale, dshift, D,
+                                 n_tiles, sh.col_blocks, (int32_t)sh.wl,
+                                 (int32_t)sh.cpb, sh.total_cols);
   };
-  return F == 64 ? go(dmod_finish_kernel<64>)
-                 : F == 32 ? go(dmod_finish_kernel<32>)
-                           : go(dmod_finish_kernel<16>);
+  return sh.F == 64 ? go(dmod_finish_kernel<64>)
+                    : sh.F == 32 ? go(dmod_finish_kernel<32>)
+                                 : go(dmod_finish_kernel<16>);
 }
 
 }  // namespace adaln
