@@ -117,9 +117,9 @@ static int finish_wpc_log2(int64_t rows, int batch) {
 }
 
 // dscale[b, d] = sum over t = 0 .. n_tiles-1 of part_scale[b, t, d] (and the
-// same for dshift).  The partials are few megabytes at most, so the kernel's
-// time is the issue rate of the CUs it runs on: it is spread over as many
-// CUs as the shape allows.
+// same for dshift).  The partials are 1-25 MB, so the kernel's time is the
+// issue rate of the CUs it runs on: it is spread over as many CUs as the
+// shape allows.
 //
 // A column block is F consecutive features (F = 64, 32 or 16) of one sample.
 // A wavefront splits into R = 64 / F lane groups: lane l reads feature
