@@ -532,13 +532,27 @@ ADALN_API int adaln_plan(int which, int64_t B, int64_t N, int64_t D,
                          int dtype, int64_t *out) {
   ADALN_TRY(check_shape(B, N, D, dtype));
   if (out == nullptr) return fail(ADALN_ERR_INVALID, "out is NULL");
-  if (which != 0 && which != 1)
+  if (which != 0 && which != 1 && which != 2)
     return fail(ADALN_ERR_INVALID,
-                "which must be 0 (forward) or 1 (fused backward), got %d",
+                "which must be 0 (forward), 1 (fused backward) or 2 "
+                "(finish), got %d",
                 which);
   const int64_t nvec = D / elems_per_vec(dtype);
   StreamPlan sp;
   TilePlan tp;
+  if (which == 2) {
+    // the partial rows each output sums: the fused plan's workgroups per
+    // sample, or the D-tile plan's tiles for rows too wide for it
+    const int64_t rows = choose_stream_plan(B, N, nvec, true, &sp)
+                             ? (B > 0 && N > 0 ? sp.bps : 0)
+                             : choose_dmod_plan(B, N, nvec).n_tiles;
+    const FinishPlan fp = finish_plan(B, (int32_t)D, rows);
+    const int64_t launched = fp.blocks < kMaxGrid ? fp.blocks : kMaxGrid;
+    const int64_t v[6] = {fp.F, fp.wpc, fp.cpb, B > 0 ? launched : 0,
+                          fp.threads, rows};
+    std::copy(v, v + 6, out);
+    return ok();
+  }
   if (choose_stream_plan(B, N, nvec, which == 1, &sp)) {
     const int64_t walkers = 4 / sp.W;  // four-wavefront workgroups
     const int64_t v[6] = {sp.V, sp.W, sp.grid, sp.bps, sp.groups, walkers};

@@ -316,15 +316,7 @@ __global__ __launch_bounds__(kFinishWaves * kWave) void finish_segments_kernel(
   }
 }
 
-// Launch shape of the finishing kernels for `vectors` modulation vectors
-// (samples) of D features whose largest sum has `rows` partial rows.
-struct FinishShape {
-  int F, wl, cpb, threads;
-  int32_t col_blocks;
-  int64_t total_cols, blocks;
-};
-
-static FinishShape finish_shape(int64_t vectors, int32_t D, int64_t rows) {
+FinishPlan finish_plan(int64_t vectors, int32_t D, int64_t rows) {
   // Column block width: 64 features when that gives every CU a block; else
   // 32 when that still covers half the CUs (16-feature blocks would then
   // put two workgroups on some CUs and split every 128-byte line between
@@ -333,23 +325,28 @@ static FinishShape finish_shape(int64_t vectors, int32_t D, int64_t rows) {
   // 30 partial rows 5.6 -> 4.0 us; 1 x 1536, 512 rows 5.9 -> 4.8 us;
   // 1 x 5120, 511 rows unchanged (6.5 us).
   constexpr int64_t kTargetCols = 256;
-  FinishShape sh;
-  sh.F = 64;
+  FinishPlan p;
+  p.F = 64;
   if (vectors * ((D + 63) / 64) < kTargetCols)
-    sh.F = vectors * ((D + 31) / 32) >= kTargetCols / 2 ? 32 : 16;
-  const int R = kWave / sh.F;
-  sh.wl = finish_wpc_log2(rows, R * kFinishBatch);
-  const int wpc = 1 << sh.wl;
-  sh.col_blocks = (D + sh.F - 1) / sh.F;
-  sh.total_cols = (int64_t)sh.col_blocks * vectors;
+    p.F = vectors * ((D + 31) / 32) >= kTargetCols / 2 ? 32 : 16;
+  const int R = kWave / p.F;
+  p.wpc = 1 << finish_wpc_log2(rows, R * kFinishBatch);
+  p.col_blocks = (D + p.F - 1) / p.F;
+  p.total_cols = (int64_t)p.col_blocks * vectors;
   // column blocks per workgroup: as many as keep 256 workgroups or more
-  int64_t cpb = sh.total_cols / kTargetCols;
-  if (cpb > kFinishWaves / wpc) cpb = kFinishWaves / wpc;
+  int64_t cpb = p.total_cols / kTargetCols;
+  if (cpb > kFinishWaves / p.wpc) cpb = kFinishWaves / p.wpc;
   if (cpb < 1) cpb = 1;
-  sh.cpb = (int)cpb;
-  sh.threads = wpc * sh.cpb * kWave;
-  sh.blocks = (sh.total_cols + cpb - 1) / cpb;
-  return sh;
+  p.cpb = (int)cpb;
+  p.threads = p.wpc * p.cpb * kWave;
+  p.blocks = (p.total_cols + cpb - 1) / cpb;
+  return p;
+}
+
+static int32_t log2_of(int v) {
+  int32_t l = 0;
+  while ((1 << l) < v) ++l;
+  return l;
 }
 
 hipError_t launch_finish_segments(const float *part_scale,
@@ -365,11 +362,11 @@ hipError_t launch_finish_segments(const float *part_scale,
       if (map.mod[s] == m) rows += map.wg_start[s + 1] - map.wg_start[s];
     most = rows > most ? rows : most;
   }
-  const FinishShape sh = finish_shape(nmod, D, most);
+  const FinishPlan sh = finish_plan(nmod, D, most);
   auto go = [&](auto kernel) {
     return launch_kernel_threads(kernel, sh.blocks, sh.threads, stream,
                                  part_scale, part_shift, dscale, dshift, D,
-                                 sh.col_blocks, (int32_t)sh.wl,
+                                 sh.col_blocks, log2_of(sh.wpc),
                                  (int32_t)sh.cpb, sh.total_cols, map);
   };
   return sh.F == 64 ? go(finish_segments_kernel<64>)
@@ -401,11 +398,11 @@ hipError_t launch_dmod_finish(const float *part_scale,
                               const float *part_shift, float *dscale,
                               float *dshift, int32_t B, int32_t D,
                               int32_t n_tiles, hipStream_t stream) {
-  const FinishShape sh = finish_shape(B, D, n_tiles);
+  const FinishPlan sh = finish_plan(B, D, n_tiles);
   auto go = [&](auto kernel) {
     return launch_kernel_threads(kernel, sh.blocks, sh.threads, stream,
                                  part_scale, part_shift, dscale, dshift, D,
-                                 n_tiles, sh.col_blocks, (int32_t)sh.wl,
+                                 n_tiles, sh.col_blocks, log2_of(sh.wpc),
                                  (int32_t)sh.cpb, sh.total_cols);
   };
   return sh.F == 64 ? go(dmod_finish_kernel<64>)

@@ -270,6 +270,22 @@ hipError_t launch_dmod_partial(int dtype, const DmodPlan &plan,
                                int32_t B, int32_t N, int32_t D,
                                hipStream_t stream);
 
+// Launch shape of the finishing kernels for `vectors` modulation vectors
+// (samples) of D features whose largest sum has `rows` partial rows: column
+// blocks of F features, wpc wavefronts per block, cpb blocks per workgroup
+// of `threads` threads, `blocks` workgroups (the kernel strides over more
+// than kMaxGrid).
+struct FinishPlan {
+  int F = 0;
+  int wpc = 0;
+  int cpb = 0;
+  int threads = 0;
+  int32_t col_blocks = 0;
+  int64_t total_cols = 0;
+  int64_t blocks = 0;
+};
+FinishPlan finish_plan(int64_t vectors, int32_t D, int64_t rows);
+
 // dscale/dshift = sums over n_tiles of [B, n_tiles, D] partials, in index
 // order (zero when n_tiles == 0).
 hipError_t launch_dmod_finish(const float *part_scale,

@@ -247,13 +247,21 @@ def plan(which: str, B: int, N: int, D: int, dtype: torch.dtype) -> dict:
     """How :func:`fwd` (``which="fwd"``) or :func:`bwd_fused` (``"bwd"``)
     splits a [B, N, D] batch into work (host-only): vectors per lane,
     wavefronts per row, workgroups, workgroups per sample, samples in
-    flight, row walkers per workgroup."""
-    if which not in ("fwd", "bwd"):
-        raise ValueError(f"which must be 'fwd' or 'bwd', got {which!r}")
+    flight, row walkers per workgroup.  ``which="finish"``: the launch that
+    sums the backward's partial rows: features per column block, wavefronts
+    per block, blocks per workgroup, workgroups, threads per workgroup,
+    partial rows summed per output."""
+    codes = {"fwd": 0, "bwd": 1, "finish": 2}
+    if which not in codes:
+        raise ValueError(f"which must be 'fwd', 'bwd' or 'finish', got "
+                         f"{which!r}")
     out = (ctypes.c_int64 * 6)()
-    rc = _lib.load().adaln_plan(0 if which == "fwd" else 1, B, N, D,
+    rc = _lib.load().adaln_plan(codes[which], B, N, D,
                                 _DTYPES.get(dtype, -1), out)
     _lib.check(rc, "adaln_plan")
+    if which == "finish":
+        return dict(F=out[0], wpc=out[1], cpb=out[2], workgroups=out[3],
+                    threads=out[4], rows=out[5])
     return dict(V=out[0], waves_per_row=out[1], workgroups=out[2],
                 bps=out[3], groups=out[4], walkers=out[5])
 

@@ -160,6 +160,17 @@ int adaln_bwd_fused_plan(int64_t B, int64_t N, int64_t D, int dtype,
  * wavefront (W = 1) or the W wavefronts that share a row.  Returns
  * ADALN_ERR_UNSUPPORTED where the entry point would take another path (rows
  * too wide for the fused backward).  Host-only; no HIP call.
+ *
+ * which = 2: the launch that sums the partial rows into dscale and dshift
+ * (adaln_bwd_finish, or the last launch of adaln_bwd_dmod for wider rows).
+ * Fills out[0..5] with {features per column block F (16, 32 or 64),
+ * wavefronts per block wpc, blocks per workgroup cpb, workgroups launched G,
+ * threads per workgroup, partial rows P summed per output}.  Block k covers
+ * sample k / C, features (k % C) * F + [0, F), C = ceil(D / F).  Workgroup g
+ * takes the blocks L * cpb + [0, cpb), then those of L + G, L + 2G, ...,
+ * where L = g, except for F < 64 and g < 8 * (G / 8): L = (g % 8) * (G / 8)
+ * + g / 8.  The j-th wpc wavefronts of a workgroup serve its j-th block;
+ * wavefront s of them sums the rows [s * P / wpc, (s + 1) * P / wpc).
  */
 int adaln_plan(int which, int64_t B, int64_t N, int64_t D, int dtype,
                int64_t *out);

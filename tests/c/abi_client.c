@@ -58,7 +58,9 @@ int main(void)
         CHECK(p[1] == 1 && p[2] == p[3] && p[5] == 4);
         CHECK(adaln_plan(1, 1, 75600, 5120, ADALN_BF16, p) == ADALN_OK);
         CHECK(p[1] == 2 && p[5] == 2);
-        CHECK(adaln_plan(2, 1, 75600, 5120, ADALN_BF16, p) == ADALN_ERR_INVALID);
+        CHECK(adaln_plan(2, 1, 75600, 5120, ADALN_BF16, p) == ADALN_OK);
+        CHECK(p[0] == 32 && p[5] == 511 && p[4] == p[1] * p[2] * 64);
+        CHECK(adaln_plan(3, 1, 75600, 5120, ADALN_BF16, p) == ADALN_ERR_INVALID);
     }
     /* an invalid call enqueues nothing and explains itself */
     CHECK(adaln_fwd(NULL, NULL, NULL, NULL, NULL, NULL, 1, 1, 64, 9, NULL) ==
