@@ -49,10 +49,10 @@ SIGNATURES = {
     "adaln_bwd_segments": (_INT, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                   _SZ, _VP, _VP, _I64, _I64, _I64, _INT,
                                   _VP]),
-    "adaln_stream_probe": (_INT, [_INT, _VP, _VP, _VP, _I64, _VP]),
     "adaln_bshape": (_I64, [_I64, _I64, _I64, ctypes.c_int32]),
     "adaln_bshape_real": (_I64, [_I64, _I64, ctypes.c_double,
                                  ctypes.c_double]),
+    "adaln_mcomp": (ctypes.c_double, [ctypes.c_double, _I64, _I64]),
     "adaln_costfit": (_INT, [_VP, _VP, _VP, _I64, ctypes.c_double,
                              ctypes.c_double, _VP]),
     "adaln_max_d": (_I64, [_INT]),

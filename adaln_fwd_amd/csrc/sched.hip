@@ -141,3 +141,15 @@ ADALN_API int64_t adaln_bshape_real(int64_t S, int64_t m_mem, double m_comp,
   ok();
   return b < 1 ? 1 : b;
 }
+
+ADALN_API double adaln_mcomp(double p, int64_t m_mem, int64_t s_ref) {
+  if (s_ref <= 0 || m_mem < 0 || !(p >= 0.0) || !isfinite(p)) {
+    fail(ADALN_ERR_INVALID,
+         "mcomp needs s_ref > 0, m_mem >= 0 and a finite exponent >= 0");
+    return -1.0;
+  }
+  // the memory-bound batch of the reference length, times its S^p
+  const int64_t b_mem = m_mem / s_ref;
+  ok();
+  return (double)b_mem * pow((double)s_ref, p);
+}

@@ -4,7 +4,10 @@ Argument marshalling only: shapes, dtypes, devices and contiguity are checked
 here because the C ABI cannot see torch metadata; every step of the operator
 runs in the HIP kernels of ``libadaln.so``.  Outputs that are not passed in
 are allocated with torch on the input's device; work is enqueued on the
-current torch stream of that device unless ``stream`` is given.
+current torch stream of that device unless ``stream`` is given (a
+torch.cuda.Stream or a raw hipStream_t), in which case the outputs and any
+temporary workspace are allocated on that stream, so torch's allocator does
+not hand the workspace to another stream while the kernels still use it.
 """
 
 from __future__ import annotations
@@ -55,6 +58,19 @@ def _stream(device: torch.device, stream) -> int:
     return int(stream)
 
 
+def _on(device: torch.device, stream):
+    """Context in which the outputs and the workspace of a call are
+    allocated: the stream the call's kernels run on.  torch's caching
+    allocator hands a freed block only to later allocations on the stream it
+    was allocated on, so a workspace dropped when the call returns cannot be
+    reused by another stream while the kernels still write to it."""
+    if stream is None:
+        return torch.cuda.device(device)
+    if not isinstance(stream, torch.cuda.Stream):
+        stream = torch.cuda.ExternalStream(int(stream), device=device)
+    return torch.cuda.stream(stream)
+
+
 def _shape3(x: torch.Tensor) -> Tuple[int, int, int]:
     if x.dim() != 3:
         raise ValueError(f"x must be [B, N, D], got shape {tuple(x.shape)}")
@@ -74,17 +90,17 @@ def fwd(x: torch.Tensor, scale: torch.Tensor, shift: torch.Tensor, *,
     _check(x, "x", (B, N, D), dt, dev)
     _check(scale, "scale", (B, D), dt, dev)
     _check(shift, "shift", (B, D), dt, dev)
-    if y is None:
-        y = torch.empty_like(x)
-    if mean is None:
-        mean = torch.empty(B, N, dtype=torch.float32, device=dev)
-    if rstd is None:
-        rstd = torch.empty(B, N, dtype=torch.float32, device=dev)
-    _check(y, "y", (B, N, D), dt, dev)
-    _check(mean, "mean", (B, N), torch.float32, dev)
-    _check(rstd, "rstd", (B, N), torch.float32, dev)
     lib = _lib.load()
-    with torch.cuda.device(dev):
+    with _on(dev, stream):
+        if y is None:
+            y = torch.empty_like(x)
+        if mean is None:
+            mean = torch.empty(B, N, dtype=torch.float32, device=dev)
+        if rstd is None:
+            rstd = torch.empty(B, N, dtype=torch.float32, device=dev)
+        _check(y, "y", (B, N, D), dt, dev)
+        _check(mean, "mean", (B, N), torch.float32, dev)
+        _check(rstd, "rstd", (B, N), torch.float32, dev)
         rc = lib.adaln_fwd(_ptr(x), _ptr(scale), _ptr(shift), _ptr(y),
                            _ptr(mean), _ptr(rstd), B, N, D, code,
                            _stream(dev, stream))
@@ -131,18 +147,18 @@ def bwd(dy: torch.Tensor, x: torch.Tensor, scale: torch.Tensor,
     dscale and dshift are float32 [B, D]; the workspace (bytes from
     :func:`bwd_workspace_bytes`) is allocated if not given."""
     B, N, D, dev, dt = _bwd_common(dy, x, scale, mean, rstd)
-    if dx is None:
-        dx = torch.empty_like(x)
-    if dscale is None:
-        dscale = torch.empty(B, D, dtype=torch.float32, device=dev)
-    if dshift is None:
-        dshift = torch.empty(B, D, dtype=torch.float32, device=dev)
-    _check(dx, "dx", (B, N, D), dt, dev)
-    _check(dscale, "dscale", (B, D), torch.float32, dev)
-    _check(dshift, "dshift", (B, D), torch.float32, dev)
-    workspace, wbytes = _workspace(workspace, B, N, D, dt, dev)
     lib = _lib.load()
-    with torch.cuda.device(dev):
+    with _on(dev, stream):
+        if dx is None:
+            dx = torch.empty_like(x)
+        if dscale is None:
+            dscale = torch.empty(B, D, dtype=torch.float32, device=dev)
+        if dshift is None:
+            dshift = torch.empty(B, D, dtype=torch.float32, device=dev)
+        _check(dx, "dx", (B, N, D), dt, dev)
+        _check(dscale, "dscale", (B, D), torch.float32, dev)
+        _check(dshift, "dshift", (B, D), torch.float32, dev)
+        workspace, wbytes = _workspace(workspace, B, N, D, dt, dev)
         rc = lib.adaln_bwd(_ptr(dy), _ptr(x), _ptr(scale), _ptr(mean),
                            _ptr(rstd), _ptr(dx), _ptr(dscale), _ptr(dshift),
                            _ptr(workspace), wbytes, B, N, D, _code(x),
@@ -157,12 +173,12 @@ def bwd_fused(dy, x, scale, mean, rstd, *, dx=None, workspace=None,
     the workspace.  Returns (dx, workspace); pass the workspace to
     :func:`bwd_finish`."""
     B, N, D, dev, dt = _bwd_common(dy, x, scale, mean, rstd)
-    if dx is None:
-        dx = torch.empty_like(x)
-    _check(dx, "dx", (B, N, D), dt, dev)
-    workspace, wbytes = _workspace(workspace, B, N, D, dt, dev)
     lib = _lib.load()
-    with torch.cuda.device(dev):
+    with _on(dev, stream):
+        if dx is None:
+            dx = torch.empty_like(x)
+        _check(dx, "dx", (B, N, D), dt, dev)
+        workspace, wbytes = _workspace(workspace, B, N, D, dt, dev)
         rc = lib.adaln_bwd_fused(_ptr(dy), _ptr(x), _ptr(scale), _ptr(mean),
                                  _ptr(rstd), _ptr(dx), _ptr(workspace),
                                  wbytes, B, N, D, _code(x),
@@ -176,19 +192,19 @@ def bwd_finish(workspace, B: int, N: int, D: int, dtype: torch.dtype, *,
     """Second launch of :func:`bwd`: dscale, dshift from the partial sums
     that :func:`bwd_fused` left in ``workspace``."""
     dev = workspace.device
-    if dscale is None:
-        dscale = torch.empty(B, D, dtype=torch.float32, device=dev)
-    if dshift is None:
-        dshift = torch.empty(B, D, dtype=torch.float32, device=dev)
-    _check(dscale, "dscale", (B, D), torch.float32, dev)
-    _check(dshift, "dshift", (B, D), torch.float32, dev)
     if not workspace.is_contiguous():
         raise ValueError("workspace must be contiguous")
     code = _DTYPES.get(dtype)
     if code is None:
         raise TypeError(f"unsupported dtype {dtype}")
     lib = _lib.load()
-    with torch.cuda.device(dev):
+    with _on(dev, stream):
+        if dscale is None:
+            dscale = torch.empty(B, D, dtype=torch.float32, device=dev)
+        if dshift is None:
+            dshift = torch.empty(B, D, dtype=torch.float32, device=dev)
+        _check(dscale, "dscale", (B, D), torch.float32, dev)
+        _check(dshift, "dshift", (B, D), torch.float32, dev)
         rc = lib.adaln_bwd_finish(_ptr(workspace),
                                   workspace.numel() * workspace.element_size(),
                                   _ptr(dscale), _ptr(dshift), B, N, D, code,
@@ -200,11 +216,11 @@ def bwd_finish(workspace, B: int, N: int, D: int, dtype: torch.dtype, *,
 def bwd_dx(dy, x, scale, mean, rstd, *, dx=None, stream=None):
     """Input gradient only (one launch); returns dx."""
     B, N, D, dev, dt = _bwd_common(dy, x, scale, mean, rstd)
-    if dx is None:
-        dx = torch.empty_like(x)
-    _check(dx, "dx", (B, N, D), dt, dev)
     lib = _lib.load()
-    with torch.cuda.device(dev):
+    with _on(dev, stream):
+        if dx is None:
+            dx = torch.empty_like(x)
+        _check(dx, "dx", (B, N, D), dt, dev)
         rc = lib.adaln_bwd_dx(_ptr(dy), _ptr(x), _ptr(scale), _ptr(mean),
                               _ptr(rstd), _ptr(dx), B, N, D, _code(x),
                               _stream(dev, stream))
@@ -216,15 +232,15 @@ def bwd_dmod(dy, x, mean, rstd, *, dscale=None, dshift=None, workspace=None,
              stream=None):
     """Modulation gradients only (D-tile reduction); returns (dscale, dshift)."""
     B, N, D, dev, dt = _bwd_common(dy, x, None, mean, rstd)
-    if dscale is None:
-        dscale = torch.empty(B, D, dtype=torch.float32, device=dev)
-    if dshift is None:
-        dshift = torch.empty(B, D, dtype=torch.float32, device=dev)
-    _check(dscale, "dscale", (B, D), torch.float32, dev)
-    _check(dshift, "dshift", (B, D), torch.float32, dev)
-    workspace, wbytes = _workspace(workspace, B, N, D, dt, dev)
     lib = _lib.load()
-    with torch.cuda.device(dev):
+    with _on(dev, stream):
+        if dscale is None:
+            dscale = torch.empty(B, D, dtype=torch.float32, device=dev)
+        if dshift is None:
+            dshift = torch.empty(B, D, dtype=torch.float32, device=dev)
+        _check(dscale, "dscale", (B, D), torch.float32, dev)
+        _check(dshift, "dshift", (B, D), torch.float32, dev)
+        workspace, wbytes = _workspace(workspace, B, N, D, dt, dev)
         rc = lib.adaln_bwd_dmod(_ptr(dy), _ptr(x), _ptr(mean), _ptr(rstd),
                                 _ptr(dscale), _ptr(dshift), _ptr(workspace),
                                 wbytes, B, N, D, _code(x),
@@ -332,17 +348,17 @@ def fwd_segments(x: torch.Tensor, scale: torch.Tensor, shift: torch.Tensor,
     _check(x, "x", (T, D), dt, dev)
     _check(scale, "scale", (nmod, D), dt, dev)
     _check(shift, "shift", (nmod, D), dt, dev)
-    if y is None:
-        y = torch.empty_like(x)
-    if mean is None:
-        mean = torch.empty(T, dtype=torch.float32, device=dev)
-    if rstd is None:
-        rstd = torch.empty(T, dtype=torch.float32, device=dev)
-    _check(y, "y", (T, D), dt, dev)
-    _check(mean, "mean", (T,), torch.float32, dev)
-    _check(rstd, "rstd", (T,), torch.float32, dev)
     lib = _lib.load()
-    with torch.cuda.device(dev):
+    with _on(dev, stream):
+        if y is None:
+            y = torch.empty_like(x)
+        if mean is None:
+            mean = torch.empty(T, dtype=torch.float32, device=dev)
+        if rstd is None:
+            rstd = torch.empty(T, dtype=torch.float32, device=dev)
+        _check(y, "y", (T, D), dt, dev)
+        _check(mean, "mean", (T,), torch.float32, dev)
+        _check(rstd, "rstd", (T,), torch.float32, dev)
         rc = lib.adaln_fwd_segments(_ptr(x), _ptr(scale), _ptr(shift),
                                     _ptr(y), _ptr(mean), _ptr(rstd),
                                     tab.offsets_ptr, tab.mod_ptr, tab.nseg,
@@ -371,24 +387,26 @@ def bwd_segments(dy, x, scale, mean, rstd, seg_offsets, seg_mod=None, *,
     _check(scale, "scale", (nmod, D), dt, dev)
     _check(mean, "mean", (T,), torch.float32, dev)
     _check(rstd, "rstd", (T,), torch.float32, dev)
-    if dx is None:
-        dx = torch.empty_like(x)
-    if dscale is None:
-        dscale = torch.empty(nmod, D, dtype=torch.float32, device=dev)
-    if dshift is None:
-        dshift = torch.empty(nmod, D, dtype=torch.float32, device=dev)
-    _check(dx, "dx", (T, D), dt, dev)
-    _check(dscale, "dscale", (nmod, D), torch.float32, dev)
-    _check(dshift, "dshift", (nmod, D), torch.float32, dev)
     lib = _lib.load()
     need = int(lib.adaln_bwd_segments_workspace_bytes(tab.offsets_ptr,
                                                       tab.nseg, D, code))
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-    if workspace.device != dev or not workspace.is_contiguous():
-        raise ValueError(f"workspace must be a contiguous tensor on {dev}")
-    wbytes = workspace.numel() * workspace.element_size()
-    with torch.cuda.device(dev):
+    with _on(dev, stream):
+        if dx is None:
+            dx = torch.empty_like(x)
+        if dscale is None:
+            dscale = torch.empty(nmod, D, dtype=torch.float32, device=dev)
+        if dshift is None:
+            dshift = torch.empty(nmod, D, dtype=torch.float32, device=dev)
+        _check(dx, "dx", (T, D), dt, dev)
+        _check(dscale, "dscale", (nmod, D), torch.float32, dev)
+        _check(dshift, "dshift", (nmod, D), torch.float32, dev)
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8,
+                                    device=dev)
+        if workspace.device != dev or not workspace.is_contiguous():
+            raise ValueError(f"workspace must be a contiguous tensor on "
+                             f"{dev}")
+        wbytes = workspace.numel() * workspace.element_size()
         rc = lib.adaln_bwd_segments(_ptr(dy), _ptr(x), _ptr(scale),
                                     _ptr(mean), _ptr(rstd), _ptr(dx),
                                     _ptr(dscale), _ptr(dshift),
@@ -397,26 +415,6 @@ def bwd_segments(dy, x, scale, mean, rstd, seg_offsets, seg_mod=None, *,
                                     _stream(dev, stream))
     _lib.check(rc, "adaln_bwd_segments")
     return dx, dscale, dshift
-
-
-def stream_probe(kind: int, a: torch.Tensor, dst: torch.Tensor,
-                 b: Optional[torch.Tensor] = None, stream=None) -> None:
-    """Diagnostic streaming probe: kind 0 copies a into dst, kind 1 writes
-    a XOR b into dst (byte buffers of equal size, a multiple of 10240)."""
-    for t, name in ((a, "a"), (dst, "dst"), (b, "b")):
-        if t is None:
-            continue
-        if t.device.type != "cuda" or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous GPU tensor")
-    n = a.numel() * a.element_size()
-    if dst.numel() * dst.element_size() != n or (
-            b is not None and b.numel() * b.element_size() != n):
-        raise ValueError("probe buffers must have the same size")
-    with torch.cuda.device(a.device):
-        rc = _lib.load().adaln_stream_probe(int(kind), _ptr(a), _ptr(b),
-                                            _ptr(dst), n,
-                                            _stream(a.device, stream))
-    _lib.check(rc, "adaln_stream_probe")
 
 
 def bshape(S: int, m_mem: int, m_comp: int, p: int) -> int:

@@ -3,9 +3,10 @@ summary, section 2.A): shape benchmarking of a synthetic training step, the
 step-time cost model t = a + b * B * S^p, the compute bound it implies, and
 the resulting bucket batch sizes.
 
-The arithmetic (the least-squares fit and the bucket rule) runs in
-``libadaln.so`` (``adaln_costfit``, ``adaln_bshape_real``); this module
-marshals arrays and times the synthetic step.
+The arithmetic (the least-squares fit, the compute bound it implies and the
+bucket rule) runs in ``libadaln.so`` (``adaln_costfit``, ``adaln_mcomp``,
+``adaln_bshape_real``); this module marshals arrays and times the synthetic
+step.
 
 The synthetic step of a [B, S, D] bucket is the AdaLN forward (this
 library), self-attention over the normalised tokens, forward and backward
@@ -70,10 +71,12 @@ def bshape_real(S: int, m_mem: int, m_comp: float, p: float) -> int:
 
 def m_comp_for(p: float, m_mem: int, s_ref: int) -> float:
     """The compute bound that caps every bucket at the predicted cost of the
-    memory-bound bucket of length s_ref: B_mem(s_ref) * s_ref^p.  (Under
-    t = a + b * B * S^p, B * S^p <= M_comp is a bound on the predicted step
-    time.)"""
-    return (m_mem // s_ref) * float(s_ref) ** p
+    memory-bound bucket of length s_ref (``adaln_mcomp`` in the library)."""
+    lib = _lib.load()
+    v = float(lib.adaln_mcomp(float(p), int(m_mem), int(s_ref)))
+    if v < 0:
+        _lib.check(_lib.ERR_INVALID, "adaln_mcomp")
+    return v
 
 
 def buckets(lengths: Iterable[int], m_mem: int, m_comp: float,
@@ -168,6 +171,10 @@ class SyntheticStep:
             step()
             ev[i + 1].record()
         torch.cuda.synchronize(dev)
+        # the last step's AdaLN inputs and outputs, for callers that check
+        # them against the operator called on its own
+        self.last = dict(x=x, dy=dy, scale=scale, shift=shift, y=y, dx=dx,
+                         mean=mean, rstd=rstd, dscale=dscale, dshift=dshift)
         return [ev[i].elapsed_time(ev[i + 1]) for i in range(iters)]
 
 

@@ -77,6 +77,66 @@ KERNEL_SYMBOLS = {
 }
 
 
+# The streaming probes (bench_probe.hip): the operator's access pattern with
+# no arithmetic, built beside this script, not part of the library.
+PROBE_SRC = os.path.join(ROOT, "bench_probe.hip")
+PROBE_LIB = os.path.join(ROOT, "bench_probe.so")
+_probe_lib = None
+
+
+def build_probe(verbose: bool = False) -> str:
+    """Compile bench_probe.hip into bench_probe.so for gfx950."""
+    import subprocess
+    from adaln_fwd_amd import build as hip_build
+    tmp = PROBE_LIB + ".tmp"
+    cmd = [hip_build.hipcc(), *hip_build.FLAGS, "-shared", PROBE_SRC, "-o",
+           tmp]
+    if verbose:
+        print(" ".join(cmd), file=sys.stderr)
+    res = subprocess.run(cmd, stdout=subprocess.PIPE,
+                         stderr=subprocess.STDOUT, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{res.stdout}")
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
+
+
+def probe_lib():
+    """ctypes handle of bench_probe.so (raises if it is not built)."""
+    global _probe_lib
+    if _probe_lib is None:
+        import ctypes
+        if not os.path.exists(PROBE_LIB):
+            raise ImportError(f"{PROBE_LIB} is not built; run "
+                              "__graft_entry__.build() first")
+        lib = ctypes.CDLL(PROBE_LIB)
+        vp = ctypes.c_void_p
+        lib.bench_stream_probe.argtypes = [ctypes.c_int, vp, vp, vp,
+                                           ctypes.c_int64, vp]
+        lib.bench_stream_probe.restype = ctypes.c_int
+        _probe_lib = lib
+    return _probe_lib
+
+
+def run_probe(kind: int, a, dst, b=None, stream=None) -> None:
+    """Enqueue a streaming probe on byte tensors of equal size (a multiple
+    of 10240): kind 0 copies a into dst, kind 1 writes a XOR b."""
+    import torch
+    n = a.numel() * a.element_size()
+    for t in (a, dst, b):
+        if t is not None and (t.device.type != "cuda" or
+                              not t.is_contiguous() or
+                              t.numel() * t.element_size() != n):
+            raise ValueError("probe buffers: contiguous GPU tensors of one "
+                             "size")
+    s = (stream or torch.cuda.current_stream(a.device)).cuda_stream
+    rc = probe_lib().bench_stream_probe(int(kind), a.data_ptr(),
+                                        None if b is None else b.data_ptr(),
+                                        dst.data_ptr(), n, s)
+    if rc != 0:
+        raise ValueError(f"bench_stream_probe: code {rc}")
+
+
 def kernel_source_hash(kernel: str = None) -> str:
     """Hash of the sources of one step component (all of them if None)."""
     h = hashlib.sha256()
@@ -554,8 +614,8 @@ def eager_reference(args) -> int:
 
 
 def stream_probe(args) -> int:
-    """The library's streaming probes on buffers of the workload's activation
-    size; prints one JSON line."""
+    """The streaming probes (bench_probe.hip) on buffers of the workload's
+    activation size; prints one JSON line."""
     import torch
     import adaln_fwd_amd as A
     import synth
@@ -572,16 +632,16 @@ def stream_probe(args) -> int:
     a = torch.empty(n, dtype=torch.uint8, device="cuda").random_()
     b = torch.empty_like(a).random_()
     d = torch.empty_like(a)
-    out = {"probe": "adaln_stream_probe", "workload": wl.name,
+    out = {"probe": "bench_stream_probe", "workload": wl.name,
            "buffer_bytes": n}
     for kind, name, streams in ((0, "copy", 2), (1, "read2_write1", 3)):
         for _ in range(args.warmup or 1):
-            A.stream_probe(kind, a, d, b=b)
+            run_probe(kind, a, d, b=b)
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         torch.cuda.synchronize()
         ev[0].record()
         for _ in range(args.steps):
-            A.stream_probe(kind, a, d, b=b)
+            run_probe(kind, a, d, b=b)
         ev[1].record()
         torch.cuda.synchronize()
         ms = ev[0].elapsed_time(ev[1]) / args.steps
@@ -619,9 +679,9 @@ def main(argv=None) -> int:
                          "modulation, autograd backward) beside this library "
                          "on the workload")
     ap.add_argument("--probe", action="store_true",
-                    help="time the library's streaming probes (copy; 2 reads "
-                         "+ 1 write) on buffers of the workload's activation "
-                         "size")
+                    help="time the streaming probes of bench_probe.hip (copy; "
+                         "2 reads + 1 write) on buffers of the workload's "
+                         "activation size")
     ap.add_argument("--copy-probe", action="store_true",
                     help="time torch's device copy of one workload-sized "
                          "tensor instead (achievable-bandwidth reference and "
@@ -839,17 +899,17 @@ def main(argv=None) -> int:
             b = job["dy"].view(-1).view(torch.uint8)[:n]
             d = job["y"].view(-1).view(torch.uint8)[:n]
             for _ in range(3):
-                A.stream_probe(1, a, d, b=b, stream=stream)
+                run_probe(1, a, d, b=b, stream=stream)
             pev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
             pev[0].record(stream)
             reps = 10
             for _ in range(reps):
-                A.stream_probe(1, a, d, b=b, stream=stream)
+                run_probe(1, a, d, b=b, stream=stream)
             pev[1].record(stream)
             torch.cuda.synchronize()
             pms = pev[0].elapsed_time(pev[1]) / reps
             probe = {"pattern": "2 reads + 1 write, nontemporal, no "
-                                "arithmetic (adaln_stream_probe kind 1)",
+                                "arithmetic (bench_probe.hip, kind 1)",
                      "bytes": 3 * n, "avg_ms": round(pms, 5),
                      "gbps": round(3 * n / (pms * 1e-3) / 1e9, 1)}
     step_bytes = sum(tot_bytes.values())

@@ -1,0 +1,74 @@
+// Streaming-bandwidth probes for the benchmark (bench.py), built into
+// bench_probe.so beside it; not part of the operator's library.  They run
+// the access pattern of the operator's row-stream kernels with no
+// arithmetic, to measure what HBM sustains for it on the same buffers:
+//
+//   kind 0: copy          dst = a           (one read stream, one write)
+//   kind 1: read2 write1  dst = a ^ b       (the fused backward's pattern)
+//
+// Organisation of the row-stream kernels: 256 workgroups of four
+// wavefronts, one 10 KiB row per wavefront per step, grid-stride over the
+// rows, nontemporal 16-byte loads and stores, every lane one vector per
+// instruction.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+constexpr int kWave = 64;
+constexpr int kProbeV = 10;  // vectors per lane per row: rows of 10 KiB
+constexpr int64_t kRow = (int64_t)kProbeV * kWave * 16;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <int KIND>
+__global__ __launch_bounds__(256) void probe_kernel(
+    const u32x4 *__restrict__ a, const u32x4 *__restrict__ b,
+    u32x4 *__restrict__ dst, int64_t rows) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  for (int64_t r = (int64_t)blockIdx.x * 4 + wave; r < rows;
+       r += (int64_t)gridDim.x * 4) {
+    const int64_t base = r * kProbeV * kWave + lane;
+    u32x4 va[kProbeV], vb[kProbeV];
+#pragma unroll
+    for (int k = 0; k < kProbeV; ++k) {
+      va[k] = __builtin_nontemporal_load(a + base + k * kWave);
+      if (KIND == 1) vb[k] = __builtin_nontemporal_load(b + base + k * kWave);
+    }
+#pragma unroll
+    for (int k = 0; k < kProbeV; ++k) {
+      u32x4 o = va[k];
+      if (KIND == 1) o ^= vb[k];
+      __builtin_nontemporal_store(o, dst + base + k * kWave);
+    }
+  }
+}
+
+}  // namespace
+
+// Returns 0, -1 for invalid arguments (kind not 0 or 1, a NULL or
+// misaligned buffer, bytes not a multiple of 10240), or -5 when the launch
+// fails.  a, b, dst: device buffers of `bytes` bytes, 16-byte aligned, not
+// overlapping (b unused for kind 0).  Enqueued on `stream`, not waited for.
+extern "C" __attribute__((visibility("default"))) int bench_stream_probe(
+    int kind, const void *a, const void *b, void *dst, int64_t bytes,
+    void *stream) {
+  if ((kind != 0 && kind != 1) || bytes < 0 || bytes % kRow != 0) return -1;
+  if (bytes == 0) return 0;
+  if (a == nullptr || dst == nullptr || (kind == 1 && b == nullptr))
+    return -1;
+  if ((reinterpret_cast<uintptr_t>(a) | reinterpret_cast<uintptr_t>(dst) |
+       reinterpret_cast<uintptr_t>(b)) % 16 != 0)
+    return -1;
+  int64_t rows = bytes / kRow;
+  const u32x4 *pa = static_cast<const u32x4 *>(a);
+  const u32x4 *pb = static_cast<const u32x4 *>(b);
+  u32x4 *pd = static_cast<u32x4 *>(dst);
+  void *args[] = {&pa, &pb, &pd, &rows};
+  const void *k = kind == 0 ? (const void *)probe_kernel<0>
+                            : (const void *)probe_kernel<1>;
+  const hipError_t e = hipLaunchKernel(k, dim3(256), dim3(256), args, 0,
+                                       (hipStream_t)stream);
+  return e == hipSuccess ? 0 : -5;
+}

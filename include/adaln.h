@@ -55,9 +55,10 @@
 extern "C" {
 #endif
 
-#define ADALN_F32 0
-#define ADALN_BF16 1
+/* Element types of x, y, dy, dx, scale and shift (the `dtype` argument). */
+typedef enum adaln_dtype { ADALN_F32 = 0, ADALN_BF16 = 1 } adaln_dtype_t;
 
+/* Return codes.  Each has a short alias (ADALN_EINVAL, ...). */
 #define ADALN_OK 0
 #define ADALN_ERR_INVALID (-1)     /* NULL pointer, bad size or exponent */
 #define ADALN_ERR_DTYPE (-2)       /* unknown dtype code */
@@ -66,6 +67,12 @@ extern "C" {
 #define ADALN_ERR_WORKSPACE (-4)   /* workspace NULL or too small */
 #define ADALN_ERR_HIP (-5)         /* the HIP runtime reported an error */
 #define ADALN_ERR_UNSUPPORTED (-6) /* D too wide for the entry point */
+#define ADALN_EINVAL ADALN_ERR_INVALID
+#define ADALN_EDTYPE ADALN_ERR_DTYPE
+#define ADALN_EALIGN ADALN_ERR_ALIGN
+#define ADALN_EWORKSPACE ADALN_ERR_WORKSPACE
+#define ADALN_EHIP ADALN_ERR_HIP
+#define ADALN_EUNSUPPORTED ADALN_ERR_UNSUPPORTED
 
 /*
  * Forward pass: mean, rstd and y for every token row, one kernel launch.
@@ -93,7 +100,12 @@ int adaln_fwd(const void *x, const void *scale, const void *shift, void *y,
 size_t adaln_bwd_workspace_bytes(int64_t B, int64_t N, int64_t D, int dtype);
 
 /*
- * Backward pass: dx, dscale and dshift.  For rows of at most 1280 vectors
+ * Backward pass: dx, dscale and dshift.  Section 2.B, backward pass: the
+ * gradients of the modulation parameters are sums along the sequence
+ * dimension N, taken over a (d_tile, n_tile) grid with every lane pinned to
+ * its features so that each access is contiguous along D, then combined
+ * across the n_tiles; dx, on which the pages are silent, is the exact
+ * gradient of the forward formula above.  For rows of at most 1280 vectors
  * (D <= 10240 bf16 / 5120 f32) it enqueues adaln_bwd_fused then
  * adaln_bwd_finish (x and dy read once); for wider rows, adaln_bwd_dx then
  * adaln_bwd_dmod.
@@ -235,19 +247,6 @@ int adaln_bwd_segments(const void *dy, const void *x, const void *scale,
                        int64_t D, int dtype, void *stream);
 
 /*
- * Streaming-bandwidth probe (diagnostic): the access pattern of the
- * row-stream kernels without their arithmetic, to measure what HBM sustains
- * for it.  kind 0 copies a to dst; kind 1 writes dst = a XOR b (two read
- * streams and one write stream, the fused backward's pattern).  a, b, dst:
- * device buffers of `bytes` bytes, 16-byte aligned, not overlapping (b is
- * unused for kind 0); bytes a multiple of 10240 (one 10 KiB row per
- * wavefront per step).  Returns ADALN_ERR_INVALID / ADALN_ERR_ALIGN for
- * other arguments.
- */
-int adaln_stream_probe(int kind, const void *a, const void *b, void *dst,
-                       int64_t bytes, void *stream);
-
-/*
  * Dual-constraint bucket batch size of section 2.A:
  *     max(1, min(floor(m_mem / S), floor(m_comp / S^p)))
  * in exact integer arithmetic.  When S^p exceeds the int64 range the compute
@@ -264,6 +263,19 @@ int64_t adaln_bshape(int64_t S, int64_t m_mem, int64_t m_comp, int32_t p);
  * exponent.  Host-only.
  */
 int64_t adaln_bshape_real(int64_t S, int64_t m_mem, double m_comp, double p);
+
+/*
+ * Compute bound implied by a fitted exponent (section 2.A, cost-fitting
+ * system; how M_comp follows from the fit is not stated there, so it is read
+ * as the B * S^p of the memory-bound bucket of a reference length s_ref,
+ * which no bucket's predicted cost a + b * B * S^p then exceeds):
+ *     (m_mem / s_ref) * s_ref^p      (integer quotient, then a double)
+ * With the pages' own p = 2, M_mem = 131072 and s_ref = 16380 this gives
+ * 8 * 16380^2 = 2.146e9, the 2.2e9 they quote to two digits.  Returns -1.0
+ * (and records ADALN_ERR_INVALID) for s_ref <= 0, m_mem < 0 or an exponent
+ * that is negative or not finite.  Host-only.
+ */
+double adaln_mcomp(double p, int64_t m_mem, int64_t s_ref);
 
 /*
  * Step-time cost model of section 2.A: fits t ~ a + b * B * S^p to n >= 3

@@ -50,6 +50,9 @@ def _load():
     lib.oracle_num_threads.restype = ctypes.c_int
     lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
     lib.oracle_set_num_threads.restype = None
+    lib.check_rows.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, i64, i64,
+                               i64, i64, vp, vp, vp, vp, vp, f64, vp]
+    lib.check_rows.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -166,3 +169,63 @@ def num_threads() -> int:
 
 def set_num_threads(n: int) -> None:
     _load().oracle_set_num_threads(int(n))
+
+
+class CheckStat(ctypes.Structure):
+    """Running comparison of one output (``check_rows.c``)."""
+    _fields_ = [("n", ctypes.c_int64), ("nonfinite", ctypes.c_int64),
+                ("over_atol", ctypes.c_int64), ("max_err", ctypes.c_double),
+                ("max_ratio", ctypes.c_double),
+                ("max_excess", ctypes.c_double),
+                ("max_above", ctypes.c_double),
+                ("sum_sq_err", ctypes.c_double),
+                ("sum_sq_ref", ctypes.c_double)]
+
+
+def check_rows(x, dy, scale, shift, *, y=None, dx=None, mean=None,
+               rstd=None, N: int = 1, row_mod=None, row0: int = 0,
+               nrows: Optional[int] = None, tol=(0.0, 0.0, 0.0, 0.0),
+               eps: float = 1e-6):
+    """Compare device outputs (host copies) with the oracle, row by row.
+
+    x, dy: [T, D] (or [B, N, D]) CPU tensors in float32 or bfloat16;
+    scale, shift: [nmod, D] in the same dtype; y, dx: outputs of x's shape
+    and dtype; mean, rstd: float32 [T].  Row r uses modulation vector
+    row_mod[r] (int64 [T]) or, if row_mod is None, r // N.  tol =
+    (atol, rtol, rel, rtol_stat), see ``check_rows.c``.  Returns a dict of
+    CheckStat for "y", "dx", "mean" and "rstd" (n == 0 where not given)."""
+    import torch
+
+    def raw(t, dtype=None):
+        if t is None:
+            return None
+        assert t.device.type == "cpu" and t.is_contiguous()
+        if dtype is not None:
+            assert t.dtype == dtype, (t.dtype, dtype)
+        return t
+
+    codes = {torch.float32: 0, torch.bfloat16: 1}
+    dt = x.dtype
+    code = codes[dt]
+    D = x.shape[-1]
+    T = x.numel() // D
+    tensors = [raw(x, dt), raw(dy, dt), raw(scale, dt), raw(shift, dt),
+               raw(y, dt), raw(dx, dt), raw(mean, torch.float32),
+               raw(rstd, torch.float32)]
+    ptrs = [None if t is None else t.data_ptr() for t in tensors]
+    mods = None
+    if row_mod is not None:
+        mods = np.ascontiguousarray(np.asarray(row_mod, dtype=np.int64))
+        assert mods.shape == (T,)
+    n = T - row0 if nrows is None else nrows
+    assert 0 <= row0 and row0 + n <= T
+    tolv = (ctypes.c_double * 4)(*[float(v) for v in tol])
+    out = (CheckStat * 4)()
+    rc = _load().check_rows(code, ptrs[0], ptrs[1], ptrs[2], ptrs[3],
+                            _ptr(mods), int(N), int(D), int(row0), int(n),
+                            ptrs[4], ptrs[5], ptrs[6], ptrs[7],
+                            ctypes.cast(tolv, ctypes.c_void_p), float(eps),
+                            ctypes.cast(out, ctypes.c_void_p))
+    if rc != 0:
+        raise MemoryError("check_rows: out of host memory")
+    return dict(zip(("y", "dx", "mean", "rstd"), out))

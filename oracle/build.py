@@ -1,4 +1,6 @@
-"""Compile the oracle's C source into ``oracle/liboracle.so`` (gcc, OpenMP).
+"""Compile the oracle's C sources into ``oracle/liboracle.so`` (gcc, OpenMP):
+the oracle itself (``adaln_oracle.c``) and the row-by-row comparison the
+parity tests use (``check_rows.c``, which calls the oracle).
 
 Test infrastructure only; see ``adaln_oracle.c``."""
 
@@ -9,7 +11,8 @@ import subprocess
 import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-SRC = os.path.join(HERE, "adaln_oracle.c")
+SRCS = [os.path.join(HERE, "adaln_oracle.c"),
+        os.path.join(HERE, "check_rows.c")]
 LIB = os.path.join(HERE, "liboracle.so")
 
 
@@ -17,7 +20,7 @@ def build(verbose: bool = False) -> str:
     """Build the oracle library and return its path (always recompiles)."""
     tmp = LIB + ".tmp"
     cmd = ["gcc", "-O2", "-std=c99", "-fopenmp", "-fPIC", "-shared",
-           "-Wall", "-Wextra", SRC, "-o", tmp, "-lm"]
+           "-Wall", "-Wextra", *SRCS, "-o", tmp, "-lm"]
     if verbose:
         print(" ".join(cmd), file=sys.stderr)
     subprocess.run(cmd, check=True)

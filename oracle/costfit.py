@@ -82,3 +82,13 @@ def bshape_real(S: int, m_mem: int, m_comp: float, p: float) -> int:
         return -1
     q = math.floor(m_comp / math.pow(float(S), p))
     return max(1, min(m_mem // S, q))
+
+
+def m_comp(p: float, m_mem: int, s_ref: int) -> float:
+    """Compute bound implied by an exponent p: the B * S^p of the
+    memory-bound bucket of the reference length s_ref (the reading of how
+    section 2.A's M_comp follows from the fit), floor(m_mem / s_ref) *
+    s_ref^p; -1.0 for invalid arguments."""
+    if s_ref <= 0 or m_mem < 0 or not (p >= 0) or not math.isfinite(p):
+        return -1.0
+    return float(m_mem // s_ref) * math.pow(float(s_ref), p)

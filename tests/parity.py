@@ -181,6 +181,73 @@ def compare_full(inp, out, dtype: str, with_rows: bool = True):
     return reps
 
 
+def _tol(dtype: str):
+    """(atol, rtol, rel, rtol_stat) of the row checker for y and dx."""
+    if dtype == "f32":
+        return (0.0, F32_RTOL, F32_RTOL, STAT_RTOL)
+    return (BF16_ATOL, BF16_RTOL, STRICT_RTOL, STAT_RTOL)
+
+
+def _grade_stat(name: str, st, dtype: str) -> Sequence[Report]:
+    """Reports of one output of the row checker under the rules above.
+
+    The bounds with a whole-tensor rms floor are decided from running
+    quantities: an element fails ``err <= rel*|r| + f*rms`` (bf16 strict)
+    exactly when ``max(err - rel*|r|) > f*rms``, and fails ``err <= rtol *
+    max(|r|, rms)`` (float32) exactly when some element with err > rtol*|r|
+    has err > rtol*rms.  Their worst/allowed figure is that maximum over the
+    floor."""
+    assert st.n > 0, f"{name}: nothing compared"
+    assert st.nonfinite == 0, f"{name}: {st.nonfinite} non-finite GPU values"
+    rms = float(np.sqrt(st.sum_sq_ref / st.n))
+    if dtype == "f32":
+        ratio = st.max_above / (F32_RTOL * rms) if st.max_above > 0 else 0.0
+        rep = Report(name, st.max_err, ratio, 0, st.n)
+        assert ratio <= 1.0, f"parity failure: {rep}"
+        return [rep]
+    a = Report(name + "[contract]", st.max_err, st.max_ratio, st.over_atol,
+               st.n)
+    assert a.max_ratio <= 1.0, f"parity failure: {a}"
+    if st.sum_sq_ref > 0:
+        a.normwise = float(np.sqrt(st.sum_sq_err / st.sum_sq_ref))
+        assert a.normwise <= NORMWISE_MAX, f"parity failure: {a}"
+    floor = STRICT_RMS * rms + 1e-30
+    b = Report(name + "[strict]", st.max_err, max(st.max_excess, 0.0) / floor,
+               0, st.n)
+    assert b.max_ratio <= 1.0, f"parity failure: {b}"
+    return [a, b]
+
+
+def check_all_rows(x, dy, scale, shift, got, dtype: str, N: int = 1,
+                   row_mod=None) -> Sequence[Report]:
+    """Every token row of y, dx, mean and rstd (host copies in ``got``)
+    against the oracle, through the oracle library's row checker; x, dy are
+    [T, D] or [B, N, D] host tensors, row r modulated by vector row_mod[r]
+    or r // N."""
+    import oracle
+    st = oracle.check_rows(x, dy, scale, shift, y=got["y"], dx=got["dx"],
+                           mean=got["mean"], rstd=got["rstd"], N=N,
+                           row_mod=row_mod, tol=_tol(dtype))
+    reps = []
+    reps += _grade_stat("y", st["y"], dtype)
+    reps += _grade_stat("dx", st["dx"], dtype)
+    for k in ("mean", "rstd"):
+        s = st[k]
+        assert s.nonfinite == 0, f"{k}: non-finite GPU values"
+        rep = Report(k, s.max_err, s.max_ratio, 0, s.n)
+        assert rep.max_ratio <= 1.0, f"parity failure: {rep}"
+        reps.append(rep)
+    return reps
+
+
+def compare_all_rows(inp, out, dtype: str) -> Sequence[Report]:
+    """Every row of a batched result (host copies) against the oracle."""
+    B, N, D = inp.x.shape
+    got = {k: out[k].contiguous() for k in ("y", "dx", "mean", "rstd")}
+    return check_all_rows(inp.x, inp.dy, inp.scale, inp.shift, got, dtype,
+                          N=N)
+
+
 def sample_rows(total: int, k: int, seed: int = 0) -> np.ndarray:
     """k distinct rows: the first and last 8 plus a seeded random draw."""
     g = np.random.default_rng(seed)

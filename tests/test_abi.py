@@ -207,17 +207,6 @@ def test_segments_workspace_bytes(lib):
     assert ws(None, 0, 64, 1) == 0           # no segments: no partials
 
 
-def test_stream_probe_validation(lib):
-    _no_gpu()
-    p = 0x1000
-    f = lib.adaln_stream_probe
-    assert f(2, p, p, p, 10240, None) == _lib.ERR_INVALID
-    assert f(0, p, None, p, 10000, None) == _lib.ERR_ALIGN
-    assert f(1, p, None, p, 10240, None) == _lib.ERR_INVALID
-    assert f(0, p + 4, None, p, 10240, None) == _lib.ERR_ALIGN
-    assert f(0, None, None, None, 0, None) == _lib.OK
-
-
 def test_max_d(lib):
     assert lib.adaln_max_d(1) == 32768
     assert lib.adaln_max_d(0) == 16384

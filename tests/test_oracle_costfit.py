@@ -109,3 +109,42 @@ def test_bshape_real_brute_force_and_integer_rule(oracle_mod):
             for S in (1560, 8190, 16380, 32760)] == [84, 16, 8, 2]
     # 32760^1.9 = 3.80e8, so the compute bound is 5 and memory (4) binds
     assert C.bshape_real(32760, 131072, 2.2e9, 1.9) == 4
+
+
+def test_m_comp_on_the_pages_constants(oracle_mod):
+    """Section 2.A quotes p = 2, M_mem = 131072 tokens and M_comp = 2.2e9.
+    The reading of how M_comp follows from a fit -- the B * S^p of the
+    memory-bound bucket of a reference length -- gives, for the reference
+    length 16380, 8 * 16380^2 = 2,146,435,200 (by hand: 16380^2 =
+    268,304,400), which is the quoted 2.2e9 to two digits, and the same
+    bucket batches for the four lengths (tests/golden/bucket_sizes.txt)."""
+    mc = C.m_comp(2.0, 131072, 16380)
+    assert mc == 2_146_435_200.0
+    assert abs(mc - 2.2e9) / 2.2e9 < 0.025
+    lengths = (1560, 8190, 16380, 32760)
+    assert [C.bshape_real(S, 131072, mc, 2.0) for S in lengths] == \
+        [oracle_mod.bshape(S, 131072, 2_200_000_000, 2) for S in lengths] == \
+        [84, 16, 8, 2]
+
+
+def test_m_comp_is_the_reference_buckets_cost():
+    """Brute force over the memory-feasible batches of the reference length:
+    M_comp is the largest B * s_ref^p among them, so the bucket rule at M_comp
+    gives the reference length its memory-bound batch, and a longer length
+    never a batch whose B * S^p exceeds M_comp (unless that batch is 1)."""
+    g = np.random.default_rng(11)
+    for _ in range(300):
+        p = float(g.uniform(0.5, 3.0))
+        s_ref = int(g.integers(100, 40000))
+        m_mem = int(g.integers(s_ref, 400000))
+        mc = C.m_comp(p, m_mem, s_ref)
+        best = max(B * float(s_ref) ** p for B in range(1, m_mem // s_ref + 1))
+        assert mc == pytest.approx(best, rel=1e-12)
+        assert C.bshape_real(s_ref, m_mem, mc * (1 + 1e-12), p) == \
+            m_mem // s_ref
+        S = int(g.integers(s_ref, 4 * s_ref + 1))
+        b = C.bshape_real(S, m_mem, mc, p)
+        assert b == 1 or b * float(S) ** p <= mc * (1 + 1e-12)
+    assert C.m_comp(2.0, 131072, 0) == -1.0
+    assert C.m_comp(-1.0, 131072, 16380) == -1.0
+    assert C.m_comp(float("nan"), 131072, 16380) == -1.0

@@ -65,6 +65,12 @@ MUTANTS = [
      "return t - (a + bs * (S ** p) / scale)", COSTFIT),
     ("bucket rule rounds up", PY, "q = math.floor(m_comp / math.pow(float(S), p))",
      "q = math.ceil(m_comp / math.pow(float(S), p))", COSTFIT),
+    ("compute bound without the integer batch", PY,
+     "return float(m_mem // s_ref) * math.pow(float(s_ref), p)",
+     "return float(m_mem / s_ref) * math.pow(float(s_ref), p)", COSTFIT),
+    ("compute bound at the next batch", PY,
+     "return float(m_mem // s_ref) * math.pow(float(s_ref), p)",
+     "return float(m_mem // s_ref + 1) * math.pow(float(s_ref), p)", COSTFIT),
 ]
 CONTROLS = [
     ("comment only (C)", C, "/* Forward: y = xhat", "/* forward: y = xhat",
@@ -86,8 +92,8 @@ def _mutant(tmp_path, file, old, new):
     assert src.count(old) == 1, f"{old!r} occurs {src.count(old)} times"
     path.write_text(src.replace(old, new))
     subprocess.run(["gcc", "-O2", "-std=c99", "-fopenmp", "-fPIC", "-shared",
-                    str(dst / "adaln_oracle.c"), "-o",
-                    str(dst / "liboracle.so"), "-lm"], check=True)
+                    str(dst / "adaln_oracle.c"), str(dst / "check_rows.c"),
+                    "-o", str(dst / "liboracle.so"), "-lm"], check=True)
     return root
 
 

@@ -78,6 +78,23 @@ def test_bshape_real_matches_oracle():
     assert lib.adaln_bshape_real(10, 10, 1.0, float("nan")) == _lib.ERR_INVALID
 
 
+def test_mcomp_matches_oracle():
+    g = np.random.default_rng(4)
+    lib = _lib.load()
+    for _ in range(500):
+        p = float(g.uniform(0.0, 3.0))
+        s_ref = int(g.integers(1, 10 ** 6))
+        m_mem = int(g.integers(0, 10 ** 8))
+        got = lib.adaln_mcomp(p, m_mem, s_ref)
+        assert got == pytest.approx(C.m_comp(p, m_mem, s_ref), rel=1e-15,
+                                    abs=0.0), (p, m_mem, s_ref)
+    assert lib.adaln_mcomp(2.0, 131072, 16380) == 2_146_435_200.0
+    for bad in ((2.0, 131072, 0), (-0.5, 131072, 16380),
+                (float("inf"), 131072, 16380), (2.0, -1, 16380)):
+        assert lib.adaln_mcomp(*bad) == -1.0
+        assert C.m_comp(*bad) == -1.0
+
+
 def test_python_scheduler_helpers(oracle_mod):
     from adaln_fwd_amd import sched
     B, S, t = _data(7, 0.02)

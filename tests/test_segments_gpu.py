@@ -4,9 +4,9 @@ sequences back to back in one [T, D] tensor, each with its own modulation
 vector -- mixed-length samples packed without padding, and the text and
 video token segments of two-stream (MMDiT) samples.
 
-Small layouts are compared in full (every output element); the full-size
-packed mixed-length pack and the MMDiT layout on sampled rows, with dscale
-and dshift compared in full.
+Every case is compared in full: small layouts element by element in Python,
+the full-size packed mixed-length pack and the MMDiT layout row by row through
+the oracle library's row checker, with dscale and dshift in full.
 """
 
 import numpy as np
@@ -202,26 +202,20 @@ def test_wide_rows_rejected(A):
     assert e.value.code == -6
 
 
-def _full_size(A, inp, name, k_rows):
+def _full_size(A, inp, name):
+    """Every row of y, dx, mean and rstd (through the oracle's row checker,
+    each row with its segment's modulation vector) and dscale/dshift in
+    full."""
     T = int(inp.seg_offsets[-1])
     D = inp.x.shape[1]
-    _say(f"{name}: nseg={len(inp.seg_offsets) - 1} T={T} D={D}")
+    _say(f"{name}: nseg={len(inp.seg_offsets) - 1} T={T} D={D}, every row")
     dev = P.packed_to_device(inp)
     out = P.gpu_packed(inp, dev)
-    rows = P.sample_rows(T, k_rows, seed=1)
-    # every segment's first and last row too
-    ends = np.r_[inp.seg_offsets[:-1], inp.seg_offsets[1:] - 1]
-    ends = ends[(ends >= 0) & (ends < T)]
-    rows = np.unique(np.r_[rows, ends])
-    idx = torch.from_numpy(rows).to("cuda")
-    got = dict(y=out["y"].index_select(0, idx).cpu(),
-               dx=out["dx"].index_select(0, idx).cpu(),
-               mean=out["mean"].index_select(0, idx).cpu(),
-               rstd=out["rstd"].index_select(0, idx).cpu(),
-               dscale=out["dscale"].cpu(), dshift=out["dshift"].cpu())
     torch.cuda.synchronize()
+    got = {k: v.cpu() for k, v in out.items()}
     del dev, out
-    for r in P.compare_packed_rows(inp, got, rows, "bf16"):
+    for r in P.check_all_rows(inp.x, inp.dy, inp.scale, inp.shift, got,
+                              "bf16", row_mod=P.row_mods(inp)):
         _say(f"  rows {r}")
     for r in P.compare_packed_full(inp, got, "bf16", with_rows=False):
         _say(f"  full {r}")
@@ -230,14 +224,14 @@ def _full_size(A, inp, name, k_rows):
 def test_packed_mixed_full_size(A):
     lengths = synth.pack_lengths(seed=0)
     inp = synth.make_packed(synth.PACKED_MIXED, lengths, seed=0)
-    _full_size(A, inp, "packed mixed-length pack", 2048)
+    _full_size(A, inp, "packed mixed-length pack")
 
 
 def test_mmdit_layout_full_size(A):
     wl = synth.MMDIT_PACKED
     lengths, mods = synth.mmdit_layout(wl.B)
     inp = synth.make_packed(wl, lengths, mods, nmod=2 * wl.B, seed=0)
-    _full_size(A, inp, "two-stream layout", 2048)
+    _full_size(A, inp, "two-stream layout")
 
 
 def _random_tables(seed, count):
