@@ -31,6 +31,8 @@ SIGNATURES = {
     "adaln_bwd_workspace_bytes": (_SZ, [_I64, _I64, _I64, _INT]),
     "adaln_bwd": (_INT, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ,
                          _I64, _I64, _I64, _INT, _VP]),
+    "adaln_bwd_noalloc": (_INT, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                                 _I64, _I64, _I64, _INT, _VP]),
     "adaln_bwd_fused": (_INT, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _I64,
                                _I64, _I64, _INT, _VP]),
     "adaln_bwd_finish": (_INT, [_VP, _SZ, _VP, _VP, _I64, _I64, _I64, _INT,

@@ -4,6 +4,7 @@
 // invalid call enqueues nothing.
 #include <stdarg.h>
 #include <algorithm>
+#include <mutex>
 #include <stdio.h>
 #include <stdint.h>
 
@@ -754,4 +755,72 @@ ADALN_API int adaln_bwd_segments(const void *dy, const void *x,
                                (int32_t)nmod, (int32_t)D, s);
   if (e != hipSuccess) return hip_fail(e, "adaln_bwd_segments launch");
   return ok();
+}
+
+// ------------------------------------------------- backward without a buffer
+
+namespace {
+
+// Scratch of adaln_bwd_noalloc: the backward's partial rows, in a device
+// array of the library's own.  Each GPU the library runs on holds its own
+// copy until the process ends.  In host code `scratch` names a host-side
+// stand-in, never the device memory: the device address is looked up once
+// per device with hipGetSymbolAddress and only that address is passed on.
+constexpr size_t kScratchBytes = size_t(32) << 20;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mu;
+void *g_scratch[kMaxDevices] = {};
+
+// Device address of the calling thread's current device's scratch.
+int scratch_address(void **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "adaln_bwd_noalloc: hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(ADALN_ERR_HIP, "adaln_bwd_noalloc: device %d out of range",
+                dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess)
+      return hip_fail(e, "adaln_bwd_noalloc: hipGetSymbolAddress");
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return ADALN_OK;
+}
+
+}  // namespace
+
+ADALN_API int adaln_bwd_noalloc(const void *dy, const void *x,
+                                const void *scale, const float *mean,
+                                const float *rstd, void *dx, float *dscale,
+                                float *dshift, int64_t B, int64_t N,
+                                int64_t D, int dtype, void *stream) {
+  // the checks of adaln_bwd, then the size check, before any HIP call
+  ADALN_TRY(check_shape(B, N, D, dtype));
+  const bool rows = B * N > 0;
+  ADALN_TRY(check_ptr(dy, rows, "dy"));
+  ADALN_TRY(check_ptr(x, rows, "x"));
+  ADALN_TRY(check_ptr(scale, rows, "scale"));
+  ADALN_TRY(check_ptr(mean, rows, "mean"));
+  ADALN_TRY(check_ptr(rstd, rows, "rstd"));
+  ADALN_TRY(check_ptr(dx, rows, "dx"));
+  ADALN_TRY(check_ptr(dscale, B > 0, "dscale"));
+  ADALN_TRY(check_ptr(dshift, B > 0, "dshift"));
+  const size_t need = workspace_bytes(B, N, D, dtype);
+  if (need > kScratchBytes)
+    return fail(ADALN_ERR_WORKSPACE,
+                "adaln_bwd_noalloc: this shape needs %zu bytes of scratch, "
+                "the library's static scratch holds %zu (use adaln_bwd with "
+                "a workspace)",
+                need, kScratchBytes);
+  if (B == 0) return ok();
+  void *ws = nullptr;
+  ADALN_TRY(scratch_address(&ws));
+  return adaln_bwd(dy, x, scale, mean, rstd, dx, dscale, dshift, ws,
+                   kScratchBytes, B, N, D, dtype, stream);
 }

@@ -167,6 +167,35 @@ def bwd(dy: torch.Tensor, x: torch.Tensor, scale: torch.Tensor,
     return dx, dscale, dshift
 
 
+def bwd_noalloc(dy: torch.Tensor, x: torch.Tensor, scale: torch.Tensor,
+                mean: torch.Tensor, rstd: torch.Tensor, *,
+                dx: Optional[torch.Tensor] = None,
+                dscale: Optional[torch.Tensor] = None,
+                dshift: Optional[torch.Tensor] = None, stream=None):
+    """:func:`bwd` through ``adaln_bwd_noalloc``: the library keeps the
+    partial sums in its own static device scratch, so the call needs no
+    workspace (outputs not passed in are still allocated here).  Calls that
+    overlap on one GPU share that scratch and must be ordered."""
+    B, N, D, dev, dt = _bwd_common(dy, x, scale, mean, rstd)
+    lib = _lib.load()
+    with _on(dev, stream):
+        if dx is None:
+            dx = torch.empty_like(x)
+        if dscale is None:
+            dscale = torch.empty(B, D, dtype=torch.float32, device=dev)
+        if dshift is None:
+            dshift = torch.empty(B, D, dtype=torch.float32, device=dev)
+        _check(dx, "dx", (B, N, D), dt, dev)
+        _check(dscale, "dscale", (B, D), torch.float32, dev)
+        _check(dshift, "dshift", (B, D), torch.float32, dev)
+        rc = lib.adaln_bwd_noalloc(_ptr(dy), _ptr(x), _ptr(scale),
+                                   _ptr(mean), _ptr(rstd), _ptr(dx),
+                                   _ptr(dscale), _ptr(dshift), B, N, D,
+                                   _code(x), _stream(dev, stream))
+    _lib.check(rc, "adaln_bwd_noalloc")
+    return dx, dscale, dshift
+
+
 def bwd_fused(dy, x, scale, mean, rstd, *, dx=None, workspace=None,
               stream=None):
     """First launch of :func:`bwd`: dx plus dscale/dshift partial sums in

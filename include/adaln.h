@@ -126,6 +126,25 @@ int adaln_bwd(const void *dy, const void *x, const void *scale,
               int64_t B, int64_t N, int64_t D, int dtype, void *stream);
 
 /*
+ * adaln_bwd for callers that cannot allocate device memory or pass a
+ * workspace: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation.  Same arguments, kernels and results as adaln_bwd
+ * (bit for bit), without the workspace: the partial rows go to a static
+ * device array of the library, 32 MiB per GPU, held until the process ends.
+ * Shapes whose adaln_bwd_workspace_bytes exceeds 32 MiB return
+ * ADALN_ERR_WORKSPACE before any HIP call.  The first call on a device looks
+ * up the array's device address (hipGetSymbolAddress) and keeps it; make one
+ * call before capturing a graph.  Every call on a GPU shares that GPU's
+ * array, so calls that overlap on one GPU (other streams, other threads)
+ * race and must be ordered by the caller.  Nothing needs clearing between
+ * calls: each call writes every partial row it reads.
+ */
+int adaln_bwd_noalloc(const void *dy, const void *x, const void *scale,
+                      const float *mean, const float *rstd, void *dx,
+                      float *dscale, float *dshift, int64_t B, int64_t N,
+                      int64_t D, int dtype, void *stream);
+
+/*
  * The two launches adaln_bwd makes for rows of at most 1280 vectors
  * (D <= 10240 bf16 / 5120 f32), exposed so callers can schedule or time them
  * separately.  Rows of up to 320 vectors are owned by one wavefront each,

@@ -207,6 +207,22 @@ def test_segments_workspace_bytes(lib):
     assert ws(None, 0, 64, 1) == 0           # no segments: no partials
 
 
+def test_noalloc_refuses_shapes_beyond_its_scratch(lib):
+    _no_gpu()
+    p = 0x1000
+    # 1024 samples of 10240 bf16 features: 80 MiB of partial rows > 32 MiB
+    assert lib.adaln_bwd_workspace_bytes(1024, 100, 10240, 1) > 32 << 20
+    rc = lib.adaln_bwd_noalloc(p, p, p, p, p, p, p, p, 1024, 100, 10240, 1,
+                               None)
+    assert rc == _lib.ERR_WORKSPACE
+    assert b"scratch" in lib.adaln_last_error()
+    # the argument checks of adaln_bwd come first
+    assert lib.adaln_bwd_noalloc(p, p, p, p, p, p, p, p, 2, 3, 60, 1,
+                                 None) == _lib.ERR_ALIGN
+    assert lib.adaln_bwd_noalloc(None, p, p, p, p, p, p, p, 2, 3, 64, 1,
+                                 None) == _lib.ERR_INVALID
+
+
 def test_max_d(lib):
     assert lib.adaln_max_d(1) == 32768
     assert lib.adaln_max_d(0) == 16384
