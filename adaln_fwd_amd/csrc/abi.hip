@@ -168,6 +168,20 @@ DmodPlan choose_dmod_plan(int64_t B, int64_t N, int64_t nvec) {
 #define ADALN_BWD_MIN_BPS 1
 #endif
 
+// Backward of one-wavefront rows with many samples: sample b's walk starts
+// (b * 97) % N rows into the sample instead of at row 0.  Every sample's
+// workgroups sweep their own window of rows; started at the same row, the B
+// windows move in step through addresses a fixed multiple of the sample size
+// apart, and HBM serves that worse than windows offset from each other.
+// Measured on MI355X (fused backward, bf16, D = 1536): 16 x 1560 rows 49.8
+// -> 45.2 us, 32 x 780 55.3 -> 45.5 us, 96 x 260 45.7 -> 45.8 us, 2 to 8
+// samples within 1% either way; offsets of 13 to 389 rows all helped at 16
+// and 32 samples, 97 the most overall.  The pair-of-wavefronts backward
+// (wider rows) keeps the aligned start: there the offsets cost 2-4% at
+// D = 3072 with 16 and 84 samples.
+constexpr int kBwdSkewRows = 97;
+constexpr int64_t kBwdSkewMinSamples = 16;
+
 // Samples of at least this many rows count as long for the forward plan.
 constexpr int64_t kLongSample = 4096;
 
@@ -223,6 +237,7 @@ bool choose_stream_plan(int64_t B, int64_t N, int64_t nvec, bool bwd,
     p.bps = (int)bps;
     p.groups = (int)groups;
     p.grid = (int)(bps * (groups < B ? groups : B));
+    if (bwd && p.W == 1 && B >= kBwdSkewMinSamples) p.skew = kBwdSkewRows;
   }
   *plan = p;
   return true;
@@ -549,18 +564,19 @@ ADALN_API int adaln_plan(int which, int64_t B, int64_t N, int64_t D,
                              : choose_dmod_plan(B, N, nvec).n_tiles;
     const FinishPlan fp = finish_plan(B, (int32_t)D, rows);
     const int64_t launched = fp.blocks < kMaxGrid ? fp.blocks : kMaxGrid;
-    const int64_t v[6] = {fp.F, fp.wpc, fp.cpb, B > 0 ? launched : 0,
-                          fp.threads, rows};
-    std::copy(v, v + 6, out);
+    const int64_t v[7] = {fp.F, fp.wpc, fp.cpb, B > 0 ? launched : 0,
+                          fp.threads, rows, 0};
+    std::copy(v, v + 7, out);
     return ok();
   }
   if (choose_stream_plan(B, N, nvec, which == 1, &sp)) {
     const int64_t walkers = 4 / sp.W;  // four-wavefront workgroups
-    const int64_t v[6] = {sp.V, sp.W, sp.grid, sp.bps, sp.groups, walkers};
-    std::copy(v, v + 6, out);
+    const int64_t v[7] = {sp.V,      sp.W,    sp.grid, sp.bps,
+                          sp.groups, walkers, sp.skew};
+    std::copy(v, v + 7, out);
   } else if (which == 0 && choose_tile_plan(B, N, nvec, &tp)) {
-    const int64_t v[6] = {tp.V, tp.W, tp.grid, tp.bps, tp.groups, 1};
-    std::copy(v, v + 6, out);
+    const int64_t v[7] = {tp.V, tp.W, tp.grid, tp.bps, tp.groups, 1, 0};
+    std::copy(v, v + 7, out);
   } else {
     return fail(ADALN_ERR_UNSUPPORTED, "no %s plan for D=%lld",
                 which ? "fused backward" : "forward", (long long)D);

@@ -17,7 +17,10 @@
 // workgroups per sample, and each wavefront walks its sample's rows with a
 // stride of 4*bps rows, so the active wavefronts sweep a narrow window of
 // memory in order.  The set of rows a workgroup visits in one sample is its
-// sequence tile.  At the end of a sample the four wavefronts' accumulators
+// sequence tile.  With many samples, sample b's walk starts (b * skew) % N
+// rows in and wraps around (the planner's skew; rot below), so that the
+// samples' windows are not aligned with each other in memory.  At the end
+// of a sample the four wavefronts' accumulators
 // are added in wavefront order through LDS and written as one partial row
 // per (sample, workgroup): the workspace holds [B, bps, D] partial sums for
 // dscale and for dshift, which dmod_finish_kernel adds over the bps
@@ -52,10 +55,16 @@ __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void bwd_stream_kernel(
   }
 
   // One segment (a sample, or a packed sequence): rows [row0, row0 + N),
-  // modulated by vector `mod`; this workgroup is number k_in of bps and
-  // writes partial row part_row.  Workgroup-uniform (barriers below).
+  // modulated by vector `mod`, walked from row row0 + rot; this workgroup
+  // is number k_in of bps and writes partial row part_row.
+  // Workgroup-uniform (barriers below).
   for_each_segment(map, [&](int64_t row0, int N, int mod, int k_in, int bps,
-                            int part_row) {
+                            int part_row, int rot) {
+    // row of the segment that the walk's n-th position stands for
+    auto at = [&](int n) -> int64_t {
+      const int p = n + rot;
+      return row0 + (p >= N ? p - N : p);
+    };
     const int stride = bps * kWaves;
     Vec sv[V];
 #pragma unroll
@@ -70,9 +79,9 @@ __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void bwd_stream_kernel(
       for (int e = 0; e < E; ++e) acc_s[k][e] = acc_h[k][e] = 0.f;
 
     auto load_row = [&](Vec (&xv)[V], Vec (&gv)[V], float (&st)[2], int n) {
-      st[0] = mean[row0 + n];
-      st[1] = rstd[row0 + n];
-      const int64_t off = (row0 + n) * D;
+      st[0] = mean[at(n)];
+      st[1] = rstd[at(n)];
+      const int64_t off = at(n) * D;
 #pragma unroll
       for (int k = 0; k < V; ++k) {
         xv[k] = ok[k] ? load_stream(x + off + (int64_t)jv[k] * E) : vzero();
@@ -102,7 +111,7 @@ __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void bwd_stream_kernel(
 #pragma unroll
       for (int k = 0; k < V; ++k) opaque(xv[k]), opaque(gv[k]);
 
-      const int64_t off = (row0 + n) * D;
+      const int64_t off = at(n) * D;
 #pragma unroll
       for (int k = 0; k < V; ++k) {
         if (ok[k]) {
@@ -255,7 +264,7 @@ hipError_t launch_bwd_fused(int dtype, const StreamPlan &plan, const void *dy,
                             const float *mean, const float *rstd, void *dx,
                             float *part_scale, float *part_shift, int32_t B,
                             int32_t N, int32_t D, hipStream_t stream) {
-  const UniformMap map{B, N, plan.bps, plan.groups};
+  const UniformMap map{B, N, plan.bps, plan.groups, plan.skew};
   return bwd_stream_dispatch(dtype, plan.V, plan.grid, map, dy, x, scale,
                              mean, rstd, dx, part_scale, part_shift, D,
                              stream);

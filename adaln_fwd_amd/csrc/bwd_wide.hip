@@ -65,13 +65,19 @@ bwd_wide_kernel(
   }
 
   int parity = 0;
-  // One segment: rows [row0, row0 + N) modulated by vector `mod`; this
+  // One segment: rows [row0, row0 + N) modulated by vector `mod`, walked
+  // from row row0 + rot (the planner keeps rot = 0 for this kernel); this
   // workgroup is number k_in of bps and writes partial row part_row.  Every
   // wavefront of the workgroup runs the same number of loop iterations
   // (barriers below); a pair without a row in the last one only takes part
   // in its barrier.
   for_each_segment(map, [&](int64_t row0, int N, int mod, int k_in, int bps,
-                            int part_row) {
+                            int part_row, int rot) {
+    // row of the segment that the walk's n-th position stands for
+    auto at = [&](int n) -> int64_t {
+      const int p = n + rot;
+      return row0 + (p >= N ? p - N : p);
+    };
     const int stride = bps * kPairs;
     Vec sv[V];
 #pragma unroll
@@ -91,12 +97,12 @@ bwd_wide_kernel(
     for (int it = 0; it < iters; ++it) {
       const int n = first + pair + it * stride;
       const bool live = n < N;  // uniform across the wavefront
-      const int64_t off = (row0 + n) * D;
+      const int64_t off = at(n) * D;
       Vec xv[V], gv[V];
       float mu = 0.f, r = 0.f, s1 = 0.f, s2 = 0.f;
       if (live) {
-        mu = mean[row0 + n];
-        r = rstd[row0 + n];
+        mu = mean[at(n)];
+        r = rstd[at(n)];
 #pragma unroll
         for (int k = 0; k < V; ++k) {
           xv[k] = ok[k] ? load_stream(x + off + (int64_t)jv[k] * E) : vzero();
@@ -250,7 +256,7 @@ hipError_t launch_bwd_wide(int dtype, const StreamPlan &plan, const void *dy,
                            const float *mean, const float *rstd, void *dx,
                            float *part_scale, float *part_shift, int32_t B,
                            int32_t N, int32_t D, hipStream_t stream) {
-  const UniformMap map{B, N, plan.bps, plan.groups};
+  const UniformMap map{B, N, plan.bps, plan.groups, plan.skew};
   return bwd_wide_dispatch(dtype, plan.V, plan.grid, map, dy, x, scale, mean,
                            rstd, dx, part_scale, part_shift, D, stream);
 }

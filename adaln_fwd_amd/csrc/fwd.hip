@@ -54,7 +54,7 @@ __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void fwd_stream_kernel(
   // One segment (a sample, or a packed sequence): rows [row0, row0 + N),
   // modulated by vector `mod`; this workgroup is number k_in of bps.
   for_each_segment(map, [&](int64_t row0, int N, int mod, int k_in, int bps,
-                            int) {
+                            int, int) {
     const int stride = bps * kWaves;
     Vec sv[V], hv[V];
 #pragma unroll
@@ -179,7 +179,7 @@ __attribute__((amdgpu_waves_per_eu(fwd_waves_per_simd(V)))) void fwd_tile_kernel
   int parity = 0;
 
   for_each_segment(map, [&](int64_t row0, int N, int mod, int k_in, int bps,
-                            int) {
+                            int, int) {
     Vec sv[V], hv[V];
 #pragma unroll
     for (int k = 0; k < V; ++k) {
@@ -346,7 +346,7 @@ hipError_t launch_fwd_stream(int dtype, const StreamPlan &plan, const void *x,
                              const void *scale, const void *shift, void *y,
                              float *mean, float *rstd, int32_t B, int32_t N,
                              int32_t D, hipStream_t stream) {
-  const UniformMap map{B, N, plan.bps, plan.groups};
+  const UniformMap map{B, N, plan.bps, plan.groups, 0};
   return fwd_stream_dispatch(dtype, plan.V, plan.grid, map, x, scale, shift,
                              y, mean, rstd, D, stream);
 }
@@ -397,7 +397,7 @@ hipError_t launch_fwd_tiles(int dtype, const TilePlan &plan, const void *x,
                             const void *scale, const void *shift, void *y,
                             float *mean, float *rstd, int32_t B, int32_t N,
                             int32_t D, hipStream_t stream) {
-  const UniformMap map{B, N, plan.bps, plan.groups};
+  const UniformMap map{B, N, plan.bps, plan.groups, 0};
   return fwd_tile_dispatch(dtype, plan.V, plan.W, plan.grid, map, x, scale,
                            shift, y, mean, rstd, D, stream);
 }

@@ -50,6 +50,7 @@ struct StreamPlan {
   int grid = 0;
   int bps = 0;     // workgroups per sample (partial rows per sample)
   int groups = 0;  // samples in flight
+  int skew = 0;    // sample b's walk starts (b * skew) % N rows in
 };
 
 // How a stream kernel's workgroups map to token rows.  UniformMap: B samples
@@ -64,6 +65,7 @@ struct UniformMap {
   int32_t N;
   int32_t bps;
   int32_t groups;
+  int32_t skew;  // sample b's walk starts (b * skew) % N rows in
 };
 
 constexpr int kMaxSegments = 128;
@@ -75,16 +77,19 @@ struct SegMap {
   int64_t row_start[kMaxSegments + 1];
 };
 
-// Calls f(row0, rows, mod, k_in, bps, part_row) for each segment the calling
-// workgroup works on.  Workgroup-uniform, so a kernel may place barriers in
-// f.
+
+// Calls f(row0, rows, mod, k_in, bps, part_row, rot) for each segment the
+// calling workgroup works on; a kernel visits the segment's rows in the
+// order n = 0, 1, ..., rows - 1 of its walk, at row row0 + (n + rot) mod
+// rows.  Workgroup-uniform, so a kernel may place barriers in f.
 template <class F>
 __device__ __forceinline__ void for_each_segment(const UniformMap &m, F &&f) {
   const int slot = blockIdx.x / m.bps;
   const int k_in = blockIdx.x - slot * m.bps;
   if (slot >= m.groups) return;
   for (int b = slot; b < m.B; b += m.groups)
-    f((int64_t)b * m.N, m.N, b, k_in, m.bps, b * m.bps + k_in);
+    f((int64_t)b * m.N, m.N, b, k_in, m.bps, b * m.bps + k_in,
+      m.skew > 0 && m.N > 0 ? (int)(((int64_t)b * m.skew) % m.N) : 0);
 }
 
 template <class F>
@@ -103,7 +108,7 @@ __device__ __forceinline__ void for_each_segment(const SegMap &m, F &&f) {
   const int s = lo;
   const int bps = m.wg_start[s + 1] - m.wg_start[s];
   f(m.row_start[s], (int)(m.row_start[s + 1] - m.row_start[s]), m.mod[s],
-    bid - m.wg_start[s], bps, bid);
+    bid - m.wg_start[s], bps, bid, 0);
 }
 
 #define ADALN_STREAM_V(X) X(1) X(2) X(3) X(4) X(5) X(6) X(8) X(10) X(12) X(16)

@@ -292,7 +292,8 @@ def plan(which: str, B: int, N: int, D: int, dtype: torch.dtype) -> dict:
     """How :func:`fwd` (``which="fwd"``) or :func:`bwd_fused` (``"bwd"``)
     splits a [B, N, D] batch into work (host-only): vectors per lane,
     wavefronts per row, workgroups, workgroups per sample, samples in
-    flight, row walkers per workgroup.  ``which="finish"``: the launch that
+    flight, row walkers per workgroup, and the skew of each sample's walk
+    (position n of sample b is row (n + b * skew) mod N).  ``which="finish"``: the launch that
     sums the backward's partial rows: features per column block, wavefronts
     per block, blocks per workgroup, workgroups, threads per workgroup,
     partial rows summed per output."""
@@ -300,7 +301,7 @@ def plan(which: str, B: int, N: int, D: int, dtype: torch.dtype) -> dict:
     if which not in codes:
         raise ValueError(f"which must be 'fwd', 'bwd' or 'finish', got "
                          f"{which!r}")
-    out = (ctypes.c_int64 * 6)()
+    out = (ctypes.c_int64 * 7)()
     rc = _lib.load().adaln_plan(codes[which], B, N, D,
                                 _DTYPES.get(dtype, -1), out)
     _lib.check(rc, "adaln_plan")
@@ -308,7 +309,7 @@ def plan(which: str, B: int, N: int, D: int, dtype: torch.dtype) -> dict:
         return dict(F=out[0], wpc=out[1], cpb=out[2], workgroups=out[3],
                     threads=out[4], rows=out[5])
     return dict(V=out[0], waves_per_row=out[1], workgroups=out[2],
-                bps=out[3], groups=out[4], walkers=out[5])
+                bps=out[3], groups=out[4], walkers=out[5], skew=out[6])
 
 
 class SegTable:

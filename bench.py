@@ -15,10 +15,11 @@ step is adaln_fwd_segments then adaln_bwd_segments over the whole pack;
 equal-length segments.  W untimed warm-up steps
 run first; then exactly K steps are timed between two device
 synchronisations.  Inside the timed region, HIP events recorded on the same
-stream just before and after the backward's main kernel give that kernel's
-average duration (the roofline line).  Events between every pair of calls
-cost about 2% of the step, so the per-kernel breakdown comes from K further
-steps with an event at every boundary, after the timed region.
+stream just before and after the backward's main kernel, on every fourth
+step (--event-every), give that kernel's average duration (the roofline
+line); each event record costs the step a few microseconds, so they are not
+on every step.  The per-kernel breakdown comes from K further steps with an
+event at every boundary, after the timed region.
 
 Prints one JSON line:
   value         tokens/s over the timed steps (wall clock)
@@ -210,6 +211,22 @@ def traffic_from_counters(pmc_dir: str, workload: str, copy_bytes: int):
     return out
 
 
+def single_shape(synth, wl, bucket=None):
+    """(B, N, D) of a single-shape workload, or of the mixed schedule's
+    buckets of length `bucket` (B from the bucket rule)."""
+    if bucket is not None:
+        import adaln_fwd_amd as A
+        B = A.bshape(bucket, synth.MIXED_M_MEM, synth.MIXED_M_COMP,
+                     synth.MIXED_P)
+        return B, bucket, wl.D
+    return wl.shape
+
+
+def workload_name(wl, bucket=None) -> str:
+    """Name of a workload in profile file names."""
+    return wl.name if bucket is None else f"{wl.name}_S{bucket}"
+
+
 def algorithmic_bytes(B, N, D, esize, n_tiles):
     """Bytes each call must move at minimum (reads + writes)."""
     T = B * N
@@ -244,7 +261,9 @@ def cpu_baseline(inp, budget_s: float, sample_rows: int = 16384,
                  chunk_rows: int = 4096):
     """The oracle, untuned, on the first `sample_rows` token rows of the
     workload (converted to float64 once), in chunks of `chunk_rows`, cycling
-    over the sample until about `budget_s` seconds of oracle time."""
+    over the sample until about `budget_s` seconds of oracle time, on every
+    host thread it may use; then the same on one thread for half the time
+    (reported under "single_thread")."""
     import torch
     import oracle
     B, N, D = inp.x.shape
@@ -255,24 +274,43 @@ def cpu_baseline(inp, budget_s: float, sample_rows: int = 16384,
     gs = inp.dy.reshape(B * N, D)[:R].unsqueeze(1).double().numpy()
     ss = inp.scale[b].double().numpy()
     hs = inp.shift[b].double().numpy()
-    rows_done, spent, r0 = 0, 0.0, 0
-    while spent < budget_s:
-        r1 = min(R, r0 + chunk_rows)
-        t0 = time.perf_counter()
-        oracle.fwd(xs[r0:r1], ss[r0:r1], hs[r0:r1])
-        oracle.bwd(gs[r0:r1], xs[r0:r1], ss[r0:r1])
-        spent += time.perf_counter() - t0
-        rows_done += r1 - r0
-        r0 = r1 % R
-    return {
-        "value": rows_done / spent,
+
+    def run(seconds, chunk):
+        rows_done, spent, r0 = 0, 0.0, 0
+        while spent < seconds:
+            r1 = min(R, r0 + chunk)
+            t0 = time.perf_counter()
+            oracle.fwd(xs[r0:r1], ss[r0:r1], hs[r0:r1])
+            oracle.bwd(gs[r0:r1], xs[r0:r1], ss[r0:r1])
+            spent += time.perf_counter() - t0
+            rows_done += r1 - r0
+            r0 = r1 % R
+        return rows_done, spent
+
+    def describe(rows_done, spent, chunk):
+        return (f"the first {R} token rows of {B}x{N}x{D}, in chunks of "
+                f"{chunk} rows, forward + backward in float64, cycled for "
+                f"{spent:.1f} s of oracle time ({rows_done} rows)")
+
+    threads = oracle.num_threads()
+    done, spent = run(budget_s, chunk_rows)
+    rec = {
+        "value": done / spent,
         "unit": "tokens/s",
-        "cores": oracle.num_threads(),
+        "cores": threads,
         "kind": "oracle",
-        "sample": (f"the first {R} token rows of {B}x{N}x{D}, in chunks of "
-                   f"{chunk_rows} rows, forward + backward in float64, cycled "
-                   f"for {spent:.1f} s of oracle time ({rows_done} rows)"),
+        "sample": describe(done, spent, chunk_rows),
     }
+    oracle.set_num_threads(1)
+    try:
+        one_chunk = max(1, chunk_rows // 16)
+        done1, spent1 = run(budget_s / 2, one_chunk)
+    finally:
+        oracle.set_num_threads(threads)
+    rec["single_thread"] = {"value": done1 / spent1, "unit": "tokens/s",
+                            "cores": 1,
+                            "sample": describe(done1, spent1, one_chunk)}
+    return rec
 
 
 def copy_probe(nbytes: int, steps: int, warmup: int) -> int:
@@ -660,11 +698,17 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="large_model")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--event-every", type=int, default=4, metavar="K",
+                    help="bracket the dominant kernel with HIP events on "
+                         "every K-th timed step (default 4)")
     ap.add_argument("--cpu-budget", type=float, default=10.0,
                     help="seconds of oracle time for cpu_baseline (0: skip)")
     ap.add_argument("--traffic-from", metavar="DIR",
                     help="print per-kernel HBM traffic computed from the "
                          "rocprofv3 --pmc CSVs under DIR and exit")
+    ap.add_argument("--bucket", type=int, default=None, metavar="S",
+                    help="mixed_schedule: run only the buckets of length S "
+                         "(one shape), as a single-shape workload")
     ap.add_argument("--unpacked", action="store_true",
                     help="packed workloads: run the samples as batched "
                          "calls, one per segment length, instead")
@@ -692,9 +736,11 @@ def main(argv=None) -> int:
         import synth
         wl = synth.BY_NAME[args.workload]
         esize = 4 if wl.dtype == "f32" else 2
-        copy_bytes = wl.B * wl.N * wl.D * esize
-        print(json.dumps(traffic_from_counters(args.traffic_from, wl.name,
-                                               copy_bytes), indent=1))
+        B, N, D = single_shape(synth, wl, args.bucket)
+        copy_bytes = B * N * D * esize
+        print(json.dumps(traffic_from_counters(
+            args.traffic_from, workload_name(wl, args.bucket), copy_bytes),
+            indent=1))
         return 0
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -753,16 +799,34 @@ def main(argv=None) -> int:
                               synth.MIXED_P) for S in sorted(set(sched))}
         D = wl.D
         if args.copy_probe:
-            big = max(b * S for S, b in shapes.items())
+            big = (shapes[args.bucket] * args.bucket if args.bucket in shapes
+                   else max(b * S for S, b in shapes.items()))
             return copy_probe(big * D * esize, args.steps, args.warmup)
-        log(f"schedule of {len(sched)} buckets, D={D}: drawing one input set "
-            f"per bucket shape {shapes}")
-        jobs = {}
-        for S, Bk in shapes.items():
-            inp = synth.make_inputs(synth.mixed_bucket(Bk, S), seed=args.seed,
-                                    bucket=sched.index(S))
-            jobs[S] = make_job(A, torch, inp, dev, esize)
-        order = [jobs[S] for S in sched]
+        if args.bucket is not None:
+            # one bucket shape of the schedule on its own: a step is its
+            # forward + backward
+            if args.bucket not in shapes:
+                print(f"--bucket must be one of {sorted(shapes)}",
+                      file=sys.stderr)
+                return 2
+            S = args.bucket
+            B, N = shapes[S], S
+            log(f"bucket S={S} of the schedule: B={B} N={S} D={D}")
+            first_inp = synth.make_inputs(synth.mixed_bucket(B, S),
+                                          seed=args.seed,
+                                          bucket=sched.index(S))
+            order = [make_job(A, torch, first_inp, dev, esize)]
+        else:
+            log(f"schedule of {len(sched)} buckets, D={D}: drawing one input "
+                f"set per bucket shape {shapes}")
+            jobs = {}
+            for S, Bk in shapes.items():
+                inp = synth.make_inputs(synth.mixed_bucket(Bk, S),
+                                        seed=args.seed, bucket=sched.index(S))
+                jobs[S] = make_job(A, torch, inp, dev, esize)
+                if S == sched[0]:
+                    first_inp = inp  # the CPU baseline's sample
+            order = [jobs[S] for S in sched]
     else:
         B, N, D = wl.shape
         if args.copy_probe:
@@ -827,10 +891,17 @@ def main(argv=None) -> int:
     torch.cuda.synchronize()
     dom_events = new_events()
     log(f"timing {args.steps} steps")
+    # HIP events bracket the dominant kernel on every `every`-th timed step
+    # (each event record costs the step a few microseconds)
+    every = max(1, min(args.event_every, args.steps))
+    sampled = list(range(0, args.steps, every))
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(dom_events[i], at=(dom, dom + 1))
+        if i % every == 0:
+            step(dom_events[i], at=(dom, dom + 1))
+        else:
+            step()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_step = 1e3 * elapsed / args.steps
@@ -918,8 +989,8 @@ def main(argv=None) -> int:
     tokens_s = tokens / (ms_step * 1e-3)
 
     dname = names[dom]
-    dom_ms = sum(ev[j][dom].elapsed_time(ev[j][dom + 1])
-                 for ev in dom_events for j in range(len(order))) / args.steps
+    dom_ms = sum(dom_events[i][j][dom].elapsed_time(dom_events[i][j][dom + 1])
+                 for i in sampled for j in range(len(order))) / len(sampled)
     src_hash = kernel_source_hash()
     achieved = tot_bytes[dname] / (dom_ms * 1e-3) / 1e9
     roofline = {
@@ -929,9 +1000,11 @@ def main(argv=None) -> int:
         "peak": HBM_PEAK_GBPS,
         "unit": "GB/s",
         "frac": round(achieved / HBM_PEAK_GBPS, 4),
-        "traffic": load_traffic(dname, wl.name, kernel_source_hash(dname)),
+        "traffic": load_traffic(dname, workload_name(wl, args.bucket),
+                                kernel_source_hash(dname)),
         "algorithmic_bytes_per_launch": int(tot_bytes[dname] / launches),
         "avg_launch_ms": round(dom_ms / launches, 5),
+        "timed_launches": len(sampled) * launches,
     }
     if probe is not None:
         probe["kernel_frac_of_probe"] = round(achieved / probe["gbps"], 4)
@@ -943,6 +1016,9 @@ def main(argv=None) -> int:
                   "dtype": wl.dtype, "modulation_vectors": nmod,
                   "lengths": {str(L): lengths.count(L)
                               for L in sorted(set(lengths))}}
+    elif wl.B is None and args.bucket is not None:
+        config = {"workload": f"{wl.name} bucket S={args.bucket}", "B": B,
+                  "N": N, "D": D, "dtype": wl.dtype}
     elif wl.B is None:
         config = {"workload": wl.name, "buckets": len(order), "D": D,
                   "tokens": tokens, "dtype": wl.dtype,

@@ -183,12 +183,14 @@ int adaln_bwd_fused_plan(int64_t B, int64_t N, int64_t D, int dtype,
 /*
  * How adaln_fwd (which = 0) or adaln_bwd_fused (which = 1) splits a batch
  * into work, for callers that account for it and for tests of the planner.
- * Fills out[0..5] with {vectors per lane V, wavefronts per row W, workgroups
+ * Fills out[0..6] with {vectors per lane V, wavefronts per row W, workgroups
  * launched, workgroups per sample bps, samples in flight groups, row walkers
- * per workgroup}.  Workgroup g with g / bps < groups works on samples
- * g / bps, g / bps + groups, ... in turn; in each, its walker w visits rows
- * (g % bps) * walkers + w, then every bps * walkers rows.  A walker is one
- * wavefront (W = 1) or the W wavefronts that share a row.  Returns
+ * per workgroup, skew}.  Workgroup g with g / bps < groups works on samples
+ * g / bps, g / bps + groups, ... in turn; in each sample b, its walker w
+ * visits the walk positions (g % bps) * walkers + w, then every
+ * bps * walkers positions; position n stands for row (n + b * skew) mod N of
+ * the sample (skew is 0 except in the backward of many samples).  A walker
+ * is one wavefront (W = 1) or the W wavefronts that share a row.  Returns
  * ADALN_ERR_UNSUPPORTED where the entry point would take another path (rows
  * too wide for the fused backward).  Host-only; no HIP call.
  *
@@ -202,6 +204,7 @@ int adaln_bwd_fused_plan(int64_t B, int64_t N, int64_t D, int dtype,
  * where L = g, except for F < 64 and g < 8 * (G / 8): L = (g % 8) * (G / 8)
  * + g / 8.  The j-th wpc wavefronts of a workgroup serve its j-th block;
  * wavefront s of them sums the rows [s * P / wpc, (s + 1) * P / wpc).
+ * out[6] is 0.
  */
 int adaln_plan(int which, int64_t B, int64_t N, int64_t D, int dtype,
                int64_t *out);

@@ -53,11 +53,13 @@ int main(void)
         CHECK(plan[1] == 2);
     }
     {
-        int64_t p[6];
+        int64_t p[7];
         CHECK(adaln_plan(0, 1, 75600, 5120, ADALN_BF16, p) == ADALN_OK);
-        CHECK(p[1] == 1 && p[2] == p[3] && p[5] == 4);
+        CHECK(p[1] == 1 && p[2] == p[3] && p[5] == 4 && p[6] == 0);
         CHECK(adaln_plan(1, 1, 75600, 5120, ADALN_BF16, p) == ADALN_OK);
         CHECK(p[1] == 2 && p[5] == 2);
+        CHECK(adaln_plan(1, 16, 1560, 1536, ADALN_BF16, p) == ADALN_OK);
+        CHECK(p[1] == 1 && p[6] == 97);
         CHECK(adaln_plan(2, 1, 75600, 5120, ADALN_BF16, p) == ADALN_OK);
         CHECK(p[0] == 32 && p[5] == 511 && p[4] == p[1] * p[2] * 64);
         CHECK(adaln_plan(3, 1, 75600, 5120, ADALN_BF16, p) == ADALN_ERR_INVALID);

@@ -36,7 +36,7 @@ def _shapes(seed, n):
 
 def _visits(p, B, N):
     """Times each (sample, row) is visited under the documented mapping."""
-    count = np.zeros((B, N), dtype=np.int32)
+    pos = np.zeros((B, N), dtype=np.int32)  # by walk position
     bps, groups, walkers = p["bps"], p["groups"], p["walkers"]
     stride = bps * walkers
     for g in range(p["workgroups"]):
@@ -44,7 +44,12 @@ def _visits(p, B, N):
         if slot >= groups:
             continue
         for w in range(walkers):
-            count[slot::groups, k * walkers + w::stride] += 1
+            pos[slot::groups, k * walkers + w::stride] += 1
+    # position n of sample b is row (n + b * skew) mod N
+    count = np.zeros_like(pos)
+    n = np.arange(N)
+    for b in range(B):
+        count[b, (n + b * p["skew"]) % N] = pos[b]
     return count
 
 
@@ -104,6 +109,15 @@ def test_balanced_workgroups_per_sample():
     rows = -(-1560 // (p["bps"] * p["walkers"]))
     assert rows == -(-1560 // (32 * p["walkers"]))
     assert -(-1560 // ((p["bps"] - 1) * p["walkers"])) > rows
+
+
+def test_skewed_walks_in_the_backward_of_many_samples():
+    # one-wavefront backward rows, 16 or more samples: skewed by 97 rows
+    assert A.plan("bwd", 16, 1560, 1536, BF16)["skew"] == 97
+    assert A.plan("bwd", 15, 1560, 1536, BF16)["skew"] == 0
+    # pairs of wavefronts (D = 3072), and the forward: aligned
+    assert A.plan("bwd", 84, 1560, 3072, BF16)["skew"] == 0
+    assert A.plan("fwd", 16, 1560, 1536, BF16)["skew"] == 0
 
 
 def test_plan_validation():
