@@ -548,14 +548,21 @@ ADALN_API int adaln_plan(int which, int64_t B, int64_t N, int64_t D,
                          int dtype, int64_t *out) {
   ADALN_TRY(check_shape(B, N, D, dtype));
   if (out == nullptr) return fail(ADALN_ERR_INVALID, "out is NULL");
-  if (which != 0 && which != 1 && which != 2)
+  if (which < 0 || which > 3)
     return fail(ADALN_ERR_INVALID,
-                "which must be 0 (forward), 1 (fused backward) or 2 "
-                "(finish), got %d",
+                "which must be 0 (forward), 1 (fused backward), 2 (finish) "
+                "or 3 (D-tile grid), got %d",
                 which);
   const int64_t nvec = D / elems_per_vec(dtype);
   StreamPlan sp;
   TilePlan tp;
+  if (which == 3) {
+    const DmodPlan dp = choose_dmod_plan(B, N, nvec);
+    const int64_t v[7] = {dp.d_tiles, dp.n_tile, dp.n_tiles,
+                          (int64_t)dp.d_tiles * dp.n_tiles * B, 256, 0, 0};
+    std::copy(v, v + 7, out);
+    return ok();
+  }
   if (which == 2) {
     // the partial rows each output sums: the fused plan's workgroups per
     // sample, or the D-tile plan's tiles for rows too wide for it

@@ -63,12 +63,16 @@ def _on(device: torch.device, stream):
     allocated: the stream the call's kernels run on.  torch's caching
     allocator hands a freed block only to later allocations on the stream it
     was allocated on, so a workspace dropped when the call returns cannot be
-    reused by another stream while the kernels still write to it."""
-    if stream is None:
-        return torch.cuda.device(device)
-    if not isinstance(stream, torch.cuda.Stream):
-        stream = torch.cuda.ExternalStream(int(stream), device=device)
-    return torch.cuda.stream(stream)
+    reused by another stream while the kernels still write to it.  (When
+    `stream` is the device's current stream, only the device is set.)"""
+    if stream is not None:
+        handle = (stream.cuda_stream if isinstance(stream, torch.cuda.Stream)
+                  else int(stream))
+        if handle != torch.cuda.current_stream(device).cuda_stream:
+            if not isinstance(stream, torch.cuda.Stream):
+                stream = torch.cuda.ExternalStream(handle, device=device)
+            return torch.cuda.stream(stream)
+    return torch.cuda.device(device)
 
 
 def _shape3(x: torch.Tensor) -> Tuple[int, int, int]:
@@ -296,11 +300,13 @@ def plan(which: str, B: int, N: int, D: int, dtype: torch.dtype) -> dict:
     (position n of sample b is row (n + b * skew) mod N).  ``which="finish"``: the launch that
     sums the backward's partial rows: features per column block, wavefronts
     per block, blocks per workgroup, workgroups, threads per workgroup,
-    partial rows summed per output."""
-    codes = {"fwd": 0, "bwd": 1, "finish": 2}
+    partial rows summed per output.  ``which="dmod"``: the (d_tile, n_tile,
+    b) grid of :func:`bwd_dmod` (d_tiles, rows per n_tile, n_tiles,
+    workgroups, threads per workgroup)."""
+    codes = {"fwd": 0, "bwd": 1, "finish": 2, "dmod": 3}
     if which not in codes:
-        raise ValueError(f"which must be 'fwd', 'bwd' or 'finish', got "
-                         f"{which!r}")
+        raise ValueError(f"which must be 'fwd', 'bwd', 'finish' or 'dmod', "
+                         f"got {which!r}")
     out = (ctypes.c_int64 * 7)()
     rc = _lib.load().adaln_plan(codes[which], B, N, D,
                                 _DTYPES.get(dtype, -1), out)
@@ -308,6 +314,9 @@ def plan(which: str, B: int, N: int, D: int, dtype: torch.dtype) -> dict:
     if which == "finish":
         return dict(F=out[0], wpc=out[1], cpb=out[2], workgroups=out[3],
                     threads=out[4], rows=out[5])
+    if which == "dmod":
+        return dict(d_tiles=out[0], n_tile=out[1], n_tiles=out[2],
+                    workgroups=out[3], threads=out[4])
     return dict(V=out[0], waves_per_row=out[1], workgroups=out[2],
                 bps=out[3], groups=out[4], walkers=out[5], skew=out[6])
 

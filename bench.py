@@ -67,6 +67,8 @@ KERNEL_SOURCES = {
     "bwd_fused": ("bwd_fused.hip", "bwd_wide.hip") + _SHARED,
     "bwd_finish": ("dmod.hip",) + _SHARED,
     "bwd": ("bwd_fused.hip", "bwd_wide.hip", "dmod.hip") + _SHARED,
+    "bwd_dx": ("rows.hip",) + _SHARED,
+    "bwd_dmod": ("dmod.hip",) + _SHARED,
 }
 # rocprofv3 kernel-name prefixes of each step component (the fused backward
 # runs one wavefront per row or, for wider rows, pairs of them)
@@ -227,14 +229,21 @@ def workload_name(wl, bucket=None) -> str:
     return wl.name if bucket is None else f"{wl.name}_S{bucket}"
 
 
-def algorithmic_bytes(B, N, D, esize, n_tiles):
-    """Bytes each call must move at minimum (reads + writes)."""
+def algorithmic_bytes(B, N, D, esize, n_tiles, dmod_tiles=0):
+    """Bytes each call must move at minimum (reads + writes); dmod_tiles is
+    the n_tiles of the separate D-tile grid (adaln_bwd_dmod)."""
     T = B * N
     act = T * D * esize          # one [B, N, D] tensor
     stats = 4 * T                # one [B, N] float32 vector
     mod = B * D * esize          # one [B, D] modulation vector
     part = 2 * B * n_tiles * D * 4
+    dpart = 2 * B * dmod_tiles * D * 4
     return {
+        # the unfused backward: dx (read dy, x, stats, scale; write dx) and
+        # the D-tile grid (read x, dy, stats; write, then read, its partial
+        # sums; write dscale, dshift)
+        "bwd_dx": 3 * act + mod + 2 * stats,
+        "bwd_dmod": 2 * act + 2 * stats + 2 * dpart + 2 * B * D * 4,
         # read x, scale, shift; write y, mean, rstd
         "fwd": 2 * act + 2 * mod + 2 * stats,
         # read dy, x, scale, mean, rstd; write dx and the partial sums
@@ -419,7 +428,8 @@ def make_job(A, torch, inp, dev, esize):
     job["shape"] = (B, N, D)
     job["tokens"] = B * N
     part_rows = A.bwd_fused_plan(B, N, D, dt)["partial_rows"]
-    job["bytes"] = algorithmic_bytes(B, N, D, esize, part_rows)
+    job["bytes"] = algorithmic_bytes(
+        B, N, D, esize, part_rows, A.plan("dmod", B, N, D, dt)["n_tiles"])
     return job
 
 
@@ -709,6 +719,11 @@ def main(argv=None) -> int:
     ap.add_argument("--bucket", type=int, default=None, metavar="S",
                     help="mixed_schedule: run only the buckets of length S "
                          "(one shape), as a single-shape workload")
+    ap.add_argument("--unfused", action="store_true",
+                    help="batched workloads: the backward as the pages' "
+                         "separate kernels (adaln_bwd_dx, then adaln_bwd_dmod:"
+                         " the (d_tile, n_tile) grid and its second stage) "
+                         "instead of the fused single pass")
     ap.add_argument("--unpacked", action="store_true",
                     help="packed workloads: run the samples as batched "
                          "calls, one per segment length, instead")
@@ -835,7 +850,12 @@ def main(argv=None) -> int:
         first_inp = synth.make_inputs(wl, seed=args.seed)
         order = [make_job(A, torch, first_inp, dev, esize)]
 
-    names = ("fwd", "bwd") if packed else ("fwd", "bwd_fused", "bwd_finish")
+    if packed:
+        names = ("fwd", "bwd")
+    elif args.unfused:
+        names = ("fwd", "bwd_dx", "bwd_dmod")
+    else:
+        names = ("fwd", "bwd_fused", "bwd_finish")
 
     def job_calls(job):
         """The calls of one job's forward + backward, in order."""
@@ -850,6 +870,18 @@ def main(argv=None) -> int:
                     job["rstd"], job["table"], dx=job["dx"],
                     dscale=job["dscale"], dshift=job["dshift"],
                     workspace=job["ws"], stream=stream)]
+        if args.unfused:
+            return [
+                lambda: A.fwd(job["x"], job["scale"], job["shift"],
+                              y=job["y"], mean=job["mean"], rstd=job["rstd"],
+                              stream=stream),
+                lambda: A.bwd_dx(job["dy"], job["x"], job["scale"],
+                                 job["mean"], job["rstd"], dx=job["dx"],
+                                 stream=stream),
+                lambda: A.bwd_dmod(job["dy"], job["x"], job["mean"],
+                                   job["rstd"], dscale=job["dscale"],
+                                   dshift=job["dshift"], workspace=job["ws"],
+                                   stream=stream)]
         return [
             lambda: A.fwd(job["x"], job["scale"], job["shift"], y=job["y"],
                           mean=job["mean"], rstd=job["rstd"], stream=stream),
@@ -879,7 +911,8 @@ def main(argv=None) -> int:
     # inside the timed region with one event on each side; events on every
     # kernel boundary cost about 2% of the step (each record is a marker with
     # a cache flush), so the full per-kernel breakdown runs after it.
-    dom = names.index("bwd" if packed else "bwd_fused")
+    dom = names.index("bwd" if packed else
+                      "bwd_dx" if args.unfused else "bwd_fused")
 
     def new_events():
         return [[[torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)]
@@ -1009,6 +1042,10 @@ def main(argv=None) -> int:
     if probe is not None:
         probe["kernel_frac_of_probe"] = round(achieved / probe["gbps"], 4)
         roofline["achievable_probe"] = probe
+    if args.unfused and not packed:
+        config_backward = "unfused: dx kernel, then the (d_tile, n_tile) grid"
+    else:
+        config_backward = None
     if wl in synth.PACKED:
         config = {"workload": wl.name, "layout": "batched per length"
                   if args.unpacked else "packed", "segments": len(lengths),
@@ -1027,6 +1064,8 @@ def main(argv=None) -> int:
         config = {"workload": wl.name, "B": B, "N": N, "D": D,
                   "dtype": wl.dtype}
 
+    if config_backward:
+        config["backward"] = config_backward
     cpu = None
     if args.cpu_budget > 0 and first_inp is not None:
         log(f"cpu baseline: oracle for ~{args.cpu_budget:.0f} s")

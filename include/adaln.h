@@ -205,6 +205,12 @@ int adaln_bwd_fused_plan(int64_t B, int64_t N, int64_t D, int dtype,
  * + g / 8.  The j-th wpc wavefronts of a workgroup serve its j-th block;
  * wavefront s of them sums the rows [s * P / wpc, (s + 1) * P / wpc).
  * out[6] is 0.
+ *
+ * which = 3: the (d_tile, n_tile, b) grid of adaln_bwd_dmod's first launch.
+ * Fills out[0..6] with {d_tiles (64 vectors of features each), rows per
+ * n_tile, n_tiles per sample, workgroups d_tiles * n_tiles * B, threads per
+ * workgroup, 0, 0}; its partial sums occupy 2 * B * n_tiles * D floats of
+ * the workspace, which the second launch sums over the n_tiles.
  */
 int adaln_plan(int which, int64_t B, int64_t N, int64_t D, int dtype,
                int64_t *out);

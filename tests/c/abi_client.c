@@ -62,7 +62,9 @@ int main(void)
         CHECK(p[1] == 1 && p[6] == 97);
         CHECK(adaln_plan(2, 1, 75600, 5120, ADALN_BF16, p) == ADALN_OK);
         CHECK(p[0] == 32 && p[5] == 511 && p[4] == p[1] * p[2] * 64);
-        CHECK(adaln_plan(3, 1, 75600, 5120, ADALN_BF16, p) == ADALN_ERR_INVALID);
+        CHECK(adaln_plan(3, 1, 75600, 5120, ADALN_BF16, p) == ADALN_OK);
+        CHECK(p[0] == 10 && p[3] == p[0] * p[2] && p[1] * p[2] >= 75600);
+        CHECK(adaln_plan(4, 1, 75600, 5120, ADALN_BF16, p) == ADALN_ERR_INVALID);
     }
     /* an invalid call enqueues nothing and explains itself */
     CHECK(adaln_fwd(NULL, NULL, NULL, NULL, NULL, NULL, 1, 1, 64, 9, NULL) ==

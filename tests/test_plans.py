@@ -120,6 +120,21 @@ def test_skewed_walks_in_the_backward_of_many_samples():
     assert A.plan("fwd", 16, 1560, 1536, BF16)["skew"] == 0
 
 
+@pytest.mark.parametrize("B,N,D,dt", _shapes(11, 100))
+def test_dtile_grid_covers_every_row_and_feature(B, N, D, dt):
+    """The (d_tile, n_tile, b) grid of adaln_bwd_dmod: d_tiles of 64
+    vectors cover the row, n_tiles of n_tile rows cover the sample, one
+    workgroup per (d_tile, n_tile, b), and its partial sums fit the
+    workspace."""
+    p = A.plan("dmod", B, N, D, dt)
+    nvec = D // (8 if dt is BF16 else 4)
+    assert p["d_tiles"] == -(-nvec // 64)
+    assert p["n_tile"] % 16 == 0 and p["n_tile"] >= 16
+    assert p["n_tile"] * p["n_tiles"] >= N > p["n_tile"] * (p["n_tiles"] - 1)
+    assert p["workgroups"] == p["d_tiles"] * p["n_tiles"] * B
+    assert A.bwd_workspace_bytes(B, N, D, dt) >= 2 * B * p["n_tiles"] * D * 4
+
+
 def test_plan_validation():
     with pytest.raises(A.AdalnError):
         A.plan("fwd", 1, 1, 12, BF16)          # D not a multiple of 8
