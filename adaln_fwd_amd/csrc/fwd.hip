@@ -151,6 +151,14 @@ __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void fwd_stream_kernel(
   });
 }
 
+// Rows in flight per wavefront of the tile kernel: two, except for the
+// 8-vector bfloat16 rows (up to 4096 vectors), whose second row in flight
+// does not fit the register budget of two wavefronts per SIMD.
+template <typename T, int V>
+constexpr int fwd_tile_pf() {
+  return (V >= 8 && Elems<T>::value == 8) ? 1 : 2;
+}
+
 template <typename T, int V, bool FULL, class Map>
 __global__ __launch_bounds__(kMaxRowWaves * kWave)
 __attribute__((amdgpu_waves_per_eu(fwd_waves_per_simd(V)))) void fwd_tile_kernel(
@@ -266,7 +274,13 @@ __attribute__((amdgpu_waves_per_eu(fwd_waves_per_simd(V)))) void fwd_tile_kernel
     // Steady state: A holds row n and rows n+1, n+2 exist, so every load in
     // the loop body is unconditional; the last one or two rows follow it.
     int n = k_in;
-    if (n < N) {
+    if constexpr (fwd_tile_pf<T, V>() == 1) {
+      for (; n < N; n += bps) {
+        Vec xv[V];
+        load_row(xv, n);
+        do_row(xv, n);
+      }
+    } else if (n < N) {
       const int stride = bps;
       Vec xa[V], xb[V];
       load_row(xa, n);

@@ -1,9 +1,8 @@
 """Register budget of the streaming kernels, checked at build time without a
 GPU: hipcc's kernel resource-usage remarks for gfx950 must show no register
-spills in any row-stream forward instantiation and at most a few spilled
-registers (outside the row loop's working set) in the backward ones.  A
-spill inside the row loop costs more than anything else in these kernels
-(it turned a 32 us forward into a 52 us one)."""
+spills in any forward or fused-backward instantiation.  A spill inside the
+row loop costs more than anything else in these kernels (it turned a 32 us
+forward into a 52 us one)."""
 
 import os
 import re
@@ -54,12 +53,12 @@ def test_forward_stream_kernels_do_not_spill(usage):
     assert not spills, spills
 
 
-def test_backward_stream_kernels_spill_at_most_a_few(usage):
+def test_backward_stream_kernels_do_not_spill(usage):
     stream = {k: v for k, v in usage["bwd_fused.hip"].items()
               if "bwd_stream_kernel" in k}
     assert len(stream) >= 32
-    worst = max(stream.values())
-    assert worst <= 8, {k: v for k, v in stream.items() if v}
+    spills = {k: v for k, v in stream.items() if v}
+    assert not spills, spills
 
 
 def test_wide_backward_kernels_do_not_spill(usage):
@@ -70,13 +69,11 @@ def test_wide_backward_kernels_do_not_spill(usage):
     assert not spills, spills
 
 
-def test_forward_tile_kernels_spill_only_at_the_widest_bf16(usage):
-    """The tile forward (rows past 1024 vectors) spills only in its 8-vector
-    bf16 instantiations, which serve the widest rows (3585-4096 vectors)
-    alone: two wavefronts per SIMD are the least its 8-wavefront workgroups
-    run at."""
+def test_forward_tile_kernels_do_not_spill(usage):
+    """The tile forward (rows past 1024 vectors), the widest 8-vector bf16
+    rows included: they keep one row in flight instead of two."""
     tile = {k: v for k, v in usage["fwd.hip"].items()
             if "fwd_tile_kernel" in k}
     assert len(tile) >= 20
-    spills = {k: v for k, v in tile.items() if v and "4bf16ELi8E" not in k}
+    spills = {k: v for k, v in tile.items() if v}
     assert not spills, spills
