@@ -30,8 +30,8 @@ Prints one JSON line:
                 on the current kernel sources, else null
   cpu_baseline  the float64 CPU oracle on a bounded sample of the same
                 workload, on this host's cores
-  cold          with --cold: each call timed alone after a 1 GiB write that
-                evicts the caches (median, p10, p90)
+  cold          each call timed alone after a 1 GiB write that evicts the
+                caches, up to 20 times (median, p10, p90; --no-cold skips it)
 Other modes print their own JSON line: --cost-model (shape benchmark and
 cost-model fit of the bucket scheduler), --eager-reference (PyTorch's unfused
 chain beside this library), --copy-probe, --traffic-from.
@@ -117,6 +117,10 @@ def probe_lib():
         lib.bench_stream_probe.argtypes = [ctypes.c_int, vp, vp, vp,
                                            ctypes.c_int64, vp]
         lib.bench_stream_probe.restype = ctypes.c_int
+        i = ctypes.c_int
+        lib.bench_window_probe.argtypes = [i, vp, vp, vp, i, i, i, i, i, i,
+                                           vp]
+        lib.bench_window_probe.restype = ctypes.c_int
         _probe_lib = lib
     return _probe_lib
 
@@ -138,6 +142,29 @@ def run_probe(kind: int, a, dst, b=None, stream=None) -> None:
                                         dst.data_ptr(), n, s)
     if rc != 0:
         raise ValueError(f"bench_stream_probe: code {rc}")
+
+
+def run_window_probe(kind: int, a, dst, B: int, N: int, row_kib: int,
+                     bps: int, grid: int, skew: int = 0, b=None,
+                     stream=None) -> None:
+    """Enqueue the windowed walk of bench_window_probe on byte tensors of
+    B * N * row_kib KiB each: B sample windows of bps workgroups, `grid`
+    workgroups, sample s's walk starting (s * skew) % N rows in."""
+    import torch
+    n = B * N * row_kib * 1024
+    for t in (a, dst, b):
+        if t is not None and (t.device.type != "cuda" or
+                              not t.is_contiguous() or
+                              t.numel() * t.element_size() != n):
+            raise ValueError("window probe buffers: contiguous GPU tensors "
+                             "of B * N * row_kib KiB")
+    s = (stream or torch.cuda.current_stream(a.device)).cuda_stream
+    rc = probe_lib().bench_window_probe(
+        int(kind), a.data_ptr(), None if b is None else b.data_ptr(),
+        dst.data_ptr(), int(B), int(N), int(row_kib), int(bps), int(grid),
+        int(skew), s)
+    if rc != 0:
+        raise ValueError(f"bench_window_probe: code {rc}")
 
 
 def kernel_source_hash(kernel: str = None) -> str:
@@ -676,28 +703,62 @@ def stream_probe(args) -> int:
         print("--probe takes a workload with one shape", file=sys.stderr)
         return 2
     esize = 4 if wl.dtype == "f32" else 2
-    n = wl.B * wl.N * wl.D * esize // 10240 * 10240
-    a = torch.empty(n, dtype=torch.uint8, device="cuda").random_()
-    b = torch.empty_like(a).random_()
-    d = torch.empty_like(a)
+    full = wl.B * wl.N * wl.D * esize
+    n = full // 10240 * 10240
+    fa = torch.empty(full, dtype=torch.uint8, device="cuda").random_()
+    fb = torch.empty_like(fa).random_()
+    fd = torch.empty_like(fa)
+    a, b, d = fa[:n], fb[:n], fd[:n]
     out = {"probe": "bench_stream_probe", "workload": wl.name,
            "buffer_bytes": n}
-    for kind, name, streams in ((0, "copy", 2), (1, "read2_write1", 3)):
+
+    def timed(launch, nbytes, streams):
         for _ in range(args.warmup or 1):
-            run_probe(kind, a, d, b=b)
+            launch()
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         torch.cuda.synchronize()
         ev[0].record()
         for _ in range(args.steps):
-            run_probe(kind, a, d, b=b)
+            launch()
         ev[1].record()
         torch.cuda.synchronize()
         ms = ev[0].elapsed_time(ev[1]) / args.steps
-        out[name] = {"avg_ms": round(ms, 5),
-                     "gbps": round(streams * n / (ms * 1e-3) / 1e9, 1)}
-    ok = bool(torch.equal(d, a ^ b))
-    out["read2_write1"]["result_ok"] = ok
+        return {"avg_ms": round(ms, 5),
+                "gbps": round(streams * nbytes / (ms * 1e-3) / 1e9, 1)}
+
+    for kind, name, streams in ((0, "copy", 2), (1, "read2_write1", 3)):
+        out[name] = timed(lambda: run_probe(kind, a, d, b=b), n, streams)
+    out["read2_write1"]["result_ok"] = bool(torch.equal(d, a ^ b))
+
+    # The same bytes walked in the kernels' sample windows (grid and bps of
+    # the forward's plan for the copy, of the backward's for two reads + one
+    # write), at several skews, beside one flat window over the batch.
+    row = wl.D * esize
+    if row % 1024 == 0 and 1 <= row // 1024 <= 10:
+        rk = row // 1024
+        dt = torch.float32 if wl.dtype == "f32" else torch.bfloat16
+        wins = []
+        for kind, name, streams, op in ((0, "copy", 2, "fwd"),
+                                        (1, "read2_write1", 3, "bwd")):
+            pl = A.plan(op, wl.B, wl.N, wl.D, dt)
+            grid, bps = pl["workgroups"], pl["bps"]
+            cases = [(1, wl.B * wl.N, grid, 0)]
+            if wl.B > 1:
+                cases += [(wl.B, wl.N, bps, sk)
+                          for sk in sorted({0, 64, 97, pl.get("skew", 0)})]
+            for B_, N_, bps_, sk in cases:
+                r = timed(lambda: run_window_probe(kind, fa, fd, B_, N_, rk,
+                                                   bps_, grid, sk, b=fb),
+                          full, streams)
+                r.update({"pattern": name, "windows": B_, "grid": grid,
+                          "bps": bps_, "skew": sk})
+                want = fa ^ fb if kind == 1 else fa
+                r["result_ok"] = bool(torch.equal(fd, want))
+                wins.append(r)
+        out["windows"] = wins
     print(json.dumps(out), flush=True)
+    ok = out["read2_write1"]["result_ok"] and all(
+        w["result_ok"] for w in out.get("windows", []))
     return 0 if ok else 1
 
 
@@ -727,9 +788,14 @@ def main(argv=None) -> int:
     ap.add_argument("--unpacked", action="store_true",
                     help="packed workloads: run the samples as batched "
                          "calls, one per segment length, instead")
-    ap.add_argument("--cold", action="store_true",
-                    help="also time each call after evicting the caches "
-                         "(reported under 'cold'; single-call workloads)")
+    ap.add_argument("--cold", dest="cold", action="store_true",
+                    default=True,
+                    help="also time each call after evicting the caches, "
+                         "up to 20 times each, after the timed region "
+                         "(reported under 'cold'; single-call workloads; "
+                         "the default)")
+    ap.add_argument("--no-cold", dest="cold", action="store_false",
+                    help="skip the cold-cache timings")
     ap.add_argument("--cost-model", action="store_true",
                     help="shape benchmark of the synthetic step, cost-model "
                          "fit and bucket policies (--steps/--warmup per shape)")
@@ -740,7 +806,8 @@ def main(argv=None) -> int:
     ap.add_argument("--probe", action="store_true",
                     help="time the streaming probes of bench_probe.hip (copy; "
                          "2 reads + 1 write) on buffers of the workload's "
-                         "activation size")
+                         "activation size, flat and in the kernels' sample "
+                         "windows")
     ap.add_argument("--copy-probe", action="store_true",
                     help="time torch's device copy of one workload-sized "
                          "tensor instead (achievable-bandwidth reference and "
@@ -973,7 +1040,7 @@ def main(argv=None) -> int:
         scrub = torch.empty(1 << 28, dtype=torch.float32, device=dev)
         per = {n: [] for n in names}
         cev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-        for _ in range(args.steps):
+        for _ in range(min(args.steps, 20)):
             for i, n in enumerate(names):
                 scrub.fill_(1.0)
                 cev[0].record(stream)
