@@ -148,19 +148,20 @@ DmodPlan choose_dmod_plan(int64_t B, int64_t N, int64_t nvec) {
   return p;
 }
 
-// Row-stream plans (rows of up to 1024 vectors for the forward, 1280 for the
-// backward, which takes a pair of wavefronts per row past 320).  V is the
-// smallest instantiated count that holds the row.  The kernel's occupancy OCC
-// fixes a persistent grid of G = 256 * OCC workgroups (OCC per CU on a
-// 256-CU MI355X), spread over the samples: up to G / B workgroups per sample
-// (at least one), `groups` = G / bps samples in flight.  Of the counts that
-// keep the most rows any row walker (a wavefront, or a pair of them) visits
-// as low as G / B does, bps is the smallest, so that all walkers finish
-// together rather than a few walking one row more (measured on MI355X: the
-// 16 x 1560-token, D = 1536 backward 1% faster).  The plan depends only on
-// the shape, so the workspace size ([B, bps, D] partial sums of the
-// backward) is a pure function of it; on a part with another CU count the
-// kernels remain correct and only use the GPU less evenly.
+// Row-stream plans (rows of up to 1024 vectors for the forward, 2560 for the
+// backward, which takes a pair of wavefronts per row past 320 and four past
+// 1280).  V is the smallest instantiated count that holds the row.  The
+// kernel's occupancy OCC fixes a persistent grid of G = 256 * OCC workgroups
+// (OCC per CU on a 256-CU MI355X), spread over the samples: up to G / B
+// workgroups per sample (at least one), `groups` = G / bps samples in
+// flight.  Of the counts that keep the most rows any row walker (a
+// wavefront, or the W wavefronts sharing a row) visits as low as G / B does,
+// bps is the smallest, so that all walkers finish together rather than a few
+// walking one row more (measured on MI355X: the 16 x 1560-token, D = 1536
+// backward 1% faster).  The plan depends only on the shape, so the workspace
+// size ([B, bps, D] partial sums of the backward) is a pure function of it;
+// on a part with another CU count the kernels remain correct and only use
+// the GPU less evenly.
 #ifndef ADALN_FWD_MIN_BPS
 #define ADALN_FWD_MIN_BPS 1
 #endif
@@ -199,13 +200,17 @@ bool choose_stream_plan(int64_t B, int64_t N, int64_t nvec, bool bwd,
   ADALN_STREAM_V(ADALN_STREAM_PLAN_CASE)
 #undef ADALN_STREAM_PLAN_CASE
   if (bwd && (p.V == 0 || p.V > kMaxBwdStreamV)) {
-    // too wide for one wavefront's registers: a pair of wavefronts per row
+    // too wide for one wavefront's registers: a pair of wavefronts per row,
+    // or a quad past 1280 vectors
     p.V = 0;
-#define ADALN_WIDE_PLAN_CASE(V_) \
-  if (p.V == 0 && (int64_t)kWideWaves * 64 * V_ >= nvec) p.V = V_;
-    ADALN_BWD_WIDE_V(ADALN_WIDE_PLAN_CASE)
-#undef ADALN_WIDE_PLAN_CASE
-    p.W = kWideWaves;
+#define ADALN_PAIR_PLAN_CASE(V_) \
+  if (p.V == 0 && (int64_t)2 * 64 * V_ >= nvec) p.V = V_, p.W = 2;
+    ADALN_BWD_PAIR_V(ADALN_PAIR_PLAN_CASE)
+#undef ADALN_PAIR_PLAN_CASE
+#define ADALN_QUAD_PLAN_CASE(V_) \
+  if (p.V == 0 && (int64_t)4 * 64 * V_ >= nvec) p.V = V_, p.W = 4;
+    ADALN_BWD_QUAD_V(ADALN_QUAD_PLAN_CASE)
+#undef ADALN_QUAD_PLAN_CASE
   }
   if (p.V == 0) return false;
   if (B > 0 && N > 0) {
@@ -229,7 +234,7 @@ bool choose_stream_plan(int64_t B, int64_t N, int64_t nvec, bool bwd,
       }
     }
     if (bps < min_bps) bps = min_bps < G ? min_bps : G;
-    const int64_t walkers = p.W > 1 ? 2 : 4;  // row walkers per workgroup
+    const int64_t walkers = 4 / p.W;  // row walkers per workgroup
     const int64_t most = (N + walkers * bps - 1) / (walkers * bps);
     const int64_t even = (N + walkers * most - 1) / (walkers * most);
     if (even >= min_bps && even < bps) bps = even;
@@ -767,7 +772,7 @@ ADALN_API int adaln_bwd_segments(const void *dy, const void *x,
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = hipSuccess;
   if (rows)
-    e = sp.W > 1 ? launch_bwd_wide_segments(dtype, sp.V, map, dy, x, scale,
+    e = sp.W > 1 ? launch_bwd_wide_segments(dtype, sp, map, dy, x, scale,
                                             mean, rstd, dx, part_scale,
                                             part_shift, (int32_t)D, s)
                  : launch_bwd_segments(dtype, sp.V, map, dy, x, scale, mean,

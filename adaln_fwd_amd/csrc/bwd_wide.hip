@@ -1,43 +1,39 @@
-// Fused backward for rows of 321 to 1280 16-byte vectors (bf16 D of 2568 to
-// 10240, f32 D of 1284 to 5120): dx and the D-tile partial sums of
+// Fused backward for rows of 321 to 2560 16-byte vectors (bf16 D of 2568 to
+// 20480, f32 D of 1284 to 10240): dx and the D-tile partial sums of
 // dscale/dshift in one pass over x and dy, like bwd_stream_kernel, with each
-// row split between two wavefronts.
+// row split between W = 2 or 4 wavefronts.
 //
 // A row held in one wavefront together with its per-lane accumulators (2
 // floats per element it owns) takes the whole register file from 640
 // vectors up, and outgrows it past that; from 321 vectors up it already
 // leaves room for one wavefront per SIMD only, with nothing to cover memory
-// latency.  Here the four wavefronts of a workgroup form two pairs; a pair
-// shares a row, wavefront h of the pair owning the contiguous vectors
-// [h*V*64, (h+1)*V*64) (lane l: vector (h*V + k)*64 + l), so each keeps the
-// registers of half the row: two wavefronts per SIMD for rows of up to 640
-// vectors, one for wider ones.  The two row sums of dx
-// (of g and of g*xhat) are combined through LDS: each wavefront reduces its
-// half with DPP, lane 0 stores the two values, one barrier, and both read the
-// pair's two halves and add them in half order.  The store area is
-// double-buffered by iteration parity, so one barrier per row step
-// suffices: a wavefront can reuse a buffer only after every wavefront has
-// passed the next barrier, that is after it has read the buffer.
+// latency.  Here the four wavefronts of a workgroup form 4 / W row groups
+// (two pairs, or one quad); wavefront h of a group owns the contiguous
+// vectors [h*V*64, (h+1)*V*64) of the group's row (lane l: vector
+// (h*V + k)*64 + l), so each keeps the registers of 1/W of the row: pairs
+// take rows of up to 1280 vectors (two wavefronts per SIMD up to 640), quads
+// up to 2560.  The two row sums of dx (of g and of g*xhat) are combined
+// through LDS: each wavefront reduces its part with DPP, lane 0 stores the
+// two values, one barrier, and every wavefront of the group reads the W
+// parts and adds them in part order.  The store area is double-buffered by
+// iteration parity, so one barrier per row step suffices: a wavefront can
+// reuse a buffer only after every wavefront has passed the next barrier,
+// that is after it has read the buffer.
 //
 // As in the D-tile reduction of the AdaptiveLoad technical summary (section
 // 2.B, backward pass), every lane stays pinned to its features for all the
 // rows it visits and accumulates dy*xhat and dy in float32.  At the end of a
-// segment the two pairs' accumulators (same features, different rows) are
-// added in pair order through LDS and written as one partial row per
-// (segment, workgroup) -- the workspace layout of bwd_stream_kernel, summed
-// by the same finishing kernels.  Fixed-order sums only; no atomics.
+// segment the pairs' accumulators (same features, different rows) are added
+// in pair order through LDS -- a quad owns all of its workgroup's rows and
+// needs no such step -- and written as one partial row per (segment,
+// workgroup): the workspace layout of bwd_stream_kernel, summed by the same
+// finishing kernels.  Fixed-order sums only; no atomics.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace adaln {
 
-namespace {
-
-constexpr int kPairs = 2;  // rows a workgroup works on at a time
-
-}  // namespace
-
-template <typename T, int V, bool FULL, class Map>
+template <typename T, int V, int W, int PF, bool SPLIT, bool FULL, class Map>
 __global__ __launch_bounds__(kBlock)
 __attribute__((amdgpu_waves_per_eu(bwd_wide_occ(V), bwd_wide_occ(V)))) void
 bwd_wide_kernel(
@@ -46,13 +42,15 @@ bwd_wide_kernel(
     const float *__restrict__ rstd, T *__restrict__ dx,
     float *__restrict__ part_scale, float *__restrict__ part_shift,
     int32_t D, Map map) {
+  static_assert(W == 2 || W == 4, "a row takes two or four wavefronts");
   constexpr int E = Elems<T>::value;
-  extern __shared__ float stage[];  // [half][value][lane], one quantity
-  __shared__ float sums[2][kPairs][2][2];  // [parity][pair][half][s1, s2]
+  constexpr int kRows = kBlock / kWave / W;  // rows a workgroup works on
+  extern __shared__ float stage[];  // [part][value][lane], one quantity
+  __shared__ float sums[2][kRows][W][2];  // [parity][group][part][s1, s2]
   const int lane = lane_id();
   const int wave = wave_id();
-  const int pair = wave >> 1;
-  const int half = wave & 1;
+  const int group = wave / W;  // row group (pair or quad) of this wavefront
+  const int part = wave % W;   // its part of the group's row
   const int nvec = D / E;
   const float inv_d = 1.0f / (float)D;
 
@@ -60,7 +58,7 @@ bwd_wide_kernel(
   bool ok[V];
 #pragma unroll
   for (int k = 0; k < V; ++k) {
-    jv[k] = (half * V + k) * kWave + lane;
+    jv[k] = (part * V + k) * kWave + lane;
     ok[k] = FULL || jv[k] < nvec;
   }
 
@@ -69,8 +67,8 @@ bwd_wide_kernel(
   // from row row0 + rot (the planner keeps rot = 0 for this kernel); this
   // workgroup is number k_in of bps and writes partial row part_row.  Every
   // wavefront of the workgroup runs the same number of loop iterations
-  // (barriers below); a pair without a row in the last one only takes part
-  // in its barrier.
+  // (barriers below); a row group without a row in the last one only takes
+  // part in its barrier.
   for_each_segment(map, [&](int64_t row0, int N, int mod, int k_in, int bps,
                             int part_row, int rot) {
     // row of the segment that the walk's n-th position stands for
@@ -78,7 +76,7 @@ bwd_wide_kernel(
       const int p = n + rot;
       return row0 + (p >= N ? p - N : p);
     };
-    const int stride = bps * kPairs;
+    const int stride = bps * kRows;
     Vec sv[V];
 #pragma unroll
     for (int k = 0; k < V; ++k)
@@ -91,24 +89,31 @@ bwd_wide_kernel(
 #pragma unroll
       for (int e = 0; e < E; ++e) acc_s[k][e] = acc_h[k][e] = 0.f;
 
-    const int first = k_in * kPairs;
-    const int iters = first < N ? (N - 1 - first) / stride + 1 : 0;
-#pragma unroll 1
-    for (int it = 0; it < iters; ++it) {
-      const int n = first + pair + it * stride;
-      const bool live = n < N;  // uniform across the wavefront
-      const int64_t off = at(n) * D;
-      Vec xv[V], gv[V];
-      float mu = 0.f, r = 0.f, s1 = 0.f, s2 = 0.f;
-      if (live) {
-        mu = mean[at(n)];
-        r = rstd[at(n)];
+    // the next row of this row group is in flight while one is processed
+    // where the registers allow it (PF == 2); load_row skips rows past the
+    // segment's end, do_row computes nothing for them but still takes part
+    // in the barrier
+    auto load_row = [&](Vec (&xv)[V], Vec (&gv)[V], float (&st)[2], int n) {
+      if (n < N) {
+        st[0] = mean[at(n)];
+        st[1] = rstd[at(n)];
+        const int64_t off = at(n) * D;
 #pragma unroll
         for (int k = 0; k < V; ++k) {
           xv[k] = ok[k] ? load_stream(x + off + (int64_t)jv[k] * E) : vzero();
           gv[k] = ok[k] ? load_stream(dy + off + (int64_t)jv[k] * E) : vzero();
         }
-        // this half's sums of g = dy * (1 + scale) and g * xhat (vectors
+      }
+    };
+
+    auto do_row = [&](Vec (&xv)[V], Vec (&gv)[V], const float (&st)[2],
+                      int n) {
+      const bool live = n < N;  // uniform across the wavefront
+      const float mu = st[0];
+      const float r = st[1];
+      float s1 = 0.f, s2 = 0.f;
+      if (live) {
+        // this part's sums of g = dy * (1 + scale) and g * xhat (vectors
         // past the row end hold dy = 0, so g = 0 there)
 #pragma unroll
         for (int k = 0; k < V; ++k) {
@@ -123,17 +128,23 @@ bwd_wide_kernel(
         wave_sum2(s1, s2);
       }
       if (lane == 0) {
-        sums[parity][pair][half][0] = s1;
-        sums[parity][pair][half][1] = s2;
+        sums[parity][group][part][0] = s1;
+        sums[parity][group][part][1] = s2;
       }
       __syncthreads();
       if (live) {
-        const float c1 =
-            (sums[parity][pair][0][0] + sums[parity][pair][1][0]) * inv_d;
-        const float c2 =
-            (sums[parity][pair][0][1] + sums[parity][pair][1][1]) * inv_d;
+        float t1 = sums[parity][group][0][0];
+        float t2 = sums[parity][group][0][1];
+#pragma unroll
+        for (int h = 1; h < W; ++h) {
+          t1 += sums[parity][group][h][0];
+          t2 += sums[parity][group][h][1];
+        }
+        const float c1 = t1 * inv_d;
+        const float c2 = t2 * inv_d;
 #pragma unroll
         for (int k = 0; k < V; ++k) opaque(xv[k]), opaque(gv[k]);
+        const int64_t off = at(n) * D;
 #pragma unroll
         for (int k = 0; k < V; ++k) {
           if (ok[k]) {
@@ -152,39 +163,144 @@ bwd_wide_kernel(
         }
       }
       parity ^= 1;
+    };
+
+    // every wavefront of the workgroup runs `iters` row steps
+    const int first = k_in * kRows + group;
+    const int iters =
+        k_in * kRows < N ? (N - 1 - k_in * kRows) / stride + 1 : 0;
+    if constexpr (PF == 1 && SPLIT) {
+#pragma unroll 1
+      for (int it = 0; it < iters; ++it) {
+        Vec xv[V], gv[V];
+        float st[2] = {0.f, 0.f};
+        load_row(xv, gv, st, first + it * stride);
+        do_row(xv, gv, st, first + it * stride);
+      }
+    } else if constexpr (PF == 1) {
+      // the same steps with the loads and the first pass in one branch
+      // (the compiler schedules the two forms differently; which is faster
+      // depends on the row width)
+#pragma unroll 1
+      for (int it = 0; it < iters; ++it) {
+        const int n = first + it * stride;
+        const bool live = n < N;  // uniform across the wavefront
+        const int64_t off = at(n) * D;
+        Vec xv[V], gv[V];
+        float mu = 0.f, r = 0.f, s1 = 0.f, s2 = 0.f;
+        if (live) {
+          mu = mean[at(n)];
+          r = rstd[at(n)];
+#pragma unroll
+          for (int k = 0; k < V; ++k) {
+            xv[k] = ok[k] ? load_stream(x + off + (int64_t)jv[k] * E) : vzero();
+            gv[k] =
+                ok[k] ? load_stream(dy + off + (int64_t)jv[k] * E) : vzero();
+          }
+#pragma unroll
+          for (int k = 0; k < V; ++k) {
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+              const float xh = (elem<T>(xv[k], e) - mu) * r;
+              const float g = elem<T>(gv[k], e) * (1.0f + elem<T>(sv[k], e));
+              s1 += g;
+              s2 = fmaf(g, xh, s2);
+            }
+          }
+          wave_sum2(s1, s2);
+        }
+        if (lane == 0) {
+          sums[parity][group][part][0] = s1;
+          sums[parity][group][part][1] = s2;
+        }
+        __syncthreads();
+        if (live) {
+          float t1 = sums[parity][group][0][0];
+          float t2 = sums[parity][group][0][1];
+#pragma unroll
+          for (int h = 1; h < W; ++h) {
+            t1 += sums[parity][group][h][0];
+            t2 += sums[parity][group][h][1];
+          }
+          const float c1 = t1 * inv_d;
+          const float c2 = t2 * inv_d;
+#pragma unroll
+          for (int k = 0; k < V; ++k) opaque(xv[k]), opaque(gv[k]);
+#pragma unroll
+          for (int k = 0; k < V; ++k) {
+            if (ok[k]) {
+              float o[E];
+#pragma unroll
+              for (int e = 0; e < E; ++e) {
+                const float xh = (elem<T>(xv[k], e) - mu) * r;
+                const float gy = elem<T>(gv[k], e);
+                const float g = gy * (1.0f + elem<T>(sv[k], e));
+                o[e] = r * fmaf(-xh, c2, g - c1);
+                acc_s[k][e] = fmaf(gy, xh, acc_s[k][e]);
+                acc_h[k][e] += gy;
+              }
+              store_stream(dx + off + (int64_t)jv[k] * E, pack<T>(o));
+            }
+          }
+        }
+        parity ^= 1;
+      }
+    } else if (iters > 0) {
+      Vec xa[V], ga[V], xb[V], gb[V];
+      float sa[2] = {0.f, 0.f}, sb[2] = {0.f, 0.f};
+      int it = 0;
+      load_row(xa, ga, sa, first);
+#pragma unroll 1
+      for (; it + 2 < iters; it += 2) {
+        load_row(xb, gb, sb, first + (it + 1) * stride);
+        do_row(xa, ga, sa, first + it * stride);
+        load_row(xa, ga, sa, first + (it + 2) * stride);
+        do_row(xb, gb, sb, first + (it + 1) * stride);
+      }
+      if (it + 1 < iters) {
+        load_row(xb, gb, sb, first + (it + 1) * stride);
+        do_row(xa, ga, sa, first + it * stride);
+        do_row(xb, gb, sb, first + (it + 1) * stride);
+      } else {
+        do_row(xa, ga, sa, first + it * stride);
+      }
     }
 
-    // Add pair 1's accumulators to pair 0's (same features), one quantity
-    // at a time through LDS ([half][value][lane]), then pair 0 writes the
-    // partial row, each wavefront its half.  The first barrier keeps the
-    // staging area from being overwritten while the previous segment's
-    // values are still being read.
-    float *st = stage + (size_t)half * V * E * kWave;
+    // Pairs: add pair 1's accumulators to pair 0's (same features), one
+    // quantity at a time through LDS ([part][value][lane]), then pair 0
+    // writes the partial row, each wavefront its half.  The first barrier
+    // keeps the staging area from being overwritten while the previous
+    // segment's values are still being read.  A quad holds the workgroup's
+    // only row group and writes its parts directly.
+    if constexpr (kRows == 2) {
+      float *st = stage + (size_t)part * V * E * kWave;
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      __syncthreads();
-      if (pair == 1) {
+      for (int q = 0; q < 2; ++q) {
+        __syncthreads();
+        if (group == 1) {
 #pragma unroll
-        for (int k = 0; k < V; ++k)
+          for (int k = 0; k < V; ++k)
 #pragma unroll
-          for (int e = 0; e < E; ++e)
-            st[(k * E + e) * kWave + lane] = q == 0 ? acc_s[k][e] : acc_h[k][e];
-      }
-      __syncthreads();
-      if (pair == 0) {
+            for (int e = 0; e < E; ++e)
+              st[(k * E + e) * kWave + lane] =
+                  q == 0 ? acc_s[k][e] : acc_h[k][e];
+        }
+        __syncthreads();
+        if (group == 0) {
 #pragma unroll
-        for (int k = 0; k < V; ++k)
+          for (int k = 0; k < V; ++k)
 #pragma unroll
-          for (int e = 0; e < E; ++e) {
-            const float v = st[(k * E + e) * kWave + lane];
-            if (q == 0)
-              acc_s[k][e] += v;
-            else
-              acc_h[k][e] += v;
-          }
+            for (int e = 0; e < E; ++e) {
+              const float v = st[(k * E + e) * kWave + lane];
+              if (q == 0)
+                acc_s[k][e] += v;
+              else
+                acc_h[k][e] += v;
+            }
+        }
       }
     }
-    if (pair == 0) {
+    if (group == 0) {
       const int64_t po = (int64_t)part_row * D;
 #pragma unroll
       for (int k = 0; k < V; ++k) {
@@ -207,45 +323,71 @@ bwd_wide_kernel(
 
 namespace {
 
-template <typename T, int V, bool FULL, class Map>
+template <typename T, int V, int W, bool FULL, class Map>
 hipError_t bwd_wide_v(int64_t grid, const Map &map, const void *dy,
                       const void *x, const void *scale, const float *mean,
                       const float *rstd, void *dx, float *part_scale,
                       float *part_shift, int32_t D, hipStream_t s) {
   constexpr int E = Elems<T>::value;
-  const size_t lds = (size_t)kWideWaves * V * E * kWave * sizeof(float);
-  return launch_kernel_lds(bwd_wide_kernel<T, V, FULL, Map>, grid, kBlock,
+  // staging of the pairs' end-of-segment sum: W parts of V*E floats per lane
+  const size_t lds =
+      kBlock / kWave / W == 2 ? (size_t)W * V * E * kWave * sizeof(float) : 0;
+  return launch_kernel_lds(bwd_wide_kernel<T, V, W, bwd_wide_pf(V, E, FULL),
+                                           bwd_wide_split(V, E), FULL, Map>,
+                           grid, kBlock,
                            lds, s, (const T *)dy, (const T *)x,
                            (const T *)scale, mean, rstd, (T *)dx, part_scale,
                            part_shift, D, map);
 }
 
-template <class Map>
-hipError_t bwd_wide_dispatch(int dtype, int V, int64_t grid, const Map &map,
-                             const void *dy, const void *x, const void *scale,
-                             const float *mean, const float *rstd, void *dx,
-                             float *part_scale, float *part_shift, int32_t D,
-                             hipStream_t stream) {
+template <int W, class Map>
+hipError_t bwd_wide_dispatch_w(int dtype, int V, int64_t grid, const Map &map,
+                               const void *dy, const void *x,
+                               const void *scale, const float *mean,
+                               const float *rstd, void *dx, float *part_scale,
+                               float *part_shift, int32_t D,
+                               hipStream_t stream) {
   const int E = dtype == 1 ? 8 : 4;
-  const bool full = (int64_t)V * kWideWaves * kWave * E == D;
+  const bool full = (int64_t)V * W * kWave * E == D;
 #define ADALN_BWD_WIDE_CASE(V_)                                               \
   if (V == V_) {                                                              \
     if (dtype == 1)                                                           \
-      return full ? bwd_wide_v<bf16, V_, true>(grid, map, dy, x, scale, mean, \
-                                               rstd, dx, part_scale,          \
-                                               part_shift, D, stream)         \
-                  : bwd_wide_v<bf16, V_, false>(grid, map, dy, x, scale,      \
-                                                mean, rstd, dx, part_scale,   \
-                                                part_shift, D, stream);       \
-    return full ? bwd_wide_v<float, V_, true>(grid, map, dy, x, scale, mean,  \
-                                              rstd, dx, part_scale,           \
-                                              part_shift, D, stream)          \
-                : bwd_wide_v<float, V_, false>(grid, map, dy, x, scale, mean, \
-                                               rstd, dx, part_scale,          \
-                                               part_shift, D, stream);        \
+      return full ? bwd_wide_v<bf16, V_, W, true>(grid, map, dy, x, scale,    \
+                                                  mean, rstd, dx, part_scale, \
+                                                  part_shift, D, stream)      \
+                  : bwd_wide_v<bf16, V_, W, false>(grid, map, dy, x, scale,   \
+                                                   mean, rstd, dx,            \
+                                                   part_scale, part_shift, D, \
+                                                   stream);                   \
+    return full ? bwd_wide_v<float, V_, W, true>(grid, map, dy, x, scale,     \
+                                                 mean, rstd, dx, part_scale,  \
+                                                 part_shift, D, stream)       \
+                : bwd_wide_v<float, V_, W, false>(grid, map, dy, x, scale,    \
+                                                  mean, rstd, dx, part_scale, \
+                                                  part_shift, D, stream);     \
   }
-  ADALN_BWD_WIDE_V(ADALN_BWD_WIDE_CASE)
+  if constexpr (W == 2) {
+    ADALN_BWD_PAIR_V(ADALN_BWD_WIDE_CASE)
+  } else {
+    ADALN_BWD_QUAD_V(ADALN_BWD_WIDE_CASE)
+  }
 #undef ADALN_BWD_WIDE_CASE
+  return hipErrorInvalidValue;
+}
+
+template <class Map>
+hipError_t bwd_wide_dispatch(int dtype, int V, int W, int64_t grid,
+                             const Map &map, const void *dy, const void *x,
+                             const void *scale, const float *mean,
+                             const float *rstd, void *dx, float *part_scale,
+                             float *part_shift, int32_t D,
+                             hipStream_t stream) {
+  if (W == 2)
+    return bwd_wide_dispatch_w<2>(dtype, V, grid, map, dy, x, scale, mean,
+                                  rstd, dx, part_scale, part_shift, D, stream);
+  if (W == 4)
+    return bwd_wide_dispatch_w<4>(dtype, V, grid, map, dy, x, scale, mean,
+                                  rstd, dx, part_scale, part_shift, D, stream);
   return hipErrorInvalidValue;
 }
 
@@ -257,19 +399,21 @@ hipError_t launch_bwd_wide(int dtype, const StreamPlan &plan, const void *dy,
                            float *part_scale, float *part_shift, int32_t B,
                            int32_t N, int32_t D, hipStream_t stream) {
   const UniformMap map{B, N, plan.bps, plan.groups, plan.skew};
-  return bwd_wide_dispatch(dtype, plan.V, plan.grid, map, dy, x, scale, mean,
-                           rstd, dx, part_scale, part_shift, D, stream);
-}
-
-hipError_t launch_bwd_wide_segments(int dtype, int V, const SegMap &map,
-                                    const void *dy, const void *x,
-                                    const void *scale, const float *mean,
-                                    const float *rstd, void *dx,
-                                    float *part_scale, float *part_shift,
-                                    int32_t D, hipStream_t stream) {
-  return bwd_wide_dispatch(dtype, V, map.wg_start[map.nseg], map, dy, x,
+  return bwd_wide_dispatch(dtype, plan.V, plan.W, plan.grid, map, dy, x,
                            scale, mean, rstd, dx, part_scale, part_shift, D,
                            stream);
+}
+
+hipError_t launch_bwd_wide_segments(int dtype, const StreamPlan &plan,
+                                    const SegMap &map, const void *dy,
+                                    const void *x, const void *scale,
+                                    const float *mean, const float *rstd,
+                                    void *dx, float *part_scale,
+                                    float *part_shift, int32_t D,
+                                    hipStream_t stream) {
+  return bwd_wide_dispatch(dtype, plan.V, plan.W, map.wg_start[map.nseg], map,
+                           dy, x, scale, mean, rstd, dx, part_scale,
+                           part_shift, D, stream);
 }
 
 }  // namespace adaln

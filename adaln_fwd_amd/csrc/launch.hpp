@@ -46,7 +46,7 @@ struct DmodPlan {
 // each wavefront walks its sample's rows with a stride of 4*bps.
 struct StreamPlan {
   int V = 0;       // vectors per lane
-  int W = 1;       // wavefronts per row (2: the backward's wide rows)
+  int W = 1;       // wavefronts per row (2 or 4: the backward's wide rows)
   int grid = 0;
   int bps = 0;     // workgroups per sample (partial rows per sample)
   int groups = 0;  // samples in flight
@@ -161,18 +161,50 @@ constexpr int bwd_stream_occ(int V) {
 }
 // The fused backward keeps per-lane accumulators (2*V*E floats) next to the
 // row.  One wavefront per row (bwd_stream_kernel) holds rows of up to 320
-// vectors.  Wider rows, up to 2 * 640 vectors, split between the two
-// wavefronts of a pair (bwd_wide_kernel), V vectors per lane each; past 1280
-// vectors the accumulators outgrow the register file and the separate dx and
+// vectors.  Wider rows split between the W wavefronts of a row group
+// (bwd_wide_kernel), V vectors per lane each: pairs up to 2 * 640 vectors,
+// quads (W = 4) up to 4 * 640; past 2560 vectors the accumulators outgrow
+// the register file of a four-wavefront workgroup and the separate dx and
 // D-tile kernels take over.  A whole 640-vector row in one wavefront needs
 // the full register file at one wavefront per SIMD, so nothing covers its
 // memory latency while it computes; as halves, rows of up to 640 vectors run
 // at two wavefronts per SIMD (measured on MI355X: the D = 5120 bf16 backward
 // 411 -> 400 us, D = 3072 1-3% faster).
 constexpr int kMaxBwdStreamV = 5;
-constexpr int kWideWaves = 2;
-#define ADALN_BWD_WIDE_V(X) X(3) X(4) X(5) X(6) X(8) X(10)
+#define ADALN_BWD_PAIR_V(X) X(3) X(4) X(5) X(6) X(8) X(10)
+#define ADALN_BWD_QUAD_V(X) X(6) X(8) X(10)
 constexpr int bwd_wide_occ(int V) { return V <= 5 ? 2 : 1; }
+// Rows in flight per wavefront of bwd_wide_kernel (E elements per vector):
+// at one wavefront per SIMD, a second row where its 2*V vectors of x and dy
+// fit beside the accumulators without spills (V*E <= 64 elements; <= 48
+// where the row ends inside a wavefront's vectors and the predicated loads
+// need registers of their own).  Measured on MI355X (fused backward, bf16):
+// D = 6144 288 -> 262 us, D = 8192 471 -> 440 us, D = 12288 555 -> 517 us,
+// D = 16384 586 -> 540 us; f32 within 2%.
+constexpr int bwd_wide_pf(int V, int E, bool full) {
+#ifdef ADALN_BWD_WIDE_PF1
+  return 1;
+#else
+  return bwd_wide_occ(V) == 1 && V * E <= (full ? 64 : 48) ? 2 : 1;
+#endif
+}
+// Loop form of bwd_wide_kernel at one row in flight: the loads as one step
+// and the arithmetic as the next, or both in one branch.  The compiler
+// schedules the two forms differently, and on MI355X neither wins
+// everywhere (fused backward, HIP events): the split form for f32 rows and
+// rows of up to 4 vectors per lane (bf16 84 x 1560 x 3072 463 -> 397-454 us,
+// 4 x 30000 x 2568 446 -> 387-399 us, f32 1 x 120000 x 1288 411 -> 334-348
+// us), one branch for bf16 rows of 5 and 10 (1 x 75600 x 5120 410-415 ->
+// 403-405 us, 1 x 24000 x 20480 604 -> 587-591 us).
+constexpr bool bwd_wide_split(int V, int E) {
+#if defined(ADALN_BWD_WIDE_SPLIT_ALL)
+  return true;
+#elif defined(ADALN_BWD_WIDE_SPLIT_NONE)
+  return false;
+#else
+  return E == 4 || V <= 4;
+#endif
+}
 
 // Tile kernel of the forward for rows wider than 1024 vectors: the W
 // wavefronts of a workgroup share each row, lane l of wavefront w holding
@@ -314,12 +346,13 @@ hipError_t launch_bwd_wide(int dtype, const StreamPlan &plan, const void *dy,
                            float *part_scale, float *part_shift, int32_t B,
                            int32_t N, int32_t D, hipStream_t stream);
 
-hipError_t launch_bwd_wide_segments(int dtype, int V, const SegMap &map,
-                                    const void *dy, const void *x,
-                                    const void *scale, const float *mean,
-                                    const float *rstd, void *dx,
-                                    float *part_scale, float *part_shift,
-                                    int32_t D, hipStream_t stream);
+hipError_t launch_bwd_wide_segments(int dtype, const StreamPlan &plan,
+                                    const SegMap &map, const void *dy,
+                                    const void *x, const void *scale,
+                                    const float *mean, const float *rstd,
+                                    void *dx, float *part_scale,
+                                    float *part_shift, int32_t D,
+                                    hipStream_t stream);
 
 hipError_t launch_bwd_segments(int dtype, int V, const SegMap &map,
                                const void *dy, const void *x,

@@ -105,8 +105,8 @@ size_t adaln_bwd_workspace_bytes(int64_t B, int64_t N, int64_t D, int dtype);
  * dimension N, taken over a (d_tile, n_tile) grid with every lane pinned to
  * its features so that each access is contiguous along D, then combined
  * across the n_tiles; dx, on which the pages are silent, is the exact
- * gradient of the forward formula above.  For rows of at most 1280 vectors
- * (D <= 10240 bf16 / 5120 f32) it enqueues adaln_bwd_fused then
+ * gradient of the forward formula above.  For rows of at most 2560 vectors
+ * (D <= 20480 bf16 / 10240 f32) it enqueues adaln_bwd_fused then
  * adaln_bwd_finish (x and dy read once); for wider rows, adaln_bwd_dx then
  * adaln_bwd_dmod.
  *   dy        [B,N,D] dtype in   upstream gradient dL/dy
@@ -145,11 +145,11 @@ int adaln_bwd_noalloc(const void *dy, const void *x, const void *scale,
                       int64_t D, int dtype, void *stream);
 
 /*
- * The two launches adaln_bwd makes for rows of at most 1280 vectors
- * (D <= 10240 bf16 / 5120 f32), exposed so callers can schedule or time them
+ * The two launches adaln_bwd makes for rows of at most 2560 vectors
+ * (D <= 20480 bf16 / 10240 f32), exposed so callers can schedule or time them
  * separately.  Rows of up to 320 vectors are owned by one wavefront each,
- * wider ones by a pair of wavefronts that combine their row sums through
- * LDS.  adaln_bwd_fused reads x and dy once: it writes dx and, per
+ * wider ones by a pair of wavefronts (up to 1280 vectors) or four of them,
+ * which combine their row sums through LDS.  adaln_bwd_fused reads x and dy once: it writes dx and, per
  * (sample, n_tile), float32 partial sums of dscale and dshift into the
  * workspace -- the D-tile coalesced reduction of section 2.B with dx fused
  * into the same pass over the rows: one partial row per (sample, workgroup).
@@ -171,7 +171,7 @@ int adaln_bwd_finish(const void *workspace, size_t workspace_bytes,
 /*
  * Launch plan of adaln_bwd_fused for this shape, for callers that account
  * for the partial sums it writes: fills out[0..3] with {vectors per lane,
- * wavefronts per row (1 or 2), workgroups launched, partial rows per sample
+ * wavefronts per row (1, 2 or 4), workgroups launched, partial rows per sample
  * P}.
  * The partials occupy 2*B*P*D floats at the start of the workspace.
  * Returns ADALN_ERR_UNSUPPORTED for rows too wide for the fused kernel.
@@ -253,8 +253,8 @@ int adaln_bwd_dmod(const void *dy, const void *x, const float *mean,
  *                dscale[m] sums dy*xhat over every row of every segment
  *                with seg_mod[s] == m (zero for an unused m)
  * The per-row math is that of adaln_fwd / adaln_bwd.  The forward takes every
- * row width adaln_fwd takes; the backward rows of up to 1280 vectors (D <=
- * 10240 bf16 / 5120 f32), wider rows return ADALN_ERR_UNSUPPORTED.  The workspace of adaln_bwd_segments is
+ * row width adaln_fwd takes; the backward rows of up to 2560 vectors (D <=
+ * 20480 bf16 / 10240 f32), wider rows return ADALN_ERR_UNSUPPORTED.  The workspace of adaln_bwd_segments is
  * adaln_bwd_segments_workspace_bytes(seg_offsets, nseg, D, dtype) bytes; the
  * host arrays are read during the call only.
  */

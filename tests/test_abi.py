@@ -175,7 +175,8 @@ def test_segments_validation(lib):
              None) == _lib.ERR_WORKSPACE
     assert g(p, p, p, p, p, p, p, None, p, need, off, mod, 2, 2, 1536, 1,
              None) == _lib.ERR_INVALID
-    assert g(p, p, p, p, p, p, p, p, p, need, off, mod, 2, 2, 16384, 1,
+    # past the packed backward's widest row (2560 vectors)
+    assert g(p, p, p, p, p, p, p, p, p, need, off, mod, 2, 2, 20488, 1,
              None) == _lib.ERR_UNSUPPORTED
     # nothing to do: no segments and no modulation vectors
     assert f(None, None, None, None, None, None, None, None, 0, 0, 64, 1,

@@ -73,8 +73,8 @@ def test_video_bucket_full(A):
     (2, 17, 8192, "f32", "normal"),        # two wavefronts per row, f32
     (1, 5, 16384, "f32", "normal"),        # largest f32 row
     (3, 257, 1024, "f32", "offset"),
-    (2, 333, 2560, "f32", "offset"),       # widest fused f32 backward
-    (1, 100, 4096, "f32", "normal"),       # f32 stream forward, unfused bwd
+    (2, 333, 2560, "f32", "offset"),       # widest one-wavefront f32 bwd
+    (1, 100, 4096, "f32", "normal"),       # f32 stream forward, paired bwd
     (600, 5, 1536, "bf16", "offset"),      # more samples than workgroups
     (1100, 1, 5120, "bf16", "outliers"),   # several samples per workgroup
     (2000, 3, 64, "f32", "normal"),
@@ -92,6 +92,15 @@ def test_video_bucket_full(A):
     (1, 777, 7000, "bf16", "normal"),      # ragged half
     (5, 64, 4096, "f32", "normal"),
     (600, 3, 6144, "bf16", "offset"),      # odd rows per workgroup
+    # backward rows split between four wavefronts (1281..2560 vectors), one
+    # row per workgroup
+    (2, 77, 10248, "bf16", "offset"),      # narrowest, ragged quarter
+    (1, 300, 16384, "bf16", "normal"),     # 8 vectors per lane, exact
+    (3, 50, 20480, "bf16", "outliers"),    # widest fused backward
+    (2, 99, 5124, "f32", "normal"),        # f32, ragged
+    (1, 64, 10240, "f32", "offset"),       # widest fused f32 backward
+    (5, 333, 6144, "f32", "normal"),       # 6 vectors per lane, exact
+    (700, 2, 12288, "bf16", "offset"),     # more samples than workgroups
 ])
 def test_shapes(A, B, N, D, dtype, kind):
     wl = W.custom(B, N, D, dtype, x_kind=kind, dy_std=1e-2 if dtype ==
@@ -125,6 +134,16 @@ def test_wide_rows_all_rows(A):
     wl = synth.WIDE_ROWS
     _say(f"{wl.name} {wl.shape}, every row")
     assert A.bwd_fused_plan(*wl.shape, torch.bfloat16)["waves_per_row"] == 2
+    _run_all_rows(A, wl)
+
+
+def test_quad_rows_all_rows(A):
+    """D=16384 bf16 (2048 vectors, four wavefronts per backward row) at
+    half the large model's activation size: every row, and dscale/dshift."""
+    wl = W.custom(1, 12288, 16384, "bf16", x_kind="outliers", dy_std=1e-2,
+                  index=211)
+    _say(f"quad rows {wl.shape}, every row")
+    assert A.bwd_fused_plan(*wl.shape, torch.bfloat16)["waves_per_row"] == 4
     _run_all_rows(A, wl)
 
 
@@ -273,9 +292,9 @@ def test_unfused_entry_points(A, wl):
         _say(f"  {r}")
 
 
-@pytest.mark.parametrize("D", [10248, 16384, 32768])
+@pytest.mark.parametrize("D", [20488, 32768])
 def test_fused_unsupported_for_wide_rows(A, D):
-    """Rows wider than 1280 vectors have no fused plan; adaln_bwd falls back
+    """Rows wider than 2560 vectors have no fused plan; adaln_bwd falls back
     to the unfused kernels and gives the same bits as calling them."""
     wl = W.custom(1, 9, D, "bf16", dy_std=1e-2)
     _say("wide rows: bwd falls back to bwd_dx + bwd_dmod")

@@ -16,8 +16,9 @@ import adaln_fwd_amd as A
 
 BF16, F32 = torch.bfloat16, torch.float32
 D_BF16 = [8, 520, 1536, 2560, 2568, 3072, 4096, 5120, 5128, 7000, 8192,
-          10240, 12288, 16384, 32768]
-D_F32 = [4, 64, 1024, 1280, 1288, 2560, 4096, 8192, 16384]
+          10240, 10248, 12288, 16384, 20480, 20488, 32768]
+D_F32 = [4, 64, 1024, 1280, 1288, 2560, 4096, 5120, 5124, 8192, 10240,
+         10244, 16384]
 MAX_GRID = 256 * 8   # 256 CUs, at most 8 workgroups each
 
 
@@ -60,7 +61,7 @@ def test_every_row_once(B, N, D, dt):
             p = A.plan(which, B, N, D, dt)
         except A.AdalnError as e:
             assert which == "bwd" and e.code == -6
-            assert D // (8 if dt is BF16 else 4) > 1280
+            assert D // (8 if dt is BF16 else 4) > 2560
             continue
         assert 1 <= p["bps"] and 1 <= p["groups"]
         assert p["workgroups"] == p["bps"] * min(p["groups"], B)
@@ -83,6 +84,16 @@ def test_rows_past_320_vectors_take_pairs():
     assert A.plan("bwd", 1, 75600, 5120, BF16)["waves_per_row"] == 2
     assert A.plan("bwd", 1, 75600, 1280, F32)["waves_per_row"] == 1
     assert A.plan("bwd", 1, 75600, 1288, F32)["waves_per_row"] == 2
+    # past 1280 vectors four wavefronts share a row, one row per workgroup,
+    # up to 2560 vectors; wider rows have no fused plan
+    for D, dt in ((10240, BF16), (5120, F32)):
+        assert A.plan("bwd", 1, 75600, D, dt)["waves_per_row"] == 2
+    for D, dt in ((10248, BF16), (20480, BF16), (5124, F32), (10240, F32)):
+        p = A.plan("bwd", 1, 30000, D, dt)
+        assert p["waves_per_row"] == 4 and p["walkers"] == 1
+    for D, dt in ((20488, BF16), (10244, F32)):
+        with pytest.raises(A.AdalnError):
+            A.plan("bwd", 1, 30000, D, dt)
     # the forward keeps one wavefront per row up to 1024 vectors
     assert A.plan("fwd", 1, 75600, 8192, BF16)["waves_per_row"] == 1
     assert A.plan("fwd", 1, 75600, 8200, BF16)["waves_per_row"] > 1
@@ -141,5 +152,5 @@ def test_plan_validation():
     with pytest.raises(ValueError):
         A.plan("both", 1, 1, 64, BF16)
     with pytest.raises(A.AdalnError) as e:
-        A.plan("bwd", 1, 10, 16384, BF16)
+        A.plan("bwd", 1, 10, 32768, BF16)      # past 2560 vectors: unfused
     assert e.value.code == -6

@@ -47,7 +47,11 @@ SMALL = [
     (8192, "bf16", [300, 0, 17, 1001], [1, 0, 1, 2], 3),        # two-wavefront rows
     (7000, "bf16", [5, 64, 3], None, 3),                        # ragged two-wavefront
     (4096, "f32", [100, 257], [0, 0], 1),
-    (10240, "bf16", [33, 0, 120], [0, 1, 0], 2),   # widest bwd; tile forward
+    (10240, "bf16", [33, 0, 120], [0, 1, 0], 2),   # widest paired bwd
+    # four wavefronts per backward row (1281..2560 vectors); tile forward
+    (10248, "bf16", [7, 130, 0, 1], [0, 1, 1, 0], 2),  # narrowest, ragged
+    (20480, "bf16", [40, 3], None, 2),                 # widest bwd
+    (6144, "f32", [99, 0, 250], [2, 0, 1], 3),
 ]
 
 
@@ -186,9 +190,9 @@ def test_wide_forward_uniform_matches_batched(A):
 
 
 def test_wide_rows_rejected(A):
-    """Rows past the packed backward's width (1280 vectors) are refused
+    """Rows past the packed backward's width (2560 vectors) are refused
     before anything is enqueued; so are rows past the forward's (4096)."""
-    inp = synth.make_packed(_wl(16384, "bf16"), [10, 20], seed=1)
+    inp = synth.make_packed(_wl(20488, "bf16"), [10, 20], seed=1)
     dev = P.packed_to_device(inp)
     mean = torch.zeros(30, device="cuda")
     with pytest.raises(A.AdalnError) as e:
