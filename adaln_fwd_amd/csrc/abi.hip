@@ -188,7 +188,7 @@ constexpr int64_t kLongSample = 4096;
 
 // Waves per SIMD (and so workgroups per CU) a stream plan's kernel runs at.
 int stream_occ(const StreamPlan &p, bool bwd) {
-  if (!bwd) return fwd_stream_occ(p.V);
+  if (!bwd) return p.W > 1 ? fwd_wide_occ(p.V) : fwd_stream_occ(p.V);
   return p.W > 1 ? bwd_wide_occ(p.V) : bwd_stream_occ(p.V);
 }
 
@@ -210,6 +210,18 @@ bool choose_stream_plan(int64_t B, int64_t N, int64_t nvec, bool bwd,
 #define ADALN_QUAD_PLAN_CASE(V_) \
   if (p.V == 0 && (int64_t)4 * 64 * V_ >= nvec) p.V = V_, p.W = 4;
     ADALN_BWD_QUAD_V(ADALN_QUAD_PLAN_CASE)
+#undef ADALN_QUAD_PLAN_CASE
+  }
+  if (!bwd && p.V == 0) {
+    // the forward of rows past 1024 vectors: a pair of wavefronts per row,
+    // or a quad past 1536 vectors
+#define ADALN_PAIR_PLAN_CASE(V_) \
+  if (p.V == 0 && (int64_t)2 * 64 * V_ >= nvec) p.V = V_, p.W = 2;
+    ADALN_FWD_PAIR_V(ADALN_PAIR_PLAN_CASE)
+#undef ADALN_PAIR_PLAN_CASE
+#define ADALN_QUAD_PLAN_CASE(V_) \
+  if (p.V == 0 && (int64_t)4 * 64 * V_ >= nvec) p.V = V_, p.W = 4;
+    ADALN_FWD_QUAD_V(ADALN_QUAD_PLAN_CASE)
 #undef ADALN_QUAD_PLAN_CASE
   }
   if (p.V == 0) return false;
@@ -243,48 +255,6 @@ bool choose_stream_plan(int64_t B, int64_t N, int64_t nvec, bool bwd,
     p.groups = (int)groups;
     p.grid = (int)(bps * (groups < B ? groups : B));
     if (bwd && p.W == 1 && B >= kBwdSkewMinSamples) p.skew = kBwdSkewRows;
-  }
-  *plan = p;
-  return true;
-}
-
-// Workgroups per CU of a tile plan: 4 SIMDs times the kernel's waves per
-// SIMD, over the W wavefronts of a workgroup (at least one).
-int64_t tile_wgs_per_cu(const TilePlan &p) {
-  const int64_t n = 4 * fwd_waves_per_simd(p.V) / p.W;
-  return n > 1 ? n : 1;
-}
-
-// Forward rows wider than 1024 vectors: W wavefronts share a row; the V (of
-// the instantiated ones) that wastes the fewest vector slots, the smallest
-// such V among equals.  Rows are dealt out as in the stream plans, over the
-// G = 256 * tile_wgs_per_cu resident workgroups (one row walker each).
-bool choose_tile_plan(int64_t B, int64_t N, int64_t nvec, TilePlan *plan) {
-  TilePlan p;
-  int64_t best_waste = -1;
-#define ADALN_FWD_PLAN_CASE(V_)                                        \
-  {                                                                    \
-    const int64_t w = (nvec + 64 * V_ - 1) / (64 * V_);                \
-    const int64_t waste = 64 * V_ * w - nvec;                          \
-    if (w <= kMaxRowWaves && (best_waste < 0 || waste < best_waste)) { \
-      best_waste = waste;                                              \
-      p.V = V_;                                                        \
-      p.W = (int)w;                                                    \
-    }                                                                  \
-  }
-  ADALN_FWD_V(ADALN_FWD_PLAN_CASE)
-#undef ADALN_FWD_PLAN_CASE
-  if (p.V == 0) return false;
-  if (B > 0 && N > 0) {
-    const int64_t G = (int64_t)kCUs * tile_wgs_per_cu(p);
-    int64_t bps = G / B > 1 ? G / B : 1;
-    const int64_t most = (N + bps - 1) / bps;
-    const int64_t even = (N + most - 1) / most;
-    if (even < bps) bps = even;
-    const int64_t groups = G / bps;
-    p.bps = (int)bps;
-    p.groups = (int)groups;
-    p.grid = (int)(bps * (groups < B ? groups : B));
   }
   *plan = p;
   return true;
@@ -410,15 +380,13 @@ ADALN_API int adaln_fwd(const void *x, const void *scale, const void *shift,
   const int64_t nvec = D / elems_per_vec(dtype);
   hipError_t e = hipSuccess;
   StreamPlan sp;
-  TilePlan tp;
   if (choose_stream_plan(B, N, nvec, false, &sp))
-    e = launch_fwd_stream(dtype, sp, x, scale, shift, y, mean, rstd,
-                          (int32_t)B, (int32_t)N, (int32_t)D,
-                          (hipStream_t)stream);
-  else if (choose_tile_plan(B, N, nvec, &tp))
-    e = launch_fwd_tiles(dtype, tp, x, scale, shift, y, mean, rstd,
-                         (int32_t)B, (int32_t)N, (int32_t)D,
-                         (hipStream_t)stream);
+    e = sp.W > 1 ? launch_fwd_wide(dtype, sp, x, scale, shift, y, mean, rstd,
+                                   (int32_t)B, (int32_t)N, (int32_t)D,
+                                   (hipStream_t)stream)
+                 : launch_fwd_stream(dtype, sp, x, scale, shift, y, mean,
+                                     rstd, (int32_t)B, (int32_t)N,
+                                     (int32_t)D, (hipStream_t)stream);
   else
     return fail(ADALN_ERR_UNSUPPORTED, "no forward plan for D=%lld",
                 (long long)D);
@@ -560,7 +528,6 @@ ADALN_API int adaln_plan(int which, int64_t B, int64_t N, int64_t D,
                 which);
   const int64_t nvec = D / elems_per_vec(dtype);
   StreamPlan sp;
-  TilePlan tp;
   if (which == 3) {
     const DmodPlan dp = choose_dmod_plan(B, N, nvec);
     const int64_t v[7] = {dp.d_tiles, dp.n_tile, dp.n_tiles,
@@ -585,9 +552,6 @@ ADALN_API int adaln_plan(int which, int64_t B, int64_t N, int64_t D,
     const int64_t walkers = 4 / sp.W;  // four-wavefront workgroups
     const int64_t v[7] = {sp.V,      sp.W,    sp.grid, sp.bps,
                           sp.groups, walkers, sp.skew};
-    std::copy(v, v + 7, out);
-  } else if (which == 0 && choose_tile_plan(B, N, nvec, &tp)) {
-    const int64_t v[7] = {tp.V, tp.W, tp.grid, tp.bps, tp.groups, 1, 0};
     std::copy(v, v + 7, out);
   } else {
     return fail(ADALN_ERR_UNSUPPORTED, "no %s plan for D=%lld",
@@ -718,18 +682,15 @@ ADALN_API int adaln_fwd_segments(const void *x, const void *scale,
   const int64_t nvec = D / elems_per_vec(dtype);
   SegMap map;
   StreamPlan sp;
-  TilePlan tp;
   hipError_t e = hipSuccess;
   if (plan_segments(seg_offsets, seg_mod, nseg, nvec, false, &map, &sp)) {
     if (!rows) return ok();
-    e = launch_fwd_segments(dtype, sp.V, map, x, scale, shift, y, mean, rstd,
-                            (int32_t)D, (hipStream_t)stream);
-  } else if (choose_tile_plan(1, 1, nvec, &tp)) {
-    if (!rows) return ok();
-    build_segment_map(seg_offsets, seg_mod, nseg,
-                      (int64_t)kCUs * tile_wgs_per_cu(tp), &map);
-    e = launch_fwd_tiles_segments(dtype, tp, map, x, scale, shift, y, mean,
-                                  rstd, (int32_t)D, (hipStream_t)stream);
+    e = sp.W > 1 ? launch_fwd_wide_segments(dtype, sp, map, x, scale, shift,
+                                            y, mean, rstd, (int32_t)D,
+                                            (hipStream_t)stream)
+                 : launch_fwd_segments(dtype, sp.V, map, x, scale, shift, y,
+                                       mean, rstd, (int32_t)D,
+                                       (hipStream_t)stream);
   } else {
     return fail(ADALN_ERR_UNSUPPORTED,
                 "D=%lld is too wide for the segment kernels", (long long)D);

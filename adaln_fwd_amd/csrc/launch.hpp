@@ -46,7 +46,7 @@ struct DmodPlan {
 // each wavefront walks its sample's rows with a stride of 4*bps.
 struct StreamPlan {
   int V = 0;       // vectors per lane
-  int W = 1;       // wavefronts per row (2 or 4: the backward's wide rows)
+  int W = 1;       // wavefronts per row (2 or 4: rows too wide for one)
   int grid = 0;
   int bps = 0;     // workgroups per sample (partial rows per sample)
   int groups = 0;  // samples in flight
@@ -206,26 +206,29 @@ constexpr bool bwd_wide_split(int V, int E) {
 #endif
 }
 
-// Tile kernel of the forward for rows wider than 1024 vectors: the W
-// wavefronts of a workgroup share each row, lane l of wavefront w holding
-// vectors (k*W + w)*64 + l, k < V.  Rows are dealt out like the stream
-// kernels' (bps workgroups per sample, `groups` samples in flight, `grid`
-// workgroups).
-struct TilePlan {
-  int V = 0;
-  int W = 0;
-  int grid = 0;
-  int bps = 0;
-  int groups = 0;
-};
-
-constexpr int kMaxRowWaves = 8;  // at most 512 threads per tile workgroup
-// (V <= 2 would need W > 8 for a row past 1024 vectors: never chosen)
-#define ADALN_FWD_V(X) X(3) X(4) X(5) X(6) X(8)
-constexpr int kCUs = 256;
-constexpr int fwd_waves_per_simd(int V) {
-  return V <= 1 ? 8 : V == 2 ? 4 : V <= 4 ? 3 : 2;
+// The forward of rows wider than 1024 vectors splits each row between the W
+// wavefronts of a row group (fwd_wide_kernel), V vectors per lane each:
+// pairs up to 1536 vectors, quads up to 4096.  One wavefront per SIMD; the
+// next row in flight where it fits the registers (V <= 12).
+#define ADALN_FWD_PAIR_V(X) X(10) X(12)
+#define ADALN_FWD_QUAD_V(X) X(8) X(10) X(12) X(16)
+constexpr int fwd_wide_occ(int) { return 1; }
+constexpr int fwd_wide_pf(int V) {
+#ifdef ADALN_FWD_WIDE_PF2
+  return 2;
+#else
+  return V <= 12 ? 2 : 1;
+#endif
 }
+constexpr bool fwd_wide_rewiden(int V, int E) {
+#ifdef ADALN_FWD_WIDE_REWIDEN
+  return true;
+#else
+  return E == 8 && V >= 12;
+#endif
+}
+
+constexpr int kCUs = 256;  // compute units of an MI355X
 
 // Grid-stride kernels take at most this many workgroups per launch.
 constexpr int64_t kMaxGrid = 1 << 20;
@@ -281,19 +284,8 @@ DmodPlan choose_dmod_plan(int64_t B, int64_t N, int64_t nvec);
 // when the row is wider than kMaxStreamVectors.
 bool choose_stream_plan(int64_t B, int64_t N, int64_t nvec, bool bwd,
                         StreamPlan *plan);
-bool choose_tile_plan(int64_t B, int64_t N, int64_t nvec, TilePlan *plan);
 
 // Launchers: enqueue on `stream` and return the launch's own status.
-hipError_t launch_fwd_tiles(int dtype, const TilePlan &plan, const void *x,
-                            const void *scale, const void *shift, void *y,
-                            float *mean, float *rstd, int32_t B, int32_t N,
-                            int32_t D, hipStream_t stream);
-hipError_t launch_fwd_tiles_segments(int dtype, const TilePlan &plan,
-                                     const SegMap &map, const void *x,
-                                     const void *scale, const void *shift,
-                                     void *y, float *mean, float *rstd,
-                                     int32_t D, hipStream_t stream);
-
 hipError_t launch_bwd_dx(int dtype, const RowPlan &plan, const void *dy,
                          const void *x, const void *scale, const float *mean,
                          const float *rstd, void *dx, int64_t rows, int32_t N,
@@ -334,6 +326,17 @@ hipError_t launch_fwd_stream(int dtype, const StreamPlan &plan, const void *x,
                              const void *scale, const void *shift, void *y,
                              float *mean, float *rstd, int32_t B, int32_t N,
                              int32_t D, hipStream_t stream);
+
+hipError_t launch_fwd_wide(int dtype, const StreamPlan &plan, const void *x,
+                           const void *scale, const void *shift, void *y,
+                           float *mean, float *rstd, int32_t B, int32_t N,
+                           int32_t D, hipStream_t stream);
+
+hipError_t launch_fwd_wide_segments(int dtype, const StreamPlan &plan,
+                                    const SegMap &map, const void *x,
+                                    const void *scale, const void *shift,
+                                    void *y, float *mean, float *rstd,
+                                    int32_t D, hipStream_t stream);
 
 hipError_t launch_fwd_segments(int dtype, int V, const SegMap &map,
                                const void *x, const void *scale,

@@ -63,17 +63,17 @@ def log(msg: str) -> None:
 # Sources that determine each kernel's code and launch shape.
 _SHARED = ("common.hpp", "launch.hpp", "abi.hip")
 KERNEL_SOURCES = {
-    "fwd": ("fwd.hip",) + _SHARED,
+    "fwd": ("fwd.hip", "fwd_wide.hip") + _SHARED,
     "bwd_fused": ("bwd_fused.hip", "bwd_wide.hip") + _SHARED,
     "bwd_finish": ("dmod.hip",) + _SHARED,
     "bwd": ("bwd_fused.hip", "bwd_wide.hip", "dmod.hip") + _SHARED,
     "bwd_dx": ("rows.hip",) + _SHARED,
     "bwd_dmod": ("dmod.hip",) + _SHARED,
 }
-# rocprofv3 kernel-name prefixes of each step component (the fused backward
-# runs one wavefront per row or, for wider rows, pairs of them)
+# rocprofv3 kernel-name prefixes of each step component (one wavefront per
+# row, or for wider rows several of them)
 KERNEL_SYMBOLS = {
-    "fwd": ("void adaln::fwd_stream_kernel",),
+    "fwd": ("void adaln::fwd_stream_kernel", "void adaln::fwd_wide_kernel"),
     "bwd_fused": ("void adaln::bwd_stream_kernel",
                   "void adaln::bwd_wide_kernel"),
     "bwd_finish": ("void adaln::dmod_finish_kernel",),

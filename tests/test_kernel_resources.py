@@ -18,13 +18,13 @@ HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 
 @pytest.fixture(scope="module")
 def usage(tmp_path_factory):
-    """Spilled VGPRs per kernel of fwd.hip, bwd_fused.hip and bwd_wide.hip
-    (compiled in parallel)."""
+    """Spilled VGPRs per kernel of fwd.hip, fwd_wide.hip, bwd_fused.hip and
+    bwd_wide.hip (compiled in parallel)."""
     if not os.path.exists(HIPCC):
         pytest.skip("hipcc not available")
     tmp = tmp_path_factory.mktemp("res")
     procs = {}
-    for src in ("fwd.hip", "bwd_fused.hip", "bwd_wide.hip"):
+    for src in ("fwd.hip", "fwd_wide.hip", "bwd_fused.hip", "bwd_wide.hip"):
         procs[src] = subprocess.Popen(
             [HIPCC, "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -69,11 +69,11 @@ def test_wide_backward_kernels_do_not_spill(usage):
     assert not spills, spills
 
 
-def test_forward_tile_kernels_do_not_spill(usage):
-    """The tile forward (rows past 1024 vectors), the widest 8-vector bf16
-    rows included: they keep one row in flight instead of two."""
-    tile = {k: v for k, v in usage["fwd.hip"].items()
-            if "fwd_tile_kernel" in k}
-    assert len(tile) >= 20
-    spills = {k: v for k, v in tile.items() if v}
+def test_forward_wide_kernels_do_not_spill(usage):
+    """The forward of rows past 1024 vectors (pairs and quads of
+    wavefronts), the 16-vector rows included."""
+    wide = {k: v for k, v in usage["fwd_wide.hip"].items()
+            if "fwd_wide_kernel" in k}
+    assert len(wide) >= 24
+    spills = {k: v for k, v in wide.items() if v}
     assert not spills, spills

@@ -66,9 +66,9 @@ def test_every_row_once(B, N, D, dt):
         assert 1 <= p["bps"] and 1 <= p["groups"]
         assert p["workgroups"] == p["bps"] * min(p["groups"], B)
         assert p["bps"] * p["groups"] <= MAX_GRID
-        # four-wavefront workgroups of row walkers, or one row at a time
-        # shared by all the workgroup's wavefronts (the tile forward)
-        assert p["walkers"] * p["waves_per_row"] == 4 or p["walkers"] == 1
+        # four-wavefront workgroups of row walkers: single wavefronts,
+        # pairs or quads
+        assert p["walkers"] * p["waves_per_row"] == 4
         assert np.all(_visits(p, B, N) == 1), (which, p)
         if which == "bwd":
             # partial row b * bps + (g % bps) of [B, bps, D], and room for it
@@ -94,9 +94,14 @@ def test_rows_past_320_vectors_take_pairs():
     for D, dt in ((20488, BF16), (10244, F32)):
         with pytest.raises(A.AdalnError):
             A.plan("bwd", 1, 30000, D, dt)
-    # the forward keeps one wavefront per row up to 1024 vectors
+    # the forward keeps one wavefront per row up to 1024 vectors, then
+    # pairs up to 1536 and quads up to 4096
     assert A.plan("fwd", 1, 75600, 8192, BF16)["waves_per_row"] == 1
-    assert A.plan("fwd", 1, 75600, 8200, BF16)["waves_per_row"] > 1
+    for D, dt, w in ((8200, BF16, 2), (12288, BF16, 2), (4100, F32, 2),
+                     (6144, F32, 2), (12296, BF16, 4), (32768, BF16, 4),
+                     (6148, F32, 4), (16384, F32, 4)):
+        p = A.plan("fwd", 1, 30000, D, dt)
+        assert p["waves_per_row"] == w and p["walkers"] == 4 // w, (D, p)
 
 
 def test_long_samples_fewer_in_flight_in_the_forward():

@@ -48,7 +48,8 @@ SMALL = [
     (7000, "bf16", [5, 64, 3], None, 3),                        # ragged two-wavefront
     (4096, "f32", [100, 257], [0, 0], 1),
     (10240, "bf16", [33, 0, 120], [0, 1, 0], 2),   # widest paired bwd
-    # four wavefronts per backward row (1281..2560 vectors); tile forward
+    # four wavefronts per backward row (1281..2560 vectors), and per
+    # forward row past 1536
     (10248, "bf16", [7, 130, 0, 1], [0, 1, 1, 0], 2),  # narrowest, ragged
     (20480, "bf16", [40, 3], None, 2),                 # widest bwd
     (6144, "f32", [99, 0, 250], [2, 0, 1], 3),
@@ -145,12 +146,14 @@ def test_deterministic(A):
 
 
 WIDE_FORWARD = [
-    # D, dtype, lengths, seg_mod, nmod: rows past 1024 vectors (tile kernel)
+    # D, dtype, lengths, seg_mod, nmod: rows past 1024 vectors (pairs and
+    # quads of wavefronts)
     (16384, "bf16", [10, 20, 0, 7], [1, 0, 1, 0], 2),
     (32768, "bf16", [3, 5], None, 2),                 # widest row
     (12288, "bf16", [1, 200, 31], [0, 0, 0], 1),
     (16384, "f32", [4, 9], None, 2),                  # widest f32 row
     (8200, "bf16", [64, 1], None, 2),                 # ragged, just past 1024
+    (6148, "f32", [33, 100], [1, 1], 2),              # ragged quad, f32
 ]
 
 
@@ -175,7 +178,7 @@ def test_wide_forward_full(A, case):
 
 
 def test_wide_forward_uniform_matches_batched(A):
-    """Equal segments with the identity table through the tile kernel equal
+    """Equal segments with the identity table through the wide kernel equal
     the batched forward bit for bit (same per-row arithmetic)."""
     B, N, D = 3, 300, 16384
     inp = synth.make_packed(_wl(D, "bf16"), [N] * B, seed=5)
