@@ -46,12 +46,13 @@ __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void bwd_stream_kernel(
   const int nvec = D / E;
   const float inv_d = 1.0f / (float)D;
 
-  int jv[V];
+  int jv[V], jl[V];  // vector of lane l, and the vector its loads read
   bool ok[V];
 #pragma unroll
   for (int k = 0; k < V; ++k) {
     jv[k] = k * kWave + lane;
     ok[k] = FULL || jv[k] < nvec;
+    jl[k] = FULL ? jv[k] : clamp_vec(jv[k], nvec);
   }
 
   // One segment (a sample, or a packed sequence): rows [row0, row0 + N),
@@ -84,13 +85,14 @@ __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void bwd_stream_kernel(
       const int64_t off = at(n) * D;
 #pragma unroll
       for (int k = 0; k < V; ++k) {
-        xv[k] = ok[k] ? load_stream(x + off + (int64_t)jv[k] * E) : vzero();
-        gv[k] = ok[k] ? load_stream(dy + off + (int64_t)jv[k] * E) : vzero();
+        xv[k] = load_stream(x + off + (int64_t)jl[k] * E);
+        gv[k] = load_stream(dy + off + (int64_t)jl[k] * E);
       }
     };
 
     auto do_row = [&](Vec (&xv)[V], Vec (&gv)[V], const float (&st)[2],
                       int n) {
+      if constexpr (!FULL) mask_tail(xv, ok), mask_tail(gv, ok);
       const float mu = st[0];
       const float r = st[1];
       // row sums of g = dy * (1 + scale) and g * xhat

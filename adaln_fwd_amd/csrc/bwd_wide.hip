@@ -54,12 +54,13 @@ bwd_wide_kernel(
   const int nvec = D / E;
   const float inv_d = 1.0f / (float)D;
 
-  int jv[V];
+  int jv[V], jl[V];  // vector of lane l, and the vector its loads read
   bool ok[V];
 #pragma unroll
   for (int k = 0; k < V; ++k) {
     jv[k] = (part * V + k) * kWave + lane;
     ok[k] = FULL || jv[k] < nvec;
+    jl[k] = FULL ? jv[k] : clamp_vec(jv[k], nvec);
   }
 
   int parity = 0;
@@ -100,8 +101,8 @@ bwd_wide_kernel(
         const int64_t off = at(n) * D;
 #pragma unroll
         for (int k = 0; k < V; ++k) {
-          xv[k] = ok[k] ? load_stream(x + off + (int64_t)jv[k] * E) : vzero();
-          gv[k] = ok[k] ? load_stream(dy + off + (int64_t)jv[k] * E) : vzero();
+          xv[k] = load_stream(x + off + (int64_t)jl[k] * E);
+          gv[k] = load_stream(dy + off + (int64_t)jl[k] * E);
         }
       }
     };
@@ -113,6 +114,7 @@ bwd_wide_kernel(
       const float r = st[1];
       float s1 = 0.f, s2 = 0.f;
       if (live) {
+        if constexpr (!FULL) mask_tail(xv, ok), mask_tail(gv, ok);
         // this part's sums of g = dy * (1 + scale) and g * xhat (vectors
         // past the row end hold dy = 0, so g = 0 there)
 #pragma unroll
@@ -193,10 +195,10 @@ bwd_wide_kernel(
           r = rstd[at(n)];
 #pragma unroll
           for (int k = 0; k < V; ++k) {
-            xv[k] = ok[k] ? load_stream(x + off + (int64_t)jv[k] * E) : vzero();
-            gv[k] =
-                ok[k] ? load_stream(dy + off + (int64_t)jv[k] * E) : vzero();
+            xv[k] = load_stream(x + off + (int64_t)jl[k] * E);
+            gv[k] = load_stream(dy + off + (int64_t)jl[k] * E);
           }
+          if constexpr (!FULL) mask_tail(xv, ok), mask_tail(gv, ok);
 #pragma unroll
           for (int k = 0; k < V; ++k) {
 #pragma unroll

@@ -82,6 +82,23 @@ __device__ __forceinline__ void store_stream(void *p, const Vec &v) {
   __builtin_nontemporal_store(u, reinterpret_cast<u32x4 *>(p));
 }
 
+// Rows whose width is not a whole number of wavefront vectors: lane l's
+// vector j may lie past the row end (j >= nvec).  Its load reads the row's
+// last vector instead (a valid address, data already being fetched) with no
+// predicate, and mask_tail zeroes it at its first use.  A predicated load
+// (`ok ? load : 0`) made the compiler wait for all outstanding memory
+// traffic right after it, which took away the next row's prefetch.
+__device__ __forceinline__ int clamp_vec(int j, int nvec) {
+  return j < nvec ? j : nvec - 1;
+}
+
+template <int V>
+__device__ __forceinline__ void mask_tail(Vec (&v)[V], const bool (&ok)[V]) {
+#pragma unroll
+  for (int k = 0; k < V; ++k)
+    if (!ok[k]) v[k] = vzero();
+}
+
 // Make the compiler treat the vector's registers as rewritten here, so later
 // uses re-derive float values from the packed registers instead of keeping
 // every widened value alive across a reduction (which would double or triple

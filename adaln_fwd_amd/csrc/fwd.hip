@@ -35,12 +35,13 @@ __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void fwd_stream_kernel(
   const int nvec = D / E;
   const float inv_d = 1.0f / (float)D;
 
-  int jv[V];
+  int jv[V], jl[V];  // vector of lane l, and the vector its load reads
   bool ok[V];
 #pragma unroll
   for (int k = 0; k < V; ++k) {
     jv[k] = k * kWave + lane;
     ok[k] = FULL || jv[k] < nvec;
+    jl[k] = FULL ? jv[k] : clamp_vec(jv[k], nvec);
   }
 
   // One segment (a sample, or a packed sequence): rows [row0, row0 + N),
@@ -60,10 +61,11 @@ __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void fwd_stream_kernel(
       const int64_t off = (row0 + n) * D;
 #pragma unroll
       for (int k = 0; k < V; ++k)
-        xv[k] = ok[k] ? load_stream(x + off + (int64_t)jv[k] * E) : vzero();
+        xv[k] = load_stream(x + off + (int64_t)jl[k] * E);
     };
 
     auto do_row = [&](Vec (&xv)[V], int n) {
+      if constexpr (!FULL) mask_tail(xv, ok);
       float s = 0.f;
 #pragma unroll
       for (int k = 0; k < V; ++k)

@@ -43,12 +43,13 @@ fwd_wide_kernel(const T *__restrict__ x, const T *__restrict__ scale,
   const int nvec = D / E;
   const float inv_d = 1.0f / (float)D;
 
-  int jv[V];
+  int jv[V], jl[V];  // vector of lane l, and the vector its load reads
   bool ok[V];
 #pragma unroll
   for (int k = 0; k < V; ++k) {
     jv[k] = (part * V + k) * kWave + lane;
     ok[k] = FULL || jv[k] < nvec;
+    jl[k] = FULL ? jv[k] : clamp_vec(jv[k], nvec);
   }
   // elements of the row that part h holds (the same in every wavefront)
   auto count = [&](int h) -> float {
@@ -79,7 +80,7 @@ fwd_wide_kernel(const T *__restrict__ x, const T *__restrict__ scale,
         const int64_t off = (row0 + n) * D;
 #pragma unroll
         for (int k = 0; k < V; ++k)
-          xv[k] = ok[k] ? load_stream(x + off + (int64_t)jv[k] * E) : vzero();
+          xv[k] = load_stream(x + off + (int64_t)jl[k] * E);
       }
     };
 
@@ -87,6 +88,7 @@ fwd_wide_kernel(const T *__restrict__ x, const T *__restrict__ scale,
       const bool live = n < N;  // uniform across the wavefront
       float sum_w = 0.f, m2_w = 0.f;
       if (live) {
+        if constexpr (!FULL) mask_tail(xv, ok);
         // this part's sum, and its centred sum of squares around its mean
         float s = 0.f;
 #pragma unroll

@@ -175,17 +175,17 @@ constexpr int kMaxBwdStreamV = 5;
 #define ADALN_BWD_QUAD_V(X) X(6) X(8) X(10)
 constexpr int bwd_wide_occ(int V) { return V <= 5 ? 2 : 1; }
 // Rows in flight per wavefront of bwd_wide_kernel (E elements per vector):
-// at one wavefront per SIMD, a second row where its 2*V vectors of x and dy
-// fit beside the accumulators without spills (V*E <= 64 elements; <= 48
-// where the row ends inside a wavefront's vectors and the predicated loads
-// need registers of their own).  Measured on MI355X (fused backward, bf16):
-// D = 6144 288 -> 262 us, D = 8192 471 -> 440 us, D = 12288 555 -> 517 us,
-// D = 16384 586 -> 540 us; f32 within 2%.
+// bf16 rows at one wavefront per SIMD take a second row where its 2*V
+// vectors of x and dy fit beside the accumulators without spills (V*E <= 64
+// elements; <= 48 where the row ends inside a wavefront's vectors and the
+// tail needs registers of its own).  Measured on MI355X (fused backward,
+// bf16): D = 6144 288 -> 262 us, D = 8192 471 -> 440 us, D = 12288 555 ->
+// 517 us, D = 16384 586 -> 540 us.  f32 rows gained at most 2% and keep one.
 constexpr int bwd_wide_pf(int V, int E, bool full) {
 #ifdef ADALN_BWD_WIDE_PF1
   return 1;
 #else
-  return bwd_wide_occ(V) == 1 && V * E <= (full ? 64 : 48) ? 2 : 1;
+  return bwd_wide_occ(V) == 1 && E == 8 && V * E <= (full ? 64 : 48) ? 2 : 1;
 #endif
 }
 // Loop form of bwd_wide_kernel at one row in flight: the loads as one step
