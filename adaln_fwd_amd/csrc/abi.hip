@@ -230,23 +230,25 @@ bool choose_stream_plan(int64_t B, int64_t N, int64_t nvec, bool bwd,
     const int64_t G = (int64_t)kCUs * occ;
     const int64_t min_bps = bwd ? ADALN_BWD_MIN_BPS : ADALN_FWD_MIN_BPS;
     int64_t bps = G / B > 1 ? G / B : 1;
-    if (!bwd && B > 1 && N >= kLongSample) {
-      // Forward of long samples: the fewest samples in flight (g, a divisor
-      // of B, so every group slot walks B / g samples) that still give each
-      // wavefront 16 rows of a sample.  Measured on MI355X, D = 3072: 16 x
-      // 8190 tokens 290 -> 270 us, 8 x 16380 281 -> 273 us; for samples of
-      // 1560 tokens fewer in flight is slower, hence the length threshold.
-      // (The backward keeps one sample per slot: every extra workgroup per
-      // sample costs a partial row.)
+    const int64_t walkers = 4 / p.W;  // row walkers per workgroup
+    if (B > 1 && N >= kLongSample && (!bwd || p.W > 1)) {
+      // Long samples: the fewest samples in flight (g, a divisor of B, so
+      // every group slot walks B / g samples) that still give each row
+      // walker 16 rows of a sample.  Measured on MI355X, D = 3072, forward:
+      // 16 x 8190 tokens 290 -> 270 us, 8 x 16380 281 -> 273 us; whole
+      // backward with pairs of wavefronts per row, although every extra
+      // workgroup on a sample costs a partial row: 16 x 8190 443 -> 431 us,
+      // 8 x 16380 444 -> 424 us, 4 x 32760 424 -> 422 us.  For samples of
+      // 1560 tokens fewer in flight is slower, hence the length threshold;
+      // the one-wavefront backward keeps one sample per slot.
       for (int64_t g = 1; g < B && g <= G; ++g) {
-        if (B % g == 0 && G / g <= N / 64) {
+        if (B % g == 0 && G / g <= N / (16 * walkers)) {
           bps = G / g;
           break;
         }
       }
     }
     if (bps < min_bps) bps = min_bps < G ? min_bps : G;
-    const int64_t walkers = 4 / p.W;  // row walkers per workgroup
     const int64_t most = (N + walkers * bps - 1) / (walkers * bps);
     const int64_t even = (N + walkers * most - 1) / (walkers * most);
     if (even >= min_bps && even < bps) bps = even;
@@ -755,7 +757,7 @@ namespace {
 // copy until the process ends.  In host code `scratch` names a host-side
 // stand-in, never the device memory: the device address is looked up once
 // per device with hipGetSymbolAddress and only that address is passed on.
-constexpr size_t kScratchBytes = size_t(32) << 20;
+constexpr size_t kScratchBytes = size_t(64) << 20;
 __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 constexpr int kMaxDevices = 256;

@@ -130,8 +130,8 @@ int adaln_bwd(const void *dy, const void *x, const void *scale,
  * workspace: code under HIP graph capture, tight serving loops, harnesses
  * that forbid allocation.  Same arguments, kernels and results as adaln_bwd
  * (bit for bit), without the workspace: the partial rows go to a static
- * device array of the library, 32 MiB per GPU, held until the process ends.
- * Shapes whose adaln_bwd_workspace_bytes exceeds 32 MiB return
+ * device array of the library, 64 MiB per GPU, held until the process ends.
+ * Shapes whose adaln_bwd_workspace_bytes exceeds 64 MiB return
  * ADALN_ERR_WORKSPACE before any HIP call.  The first call on a device looks
  * up the array's device address (hipGetSymbolAddress) and keeps it; make one
  * call before capturing a graph.  Every call on a GPU shares that GPU's

@@ -5,7 +5,8 @@ walker w -> rows (g % bps) * walkers + w, + bps * walkers, ...), visit every
 token row exactly once, fit the resident grid, and for the fused backward
 give each (sample, workgroup) pair its own partial row inside the
 workspace.  The shape-dependent choices are pinned too: the wavefront
-pairs past 320 vectors, the fewest long samples in flight in the forward,
+pairs past 320 vectors, the fewest long samples in flight (forward and
+paired backward),
 and the balanced workgroups per sample.  CPU only."""
 
 import numpy as np
@@ -104,7 +105,7 @@ def test_rows_past_320_vectors_take_pairs():
         assert p["waves_per_row"] == w and p["walkers"] == 4 // w, (D, p)
 
 
-def test_long_samples_fewer_in_flight_in_the_forward():
+def test_long_samples_fewer_in_flight():
     # 16 samples of 8190 rows at D = 3072: four in flight (4 each in turn);
     # two would leave a wavefront 15.99 rows of a sample
     p = A.plan("fwd", 16, 8190, 3072, BF16)
@@ -113,9 +114,18 @@ def test_long_samples_fewer_in_flight_in_the_forward():
     # 8 samples of 16380 rows: two in flight, 32 rows per wavefront each
     p = A.plan("fwd", 8, 16380, 3072, BF16)
     assert p["groups"] == 2 and 16380 / (p["bps"] * p["walkers"]) >= 16
-    # short samples keep one group each; the backward never changes
+    # short samples keep one group each
     assert A.plan("fwd", 84, 1560, 3072, BF16)["groups"] >= 84
-    assert A.plan("bwd", 16, 8190, 3072, BF16)["groups"] >= 16
+    assert A.plan("bwd", 84, 1560, 3072, BF16)["groups"] >= 84
+    # the backward with pairs of wavefronts per row (2 walkers per
+    # workgroup) follows the same rule: 16 rows per pair
+    p = A.plan("bwd", 16, 8190, 3072, BF16)
+    assert p["walkers"] == 2 and p["groups"] == 4
+    assert 8190 / (p["bps"] * p["walkers"]) >= 16
+    p = A.plan("bwd", 8, 16380, 3072, BF16)
+    assert p["groups"] == 2 and 16380 / (p["bps"] * p["walkers"]) >= 16
+    # the one-wavefront backward keeps one sample per slot
+    assert A.plan("bwd", 16, 8190, 1536, BF16)["groups"] >= 16
 
 
 def test_balanced_workgroups_per_sample():

@@ -80,8 +80,11 @@ def test_two_calls_in_a_row_second_smaller(lib):
                 _say(f"  {r}")
 
 
-def test_rows_too_wide_for_the_fused_kernel(lib):
-    wl = W.custom(2, 300, 12288, "bf16", x_kind="normal", dy_std=1e-2)
+@pytest.mark.parametrize("D", [12288, 32768])
+def test_wide_rows(lib, D):
+    # four wavefronts per row in the fused backward (12288), and rows too
+    # wide for it (32768: the dx and D-tile kernels)
+    wl = W.custom(2, 300, D, "bf16", x_kind="normal", dy_std=1e-2)
     _say(f"wide rows {wl.shape}")
     inp, (ref, got) = _both(lib, wl, seed=5)
     for key in ("dx", "dscale", "dshift"):
