@@ -28,6 +28,12 @@
 // needs no such step -- and written as one partial row per (segment,
 // workgroup): the workspace layout of bwd_stream_kernel, summed by the same
 // finishing kernels.  Fixed-order sums only; no atomics.
+//
+// Two choices are made per row width, by measurement (launch.hpp): PF, the
+// rows in flight per wavefront (a second one where it fits beside the
+// accumulators), and SPLIT, the loop form at one row in flight (the loads as
+// one step and the arithmetic as the next, or both in one branch).  All
+// forms do the same arithmetic in the same order.
 #include "common.hpp"
 #include "launch.hpp"
 

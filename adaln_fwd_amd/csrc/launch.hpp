@@ -119,7 +119,9 @@ constexpr int kMaxStreamVectors = 16 * 64;
 // kernel instantiation.  OCC also fixes the grid: OCC workgroups per CU.
 // Short rows get two rows in flight and several workgroups per CU to keep
 // enough bytes in flight; long rows get the whole register file of one
-// wavefront per SIMD (the backward's per-lane accumulators need it).
+// wavefront per SIMD (the backward's per-lane accumulators need it).  The
+// ADALN_* macros in this part only override the measured choices at build
+// time, to measure the alternatives; the library is built without them.
 #ifndef ADALN_FWD_PF_SHORT
 #define ADALN_FWD_PF_SHORT 2
 #endif
