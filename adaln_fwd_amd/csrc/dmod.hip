@@ -51,16 +51,23 @@ __global__ __launch_bounds__(kBlock) void dmod_partial_kernel(
     for (int n = n0 + wave; n < n1; n += kWaves * U) {
       Vec xv[U], gv[U];
       float mu[U], r[U];
+      bool in[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
+        // no predicate on the loads: rows past the tile and vectors past the
+        // row end read a valid address, and are zeroed before their use
         const int nn = n + u * kWaves;
         const bool live = nn < n1;
-        const int64_t off = (row0 + (live ? nn : n0)) * D + (int64_t)j * E;
-        xv[u] = (live && ok) ? load_stream(x + off) : vzero();
-        gv[u] = (live && ok) ? load_stream(dy + off) : vzero();
+        in[u] = live && ok;
+        const int64_t off =
+            (row0 + (live ? nn : n0)) * D + (int64_t)clamp_vec(j, nvec) * E;
+        xv[u] = load_stream(x + off);
+        gv[u] = load_stream(dy + off);
         mu[u] = live ? mean[row0 + nn] : 0.f;
         r[u] = live ? rstd[row0 + nn] : 0.f;
       }
+      mask_tail(xv, in);
+      mask_tail(gv, in);
 #pragma unroll
       for (int u = 0; u < U; ++u) {
 #pragma unroll
