@@ -148,13 +148,19 @@ DmodPlan choose_dmod_plan(int64_t B, int64_t N, int64_t nvec) {
   return p;
 }
 
-// Row-stream plans (rows of up to 1024 vectors for the forward, 2560 for the
+// Row-stream plans (rows of up to 4096 vectors for the forward, 2560 for the
 // backward, which takes a pair of wavefronts per row past 320 and four past
-// 1280).  V is the smallest instantiated count that holds the row.  The
-// kernel's occupancy OCC fixes a persistent grid of G = 256 * OCC workgroups
-// (OCC per CU on a 256-CU MI355X), spread over the samples: up to G / B
-// workgroups per sample (at least one), `groups` = G / bps samples in
-// flight.  Of the counts that keep the most rows any row walker (a
+// 1280; the forward takes a pair past 1024 and four past 1536).  V is the
+// smallest instantiated count that holds the row.
+//
+// The forward of one-wavefront rows covers the rows with its grid, one row
+// per wavefront: ceil(B * N / 4) workgroups in all (fwd_rows_kernel, fwd.hip,
+// has the measurements).
+//
+// The other kernels run a persistent grid: the occupancy OCC fixes G = 256 *
+// OCC workgroups (OCC per CU on a 256-CU MI355X), spread over the samples:
+// up to G / B workgroups per sample (at least one), `groups` = G / bps
+// samples in flight.  Of the counts that keep the most rows any row walker (a
 // wavefront, or the W wavefronts sharing a row) visits as low as G / B does,
 // bps is the smallest, so that all walkers finish together rather than a few
 // walking one row more (measured on MI355X: the 16 x 1560-token, D = 1536
@@ -183,14 +189,18 @@ DmodPlan choose_dmod_plan(int64_t B, int64_t N, int64_t nvec) {
 constexpr int kBwdSkewRows = 97;
 constexpr int64_t kBwdSkewMinSamples = 16;
 
-// Samples of at least this many rows count as long for the forward plan.
+// Samples of at least this many rows count as long for a persistent plan.
 constexpr int64_t kLongSample = 4096;
 
-// Waves per SIMD (and so workgroups per CU) a stream plan's kernel runs at.
+// Waves per SIMD (and so workgroups per CU) a persistent plan's kernel runs
+// at.
 int stream_occ(const StreamPlan &p, bool bwd) {
-  if (!bwd) return p.W > 1 ? fwd_wide_occ(p.V) : fwd_stream_occ(p.V);
+  if (!bwd) return fwd_wide_occ(p.V);
   return p.W > 1 ? bwd_wide_occ(p.V) : bwd_stream_occ(p.V);
 }
+
+// The forward's one-row-per-wavefront kernel: a grid over the rows.
+bool rows_grid(const StreamPlan &p, bool bwd) { return !bwd && p.W == 1; }
 
 bool choose_stream_plan(int64_t B, int64_t N, int64_t nvec, bool bwd,
                         StreamPlan *plan) {
@@ -225,7 +235,9 @@ bool choose_stream_plan(int64_t B, int64_t N, int64_t nvec, bool bwd,
 #undef ADALN_QUAD_PLAN_CASE
   }
   if (p.V == 0) return false;
-  if (B > 0 && N > 0) {
+  if (rows_grid(p, bwd)) {
+    p.grid = (B * N + 3) / 4;  // one row per wavefront
+  } else if (B > 0 && N > 0) {
     const int occ = stream_occ(p, bwd);
     const int64_t G = (int64_t)kCUs * occ;
     const int64_t min_bps = bwd ? ADALN_BWD_MIN_BPS : ADALN_FWD_MIN_BPS;
@@ -234,12 +246,12 @@ bool choose_stream_plan(int64_t B, int64_t N, int64_t nvec, bool bwd,
     if (B > 1 && N >= kLongSample && (!bwd || p.W > 1)) {
       // Long samples: the fewest samples in flight (g, a divisor of B, so
       // every group slot walks B / g samples) that still give each row
-      // walker 16 rows of a sample.  Measured on MI355X, D = 3072, forward:
-      // 16 x 8190 tokens 290 -> 270 us, 8 x 16380 281 -> 273 us; whole
-      // backward with pairs of wavefronts per row, although every extra
-      // workgroup on a sample costs a partial row: 16 x 8190 443 -> 431 us,
-      // 8 x 16380 444 -> 424 us, 4 x 32760 424 -> 422 us.  For samples of
-      // 1560 tokens fewer in flight is slower, hence the length threshold;
+      // walker 16 rows of a sample (the wide forward and the backward with
+      // pairs or quads of wavefronts per row).  Measured on MI355X, D =
+      // 3072, whole backward with pairs of wavefronts per row, although every
+      // extra workgroup on a sample costs a partial row: 16 x 8190 443 -> 431
+      // us, 8 x 16380 444 -> 424 us, 4 x 32760 424 -> 422 us.  For samples
+      // of 1560 tokens fewer in flight is slower, hence the length threshold;
       // the one-wavefront backward keeps one sample per slot.
       for (int64_t g = 1; g < B && g <= G; ++g) {
         if (B % g == 0 && G / g <= N / (16 * walkers)) {
@@ -309,6 +321,7 @@ bool plan_segments(const int64_t *off, const int32_t *mod, int64_t nseg,
                    int64_t nvec, bool bwd, SegMap *map, StreamPlan *plan) {
   StreamPlan sp;
   if (!choose_stream_plan(1, 1, nvec, bwd, &sp)) return false;
+  // the forward of one-wavefront rows reads only the rows and vectors
   build_segment_map(off, mod, nseg, (int64_t)kCUs * stream_occ(sp, bwd), map);
   *plan = sp;
   return true;
@@ -386,9 +399,9 @@ ADALN_API int adaln_fwd(const void *x, const void *scale, const void *shift,
     e = sp.W > 1 ? launch_fwd_wide(dtype, sp, x, scale, shift, y, mean, rstd,
                                    (int32_t)B, (int32_t)N, (int32_t)D,
                                    (hipStream_t)stream)
-                 : launch_fwd_stream(dtype, sp, x, scale, shift, y, mean,
-                                     rstd, (int32_t)B, (int32_t)N,
-                                     (int32_t)D, (hipStream_t)stream);
+                 : launch_fwd_rows(dtype, sp.V, x, scale, shift, y, mean,
+                                   rstd, (int32_t)B, (int32_t)N, (int32_t)D,
+                                   (hipStream_t)stream);
   else
     return fail(ADALN_ERR_UNSUPPORTED, "no forward plan for D=%lld",
                 (long long)D);

@@ -3,16 +3,25 @@
 // D, then y = xhat * (1 + scale[b]) + shift[b], with x read from HBM once and
 // y written once, in a single launch.
 //
-// fwd_stream_kernel (rows of up to 1024 16-byte vectors): one wavefront per
-// row, lane l holding vectors k*64 + l, k < V, in registers; no barrier is
-// needed.  A small persistent grid (OCC four-wavefront workgroups per CU) is
-// spread over the samples, bps workgroups per sample, and each wavefront
-// walks its sample's rows with a stride of 4*bps rows.  All wavefronts that
-// are active at a time therefore touch a narrow window of rows that sweeps
-// through memory in order: measured on MI355X, that keeps HBM about 15%
-// busier than giving each workgroup its own contiguous block of rows.  The
-// sample's scale and shift stay in registers.  Mean and variance are
+// fwd_rows_kernel (rows of up to 1024 16-byte vectors): one wavefront per
+// row, lane l holding vectors k*64 + l, k < V, in registers; no barrier and
+// no loop.  The grid covers the rows of the call: wavefront w of workgroup g
+// takes row first + 4g + w (one launch per 2^22 rows).  A wavefront issues
+// the loads of its row first, then finds its row's modulation vector (the
+// sample r / N, or the packed segment holding r) and loads its scale and
+// shift (L2 hits after the first rows of a sample).  Mean and variance are
 // two-pass over the register-resident row (DPP reductions).
+//
+// No occupancy is imposed: with short-lived wavefronts the hardware keeps as
+// many rows in flight as the registers allow, and the rows in flight at any
+// time are the consecutive rows the dispatcher has reached, one window over
+// memory for any number of samples.  Measured on MI355X against a persistent
+// grid (a fixed number of workgroups per CU walking each sample's rows with
+// scale and shift kept in registers), in one process on the same buffers,
+// bf16: 16 x 1560 x 1536 30.5 -> 27.2 us, 84 x 1560 x 3072 307 -> 267 us,
+// 256 x 256 x 1152 61.6 -> 53.0 us, 1 x 75600 x 5120 264 -> 256 us.  The same
+// kernel walking rows inside the work map's loops kept more registers alive
+// (one wavefront per SIMD at 640 vectors instead of two) and lost most of it.
 //
 // Wider rows: fwd_wide_kernel (fwd_wide.hip).
 //
@@ -22,16 +31,40 @@
 
 namespace adaln {
 
-template <typename T, int V, bool FULL, int PF, int OCC, class Map>
-__global__ __launch_bounds__(kBlock)
-__attribute__((amdgpu_waves_per_eu(OCC, OCC))) void fwd_stream_kernel(
+// Row -> modulation vector.  BatchRows: B samples of N rows.
+struct BatchRows {
+  int32_t N;
+};
+
+__device__ __forceinline__ int row_mod(const BatchRows &m, int64_t r) {
+  return r < INT32_MAX ? (int)((uint32_t)r / (uint32_t)m.N)
+                       : (int)(r / m.N);
+}
+
+// SegMap: the segment s with row_start[s] <= r < row_start[s + 1] (the last
+// s with row_start[s] <= r skips the empty segments before it).
+__device__ __forceinline__ int row_mod(const SegMap &m, int64_t r) {
+  int lo = 0, hi = m.nseg - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) / 2;
+    if (m.row_start[mid] <= r)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  return m.mod[lo];
+}
+
+template <typename T, int V, bool FULL, class Map>
+__global__ __launch_bounds__(kBlock) void fwd_rows_kernel(
     const T *__restrict__ x, const T *__restrict__ scale,
     const T *__restrict__ shift, T *__restrict__ y, float *__restrict__ mean,
-    float *__restrict__ rstd, int32_t D, Map map) {
+    float *__restrict__ rstd, int32_t D, int64_t first, int64_t end,
+    Map map) {
   constexpr int E = Elems<T>::value;
-  constexpr int kWaves = kBlock / kWave;
   const int lane = lane_id();
-  const int wave = wave_id();
+  const int64_t r = first + (int64_t)blockIdx.x * (kBlock / kWave) + wave_id();
+  if (r >= end) return;
   const int nvec = D / E;
   const float inv_d = 1.0f / (float)D;
 
@@ -43,169 +76,132 @@ __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void fwd_stream_kernel(
     ok[k] = FULL || jv[k] < nvec;
     jl[k] = FULL ? jv[k] : clamp_vec(jv[k], nvec);
   }
-
-  // One segment (a sample, or a packed sequence): rows [row0, row0 + N),
-  // modulated by vector `mod`; this workgroup is number k_in of bps.
-  for_each_segment(map, [&](int64_t row0, int N, int mod, int k_in, int bps,
-                            int, int) {
-    const int stride = bps * kWaves;
-    Vec sv[V], hv[V];
+  const int64_t off = r * D;
+  Vec xv[V], sv[V], hv[V];
 #pragma unroll
-    for (int k = 0; k < V; ++k) {
-      const int64_t c = (int64_t)mod * D + (int64_t)jv[k] * E;
-      sv[k] = ok[k] ? load_vec(scale + c) : vzero();
-      hv[k] = ok[k] ? load_vec(shift + c) : vzero();
-    }
-
-    auto load_row = [&](Vec (&xv)[V], int n) {
-      const int64_t off = (row0 + n) * D;
+  for (int k = 0; k < V; ++k)
+    xv[k] = load_stream(x + off + (int64_t)jl[k] * E);
+  const int64_t mod = row_mod(map, r);
 #pragma unroll
-      for (int k = 0; k < V; ++k)
-        xv[k] = load_stream(x + off + (int64_t)jl[k] * E);
-    };
-
-    auto do_row = [&](Vec (&xv)[V], int n) {
-      if constexpr (!FULL) mask_tail(xv, ok);
-      float s = 0.f;
+  for (int k = 0; k < V; ++k) {
+    const int64_t c = mod * D + (int64_t)jl[k] * E;
+    sv[k] = load_vec(scale + c);
+    hv[k] = load_vec(shift + c);
+  }
+  if constexpr (!FULL) mask_tail(xv, ok);
+  float s = 0.f;
 #pragma unroll
-      for (int k = 0; k < V; ++k)
+  for (int k = 0; k < V; ++k)
 #pragma unroll
-        for (int e = 0; e < E; ++e) s += elem<T>(xv[k], e);
-      const float mu = wave_sum(s) * inv_d;
+    for (int e = 0; e < E; ++e) s += elem<T>(xv[k], e);
+  const float mu = wave_sum(s) * inv_d;
+  if constexpr (fwd_rows_rewiden(V, E)) {
 #pragma unroll
-      for (int k = 0; k < V; ++k) opaque(xv[k]);
-      float q = 0.f;
+    for (int k = 0; k < V; ++k) opaque(xv[k]);
+  }
+  float q = 0.f;
 #pragma unroll
-      for (int k = 0; k < V; ++k) {
-        if (ok[k]) {
+  for (int k = 0; k < V; ++k) {
+    if (ok[k]) {
 #pragma unroll
-          for (int e = 0; e < E; ++e) {
-            const float c = elem<T>(xv[k], e) - mu;
-            q = fmaf(c, c, q);
-          }
-        }
-      }
-      const float r = 1.0f / sqrtf(wave_sum(q) * inv_d + kEps);
-      if (lane == 0) {
-        mean[row0 + n] = mu;
-        rstd[row0 + n] = r;
-      }
-#pragma unroll
-      for (int k = 0; k < V; ++k) opaque(xv[k]);
-      // Rows of 3 and of 10 or more vectors: widen scale and shift to float
-      // again for every row.  Kept widened across the loop they do not fit
-      // the register budget of the occupancy these rows run at, and the
-      // spills cost more than the conversions (measured: 3-vector bf16 rows
-      // 52 -> 32 us for 77 MB).
-      if constexpr (V == 3 || V >= 10) {
-#pragma unroll
-        for (int k = 0; k < V; ++k) opaque(sv[k]), opaque(hv[k]);
-      }
-      const int64_t off = (row0 + n) * D;
-#pragma unroll
-      for (int k = 0; k < V; ++k) {
-        if (ok[k]) {
-          float o[E];
-#pragma unroll
-          for (int e = 0; e < E; ++e) {
-            const float xh = (elem<T>(xv[k], e) - mu) * r;
-            o[e] = fmaf(xh, 1.0f + elem<T>(sv[k], e), elem<T>(hv[k], e));
-          }
-          store_stream(y + off + (int64_t)jv[k] * E, pack<T>(o));
-        }
-      }
-    };
-
-    int n = k_in * kWaves + wave;
-    if constexpr (PF == 1) {
-      for (; n < N; n += stride) {
-        Vec xv[V];
-        load_row(xv, n);
-        do_row(xv, n);
-      }
-    } else if (n < N) {
-      // the next row of this wavefront is in flight while one is processed;
-      // in the loop body every load is unconditional
-      Vec xa[V], xb[V];
-      load_row(xa, n);
-      for (; n + 2 * stride < N; n += 2 * stride) {
-        load_row(xb, n + stride);
-        do_row(xa, n);
-        load_row(xa, n + 2 * stride);
-        do_row(xb, n + stride);
-      }
-      if (n + stride < N) {
-        load_row(xb, n + stride);
-        do_row(xa, n);
-        do_row(xb, n + stride);
-      } else {
-        do_row(xa, n);
+      for (int e = 0; e < E; ++e) {
+        const float c = elem<T>(xv[k], e) - mu;
+        q = fmaf(c, c, q);
       }
     }
-  });
+  }
+  const float rs = 1.0f / sqrtf(wave_sum(q) * inv_d + kEps);
+  if (lane == 0) {
+    mean[r] = mu;
+    rstd[r] = rs;
+  }
+  if constexpr (fwd_rows_rewiden(V, E)) {
+#pragma unroll
+    for (int k = 0; k < V; ++k) opaque(xv[k]), opaque(sv[k]), opaque(hv[k]);
+  }
+#pragma unroll
+  for (int k = 0; k < V; ++k) {
+    if (ok[k]) {
+      float o[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const float xh = (elem<T>(xv[k], e) - mu) * rs;
+        o[e] = fmaf(xh, 1.0f + elem<T>(sv[k], e), elem<T>(hv[k], e));
+      }
+      store_stream(y + off + (int64_t)jv[k] * E, pack<T>(o));
+    }
+  }
 }
 
 namespace {
 
+// Rows per launch: kMaxGrid four-wavefront workgroups, one row each.
+constexpr int64_t kRowsPerLaunch = kMaxGrid * (kBlock / kWave);
+
 template <typename T, int V, bool FULL, class Map>
-hipError_t fwd_stream_v(int64_t grid, const Map &map, const void *x,
-                        const void *scale, const void *shift, void *y,
-                        float *mean, float *rstd, int32_t D, hipStream_t s) {
-  return launch_kernel(
-      fwd_stream_kernel<T, V, FULL, fwd_stream_pf(V), fwd_stream_occ(V), Map>,
-      grid, s, (const T *)x, (const T *)scale, (const T *)shift, (T *)y, mean,
-      rstd, D, map);
+hipError_t fwd_rows_v(int64_t rows, const Map &map, const void *x,
+                      const void *scale, const void *shift, void *y,
+                      float *mean, float *rstd, int32_t D, hipStream_t s) {
+  for (int64_t first = 0; first < rows; first += kRowsPerLaunch) {
+    const int64_t end =
+        rows - first < kRowsPerLaunch ? rows : first + kRowsPerLaunch;
+    const hipError_t e = launch_kernel(
+        fwd_rows_kernel<T, V, FULL, Map>, (end - first + 3) / 4, s,
+        (const T *)x, (const T *)scale, (const T *)shift, (T *)y, mean, rstd,
+        D, first, end, map);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace
 
-#define ADALN_FWD_STREAM_CASE(V_)                                            \
+#define ADALN_FWD_ROWS_CASE(V_)                                              \
   if (V == V_) {                                                             \
     if (full)                                                                \
-      return dtype == 1 ? fwd_stream_v<bf16, V_, true>(grid, map, x, scale,   \
-                                                       shift, y, mean, rstd,  \
-                                                       D, stream)             \
-                        : fwd_stream_v<float, V_, true>(grid, map, x, scale,  \
-                                                        shift, y, mean, rstd, \
-                                                        D, stream);           \
-    return dtype == 1 ? fwd_stream_v<bf16, V_, false>(grid, map, x, scale,    \
-                                                      shift, y, mean, rstd,   \
-                                                      D, stream)              \
-                      : fwd_stream_v<float, V_, false>(grid, map, x, scale,   \
-                                                       shift, y, mean, rstd,  \
-                                                       D, stream);            \
+      return dtype == 1 ? fwd_rows_v<bf16, V_, true>(rows, map, x, scale,    \
+                                                     shift, y, mean, rstd,   \
+                                                     D, stream)              \
+                        : fwd_rows_v<float, V_, true>(rows, map, x, scale,   \
+                                                      shift, y, mean, rstd,  \
+                                                      D, stream);            \
+    return dtype == 1 ? fwd_rows_v<bf16, V_, false>(rows, map, x, scale,     \
+                                                    shift, y, mean, rstd, D, \
+                                                    stream)                  \
+                      : fwd_rows_v<float, V_, false>(rows, map, x, scale,    \
+                                                     shift, y, mean, rstd,   \
+                                                     D, stream);             \
   }
 
 namespace {
 
 template <class Map>
-hipError_t fwd_stream_dispatch(int dtype, int V, int64_t grid, const Map &map,
-                               const void *x, const void *scale,
-                               const void *shift, void *y, float *mean,
-                               float *rstd, int32_t D, hipStream_t stream) {
+hipError_t fwd_rows_dispatch(int dtype, int V, int64_t rows, const Map &map,
+                             const void *x, const void *scale,
+                             const void *shift, void *y, float *mean,
+                             float *rstd, int32_t D, hipStream_t stream) {
   const int E = dtype == 1 ? 8 : 4;
   const bool full = (int64_t)V * kWave * E == D;
-  ADALN_STREAM_V(ADALN_FWD_STREAM_CASE)
+  ADALN_STREAM_V(ADALN_FWD_ROWS_CASE)
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-hipError_t launch_fwd_stream(int dtype, const StreamPlan &plan, const void *x,
-                             const void *scale, const void *shift, void *y,
-                             float *mean, float *rstd, int32_t B, int32_t N,
-                             int32_t D, hipStream_t stream) {
-  const UniformMap map{B, N, plan.bps, plan.groups, 0};
-  return fwd_stream_dispatch(dtype, plan.V, plan.grid, map, x, scale, shift,
-                             y, mean, rstd, D, stream);
+hipError_t launch_fwd_rows(int dtype, int V, const void *x, const void *scale,
+                           const void *shift, void *y, float *mean,
+                           float *rstd, int32_t B, int32_t N, int32_t D,
+                           hipStream_t stream) {
+  return fwd_rows_dispatch(dtype, V, (int64_t)B * N, BatchRows{N}, x, scale,
+                           shift, y, mean, rstd, D, stream);
 }
 
 hipError_t launch_fwd_segments(int dtype, int V, const SegMap &map,
                                const void *x, const void *scale,
                                const void *shift, void *y, float *mean,
                                float *rstd, int32_t D, hipStream_t stream) {
-  return fwd_stream_dispatch(dtype, V, map.wg_start[map.nseg], map, x, scale,
-                             shift, y, mean, rstd, D, stream);
+  return fwd_rows_dispatch(dtype, V, map.row_start[map.nseg], map, x, scale,
+                           shift, y, mean, rstd, D, stream);
 }
 
 }  // namespace adaln

@@ -39,15 +39,17 @@ struct DmodPlan {
   int n_tiles = 0;
 };
 
-// Row-stream kernels (the forward and the fused backward for rows of up to
-// 1024 vectors): one wavefront per row, lane l holding vectors k*64 + l,
-// k < V.  A persistent grid of `grid` four-wavefront workgroups: the samples
-// are processed `groups` at a time, with `bps` workgroups per sample, and
-// each wavefront walks its sample's rows with a stride of 4*bps.
+// Row-stream kernels (the forward and the fused backward): W wavefronts per
+// row, lane l of wavefront h holding vectors (h*V + k)*64 + l, k < V.  A
+// persistent grid of `grid` four-wavefront workgroups: the samples are
+// processed `groups` at a time, with `bps` workgroups per sample, and each
+// row walker (one wavefront, or the W of a row) walks its sample's rows with
+// a stride of (4/W)*bps.  The forward of one-wavefront rows instead covers
+// the rows with its grid (bps = groups = 0, `grid` workgroups of four rows).
 struct StreamPlan {
   int V = 0;       // vectors per lane
   int W = 1;       // wavefronts per row (2 or 4: rows too wide for one)
-  int grid = 0;
+  int64_t grid = 0;
   int bps = 0;     // workgroups per sample (partial rows per sample)
   int groups = 0;  // samples in flight
   int skew = 0;    // sample b's walk starts (b * skew) % N rows in
@@ -115,19 +117,14 @@ __device__ __forceinline__ void for_each_segment(const SegMap &m, F &&f) {
 #define ADALN_BWD_STREAM_V(X) X(1) X(2) X(3) X(4) X(5)
 constexpr int kMaxStreamVectors = 16 * 64;
 
-// Rows in flight per wavefront (PF) and waves per SIMD (OCC) of each stream
-// kernel instantiation.  OCC also fixes the grid: OCC workgroups per CU.
+// Rows in flight per wavefront (PF) and waves per SIMD (OCC) of each
+// persistent stream kernel instantiation.  OCC also fixes the grid: OCC
+// workgroups per CU.
 // Short rows get two rows in flight and several workgroups per CU to keep
 // enough bytes in flight; long rows get the whole register file of one
 // wavefront per SIMD (the backward's per-lane accumulators need it).  The
 // ADALN_* macros in this part only override the measured choices at build
 // time, to measure the alternatives; the library is built without them.
-#ifndef ADALN_FWD_PF_SHORT
-#define ADALN_FWD_PF_SHORT 2
-#endif
-#ifndef ADALN_FWD_PF_LONG
-#define ADALN_FWD_PF_LONG 2
-#endif
 #ifndef ADALN_BWD_PF_SHORT
 #define ADALN_BWD_PF_SHORT 2
 #endif
@@ -143,18 +140,6 @@ constexpr int kMaxStreamVectors = 16 * 64;
 #ifndef ADALN_BWD_SHORT_V
 #define ADALN_BWD_SHORT_V 3
 #endif
-constexpr int fwd_stream_pf(int V) {
-  return V <= 8 ? ADALN_FWD_PF_SHORT : V <= 12 ? ADALN_FWD_PF_LONG : 1;
-}
-// Forward occupancy per V: the highest of {4, 2, 1} at which the
-// instantiation compiles without register spills.
-constexpr int fwd_stream_occ(int V) {
-#ifdef ADALN_FWD_OCC_ALL
-  return ADALN_FWD_OCC_ALL;
-#else
-  return (V == 1 || V == 3) ? 4 : V <= 4 ? 2 : 1;
-#endif
-}
 constexpr int bwd_stream_pf(int V) {
   return V <= 6 ? ADALN_BWD_PF_SHORT : ADALN_BWD_PF_LONG;
 }
@@ -207,6 +192,15 @@ constexpr bool bwd_wide_split(int V, int E) {
   return E == 4 || V <= 4;
 #endif
 }
+
+// fwd_rows_kernel widens x again for the variance pass and x, scale and
+// shift again for the output where keeping them widened would leave one
+// wavefront per SIMD: bf16 rows of 16 vectors per lane (256 -> 216-244
+// VGPRs, two wavefronts per SIMD).  Measured on MI355X, bf16, D = 8192: 16 x
+// 1560 rows 160.4 -> 143.1 us, 1 x 16384 106.5 -> 96.6 us; at 10 vectors per
+// lane (two -> three wavefronts per SIMD) it costs 5% (1 x 75600 x 5120
+// 256.4 -> 268.1 us), and 6 vectors 3%.
+constexpr bool fwd_rows_rewiden(int V, int E) { return E == 8 && V >= 16; }
 
 // The forward of rows wider than 1024 vectors splits each row between the W
 // wavefronts of a row group (fwd_wide_kernel), V vectors per lane each:
@@ -324,10 +318,12 @@ hipError_t launch_dmod_finish(const float *part_scale,
                               float *dshift, int32_t B, int32_t D,
                               int32_t n_tiles, hipStream_t stream);
 
-hipError_t launch_fwd_stream(int dtype, const StreamPlan &plan, const void *x,
-                             const void *scale, const void *shift, void *y,
-                             float *mean, float *rstd, int32_t B, int32_t N,
-                             int32_t D, hipStream_t stream);
+// The forward of one-wavefront rows (V vectors per lane): one launch per
+// 2^22 rows, one row per wavefront.
+hipError_t launch_fwd_rows(int dtype, int V, const void *x, const void *scale,
+                           const void *shift, void *y, float *mean,
+                           float *rstd, int32_t B, int32_t N, int32_t D,
+                           hipStream_t stream);
 
 hipError_t launch_fwd_wide(int dtype, const StreamPlan &plan, const void *x,
                            const void *scale, const void *shift, void *y,

@@ -73,7 +73,7 @@ KERNEL_SOURCES = {
 # rocprofv3 kernel-name prefixes of each step component (one wavefront per
 # row, or for wider rows several of them)
 KERNEL_SYMBOLS = {
-    "fwd": ("void adaln::fwd_stream_kernel", "void adaln::fwd_wide_kernel"),
+    "fwd": ("void adaln::fwd_rows_kernel", "void adaln::fwd_wide_kernel"),
     "bwd_fused": ("void adaln::bwd_stream_kernel",
                   "void adaln::bwd_wide_kernel"),
     "bwd_finish": ("void adaln::dmod_finish_kernel",),

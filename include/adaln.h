@@ -190,7 +190,11 @@ int adaln_bwd_fused_plan(int64_t B, int64_t N, int64_t D, int dtype,
  * visits the walk positions (g % bps) * walkers + w, then every
  * bps * walkers positions; position n stands for row (n + b * skew) mod N of
  * the sample (skew is 0 except in the backward of many samples).  A walker
- * is one wavefront (W = 1) or the W wavefronts that share a row.  Returns
+ * is one wavefront (W = 1) or the W wavefronts that share a row.  The
+ * forward of rows of up to 1024 vectors (W = 1) has bps = groups = 0 and
+ * covers the B * N rows of the batch with its grid instead: wavefront w of
+ * workgroup g takes row 4 * g + w, in launches of at most 2^20 workgroups;
+ * out[2] counts the workgroups of all of them.  Returns
  * ADALN_ERR_UNSUPPORTED where the entry point would take another path (rows
  * too wide for the fused backward).  Host-only; no HIP call.
  *

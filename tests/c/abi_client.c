@@ -55,7 +55,7 @@ int main(void)
     {
         int64_t p[7];
         CHECK(adaln_plan(0, 1, 75600, 5120, ADALN_BF16, p) == ADALN_OK);
-        CHECK(p[1] == 1 && p[2] == p[3] && p[5] == 4 && p[6] == 0);
+        CHECK(p[1] == 1 && p[2] == 75600 / 4 && p[3] == 0 && p[5] == 4 && p[6] == 0);
         CHECK(adaln_plan(1, 1, 75600, 5120, ADALN_BF16, p) == ADALN_OK);
         CHECK(p[1] == 2 && p[5] == 2);
         CHECK(adaln_plan(1, 16, 1560, 1536, ADALN_BF16, p) == ADALN_OK);

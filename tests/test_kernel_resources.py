@@ -45,10 +45,10 @@ def usage(tmp_path_factory):
     return out
 
 
-def test_forward_stream_kernels_do_not_spill(usage):
+def test_forward_row_kernels_do_not_spill(usage):
     stream = {k: v for k, v in usage["fwd.hip"].items()
-              if "fwd_stream_kernel" in k}
-    assert len(stream) >= 40
+              if "fwd_rows_kernel" in k}
+    assert len(stream) >= 80
     spills = {k: v for k, v in stream.items() if v}
     assert not spills, spills
 

@@ -1,13 +1,14 @@
 """The launch planner, on the host: for seeded random shapes over every
 kernel family, the plans adaln_plan reports, replayed through the work
-mapping the header documents (workgroup g -> samples g / bps, + groups, ...;
-walker w -> rows (g % bps) * walkers + w, + bps * walkers, ...), visit every
-token row exactly once, fit the resident grid, and for the fused backward
-give each (sample, workgroup) pair its own partial row inside the
-workspace.  The shape-dependent choices are pinned too: the wavefront
-pairs past 320 vectors, the fewest long samples in flight (forward and
-paired backward),
-and the balanced workgroups per sample.  CPU only."""
+mapping the header documents (persistent grids: workgroup g -> samples
+g / bps, + groups, ...; walker w -> rows (g % bps) * walkers + w,
++ bps * walkers, ...; the forward of one-wavefront rows: wavefront w of
+workgroup g -> row 4g + w of the batch), visit every token row exactly once,
+fit the resident grid, and for the fused backward give each (sample,
+workgroup) pair its own partial row inside the workspace.  The
+shape-dependent choices are pinned too: the wavefront pairs past 320
+vectors, the fewest long samples in flight (wide forward and paired
+backward), and the balanced workgroups per sample.  CPU only."""
 
 import numpy as np
 import pytest
@@ -64,6 +65,15 @@ def test_every_row_once(B, N, D, dt):
             assert which == "bwd" and e.code == -6
             assert D // (8 if dt is BF16 else 4) > 2560
             continue
+        if which == "fwd" and p["waves_per_row"] == 1:
+            # a grid over the rows: wavefront w of workgroup g -> row 4g + w
+            assert p["bps"] == 0 and p["groups"] == 0 and p["walkers"] == 4
+            assert p["workgroups"] == -(-B * N // 4)
+            rows = (4 * np.arange(p["workgroups"])[:, None]
+                    + np.arange(4)[None, :]).ravel()
+            rows = rows[rows < B * N]
+            assert np.all(np.bincount(rows, minlength=B * N) == 1)
+            continue
         assert 1 <= p["bps"] and 1 <= p["groups"]
         assert p["workgroups"] == p["bps"] * min(p["groups"], B)
         assert p["bps"] * p["groups"] <= MAX_GRID
@@ -105,17 +115,27 @@ def test_rows_past_320_vectors_take_pairs():
         assert p["waves_per_row"] == w and p["walkers"] == 4 // w, (D, p)
 
 
+def test_forward_rows_take_a_grid_over_the_rows():
+    # one wavefront per row up to 1024 vectors, every row its own wavefront
+    for B, N, D, dt in ((16, 1560, 1536, BF16), (1, 75600, 5120, BF16),
+                        (84, 1560, 3072, BF16), (5, 7, 8192, BF16),
+                        (3, 5, 4096, F32), (2, 256, 64, F32)):
+        p = A.plan("fwd", B, N, D, dt)
+        assert p["waves_per_row"] == 1 and p["bps"] == 0, (B, N, D, p)
+        assert p["workgroups"] == -(-B * N // 4)
+
+
 def test_long_samples_fewer_in_flight():
-    # 16 samples of 8190 rows at D = 3072: four in flight (4 each in turn);
-    # two would leave a wavefront 15.99 rows of a sample
-    p = A.plan("fwd", 16, 8190, 3072, BF16)
-    assert p["groups"] == 4
+    # the wide forward (pairs of wavefronts, D = 12288), 16 samples of 8190
+    # rows: two in flight (8 each in turn), 32 rows per pair
+    p = A.plan("fwd", 16, 8190, 12288, BF16)
+    assert p["walkers"] == 2 and p["groups"] == 2
     assert 8190 / (p["bps"] * p["walkers"]) >= 16
-    # 8 samples of 16380 rows: two in flight, 32 rows per wavefront each
-    p = A.plan("fwd", 8, 16380, 3072, BF16)
-    assert p["groups"] == 2 and 16380 / (p["bps"] * p["walkers"]) >= 16
+    # 8 samples of 16380 rows: one in flight
+    p = A.plan("fwd", 8, 16380, 12288, BF16)
+    assert p["groups"] == 1 and 16380 / (p["bps"] * p["walkers"]) >= 16
     # short samples keep one group each
-    assert A.plan("fwd", 84, 1560, 3072, BF16)["groups"] >= 84
+    assert A.plan("fwd", 84, 1560, 12288, BF16)["groups"] >= 84
     assert A.plan("bwd", 84, 1560, 3072, BF16)["groups"] >= 84
     # the backward with pairs of wavefronts per row (2 walkers per
     # workgroup) follows the same rule: 16 rows per pair
