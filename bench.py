@@ -732,7 +732,9 @@ def stream_probe(args) -> int:
 
     # The same bytes walked in the kernels' sample windows (grid and bps of
     # the forward's plan for the copy, of the backward's for two reads + one
-    # write), at several skews, beside one flat window over the batch.
+    # write), at several skews, beside one flat window over the batch.  The
+    # forward of one-wavefront rows has no sample windows (bps 0): its grid
+    # covers the rows, which the flat case with bps = grid walks the same way.
     row = wl.D * esize
     if row % 1024 == 0 and 1 <= row // 1024 <= 10:
         rk = row // 1024
@@ -743,7 +745,7 @@ def stream_probe(args) -> int:
             pl = A.plan(op, wl.B, wl.N, wl.D, dt)
             grid, bps = pl["workgroups"], pl["bps"]
             cases = [(1, wl.B * wl.N, grid, 0)]
-            if wl.B > 1:
+            if wl.B > 1 and bps > 0:
                 cases += [(wl.B, wl.N, bps, sk)
                           for sk in sorted({0, 64, 97, pl.get("skew", 0)})]
             for B_, N_, bps_, sk in cases:
