@@ -108,6 +108,26 @@ def test_shapes(A, B, N, D, dtype, kind):
     _run_full(A, wl, seed=B + N + D)
 
 
+@pytest.mark.parametrize("B,N,D,dtype", [
+    (3, 1_500_001, 8, "bf16"),   # 4,500,003 rows: two launches
+    (1, 4_194_305, 16, "f32"),   # one row past the first launch
+])
+def test_forward_launches_past_2_22_rows(A, B, N, D, dtype):
+    """The forward of one-wavefront rows takes one launch per 2^22 rows:
+    every row of batches that need a second launch (the rows on either side
+    of the launch boundary among them), with the backward, and dscale and
+    dshift in full.  The f32 case has rows of 16 features: among 4.19 M
+    rows of 4 N(0, 1) features some have a variance near 1e-3 of their mean
+    square (rstd up to ~140), where float32 arithmetic in any order exceeds
+    the float32 tolerance against the float64 oracle (a float32 emulation of
+    the kernels' order, which the GPU matches bit for bit there, 5.5x)."""
+    assert B * N > 1 << 22
+    wl = W.custom(B, N, D, dtype, x_kind="normal",
+                  dy_std=1e-2 if dtype == "bf16" else 1.0)
+    _say(f"{B}x{N}x{D} {dtype}: {B * N} rows, every row")
+    _run_all_rows(A, wl)
+
+
 def _run_all_rows(A, wl):
     inp = synth.make_inputs(wl)
     dev = P.to_device(inp)

@@ -241,6 +241,17 @@ def test_mmdit_layout_full_size(A):
     _full_size(A, inp, "two-stream layout")
 
 
+def test_forward_launches_past_2_22_rows(A):
+    """Packed rows past one launch of the forward's row grid (2^22 rows):
+    the middle segment spans the launch boundary; every row and
+    dscale/dshift against the oracle."""
+    lengths = [4_000_000, 194_305, 1000]
+    assert lengths[0] < 1 << 22 < lengths[0] + lengths[1]
+    inp = synth.make_packed(_wl(8, "bf16", x_kind="normal"), lengths,
+                            [1, 0, 1], nmod=2, seed=5)
+    _full_size(A, inp, "pack past one forward launch")
+
+
 def _random_tables(seed, count):
     g = np.random.default_rng(seed)
     out = []
