@@ -75,7 +75,8 @@ typedef enum adaln_dtype { ADALN_F32 = 0, ADALN_BF16 = 1 } adaln_dtype_t;
 #define ADALN_EUNSUPPORTED ADALN_ERR_UNSUPPORTED
 
 /*
- * Forward pass: mean, rstd and y for every token row, one kernel launch.
+ * Forward pass: mean, rstd and y for every token row, one kernel launch
+ * (for rows of up to 1024 vectors, one per 2^22 rows of the batch).
  * Section 2.B, forward pass: the row statistics stay in registers (and LDS
  * when several wavefronts share a row) and the modulation is applied on the
  * pass that writes y.
@@ -245,7 +246,8 @@ int adaln_bwd_dmod(const void *dy, const void *x, const float *mean,
 /*
  * Packed variable-length AdaLN: the token rows of several sequences
  * ("segments") concatenated in one [T, D] tensor and processed in one launch
- * per pass -- mixed-length samples of a bucket without padding, or the text
+ * per pass (the forward of rows of up to 1024 vectors: one per 2^22 rows)
+ * -- mixed-length samples of a bucket without padding, or the text
  * and video token segments of MMDiT samples, each with its own modulation.
  *   seg_offsets  host int64 [nseg+1]: segment s is rows [off[s], off[s+1]);
  *                off[0] = 0, non-decreasing, T = off[nseg] < 2^31
