@@ -321,7 +321,8 @@ bool plan_segments(const int64_t *off, const int32_t *mod, int64_t nseg,
                    int64_t nvec, bool bwd, SegMap *map, StreamPlan *plan) {
   StreamPlan sp;
   if (!choose_stream_plan(1, 1, nvec, bwd, &sp)) return false;
-  // the forward of one-wavefront rows reads only the rows and vectors
+  // (the forward of one-wavefront rows uses only the table's row and vector
+  // columns: its grid covers the rows)
   build_segment_map(off, mod, nseg, (int64_t)kCUs * stream_occ(sp, bwd), map);
   *plan = sp;
   return true;
