@@ -132,13 +132,20 @@ __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void bwd_stream_kernel(
       }
     };
 
+    // The walk compares n with N - stride rather than n + stride with N, so
+    // that no position past N is ever formed: near N = 2^31 - 1 that sum
+    // would overflow.
     int n = k_in * kWaves + wave;
     if constexpr (PF == 1) {
-      for (; n < N; n += stride) {
-        Vec xv[V], gv[V];
-        float st[2];
-        load_row(xv, gv, st, n);
-        do_row(xv, gv, st, n);
+      if (n < N) {
+        for (;;) {
+          Vec xv[V], gv[V];
+          float st[2];
+          load_row(xv, gv, st, n);
+          do_row(xv, gv, st, n);
+          if (n >= N - stride) break;
+          n += stride;
+        }
       }
     } else if (n < N) {
       // the wavefront's next row is in flight while one is processed; in the
@@ -146,13 +153,13 @@ __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void bwd_stream_kernel(
       Vec xa[V], ga[V], xb[V], gb[V];
       float sa[2], sb[2];
       load_row(xa, ga, sa, n);
-      for (; n + 2 * stride < N; n += 2 * stride) {
+      for (; n < N - 2 * stride; n += 2 * stride) {
         load_row(xb, gb, sb, n + stride);
         do_row(xa, ga, sa, n);
         load_row(xa, ga, sa, n + 2 * stride);
         do_row(xb, gb, sb, n + stride);
       }
-      if (n + stride < N) {
+      if (n < N - stride) {
         load_row(xb, gb, sb, n + stride);
         do_row(xa, ga, sa, n);
         do_row(xb, gb, sb, n + stride);

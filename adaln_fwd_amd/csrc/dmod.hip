@@ -40,15 +40,20 @@ __global__ __launch_bounds__(kBlock) void dmod_partial_kernel(
     const int b = (int)(rest / n_tiles);
     const int j = dt * kWave + lane;  // this lane's vector of the row
     const bool ok = j < nvec;
+    // No position past the tile end is formed: near N = 2^31 - 1 it would
+    // overflow 32 bits.  steps: walk positions of this wavefront in the tile.
     const int n0 = t * n_tile;
-    const int n1 = min(N, n0 + n_tile);
+    const int n1 = (int)((int64_t)n0 + n_tile < N ? (int64_t)n0 + n_tile : N);
+    constexpr int kStep = kWaves * U;
+    const int steps = n1 - n0 > wave ? (n1 - n0 - wave - 1) / kStep + 1 : 0;
     const int64_t row0 = (int64_t)b * N;
 
     float acc_s[E], acc_h[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) acc_s[e] = acc_h[e] = 0.f;
 
-    for (int n = n0 + wave; n < n1; n += kWaves * U) {
+    for (int i = 0; i < steps; ++i) {
+      const int n = n0 + wave + i * kStep;
       Vec xv[U], gv[U];
       float mu[U], r[U];
       bool in[U];
@@ -56,8 +61,8 @@ __global__ __launch_bounds__(kBlock) void dmod_partial_kernel(
       for (int u = 0; u < U; ++u) {
         // no predicate on the loads: rows past the tile and vectors past the
         // row end read a valid address, and are zeroed before their use
-        const int nn = n + u * kWaves;
-        const bool live = nn < n1;
+        const bool live = u * kWaves < n1 - n;
+        const int nn = live ? n + u * kWaves : n0;
         in[u] = live && ok;
         const int64_t off =
             (row0 + (live ? nn : n0)) * D + (int64_t)clamp_vec(j, nvec) * E;

@@ -47,15 +47,19 @@ __global__ __launch_bounds__(kBlock) void dx_kernel(
   const int grp = wave / W;
   const int wig = wave - grp * W;
   const int nvec = D / E;
-  const int row_blocks = (rows + G - 1) / G;
+  // 64-bit: near rows = 2^31 - 1 the rounding up and the last block's rows
+  // would overflow 32 bits
+  const int row_blocks = (int)(((int64_t)rows + G - 1) / G);
   const float inv_d = 1.0f / (float)D;
   int parity = 0;
 
   for (int rb = blockIdx.x; rb < row_blocks; rb += gridDim.x) {
-    const int row = rb * G + grp;
+    const int64_t row = (int64_t)rb * G + grp;
     const bool live = row < rows;
     const int64_t off = (int64_t)(live ? row : 0) * D;
-    const int64_t moff = (int64_t)(live ? row / N : 0) * D;
+    // row < rows <= 2^31 - 1: the sample index in 32-bit arithmetic
+    const int64_t moff =
+        (int64_t)(live ? (int)((uint32_t)row / (uint32_t)N) : 0) * D;
 
     // Loads with no predicate (vectors past the row end read its last
     // vector, and are zeroed before their first use) where the registers
