@@ -12,19 +12,18 @@
 // feature it holds: its lanes are pinned to their features for every row it
 // visits, and each of its loads covers 1 KiB of contiguous memory.
 //
-// Grid: as in the forward stream kernel, a small persistent grid (OCC
-// four-wavefront workgroups per CU) is spread over the samples, bps
-// workgroups per sample, and each wavefront walks its sample's rows with a
-// stride of 4*bps rows, so the active wavefronts sweep a narrow window of
-// memory in order.  The set of rows a workgroup visits in one sample is its
-// sequence tile.  With many samples, sample b's walk starts (b * skew) % N
-// rows in and wraps around (the planner's skew; rot below), so that the
-// samples' windows are not aligned with each other in memory.  At the end
-// of a sample the four wavefronts' accumulators
-// are added in wavefront order through LDS and written as one partial row
-// per (sample, workgroup): the workspace holds [B, bps, D] partial sums for
-// dscale and for dshift, which dmod_finish_kernel adds over the bps
-// workgroups in index order.  No floating-point atomics anywhere.
+// Grid: a small persistent grid (OCC four-wavefront workgroups per CU) is
+// spread over the samples, bps workgroups per sample, and each wavefront
+// walks its sample's rows with a stride of 4*bps rows, so the active
+// wavefronts sweep a narrow window of memory in order.  The set of rows a
+// workgroup visits in one sample is its sequence tile.  With many samples,
+// sample b's walk starts (b * skew) % N rows in and wraps around (the
+// planner's skew; rot below), so that the samples' windows are not aligned
+// with each other in memory.  At the end of a sample the four wavefronts'
+// accumulators are added in wavefront order through LDS and written as one
+// partial row per (sample, workgroup): the workspace holds [B, bps, D]
+// partial sums for dscale and for dshift, which dmod_finish_kernel adds over
+// the bps workgroups in index order.  No floating-point atomics anywhere.
 #include "common.hpp"
 #include "launch.hpp"
 

@@ -11,11 +11,12 @@
 // rows, nontemporal 16-byte loads and stores, every lane one vector per
 // instruction.
 //
-// bench_window_probe walks the rows the way the kernels walk a batch of B
-// samples: bps workgroups per sample, grid / bps samples in flight, the
-// wavefronts of a sample's workgroups taking rows k_in*4 + w, stride 4*bps,
-// from (b * skew) % N rows in (wrapping).  Same two kinds, rows of 1 to 10
-// KiB.
+// bench_window_probe walks the rows the way the persistent kernels (the
+// backward's) walk a batch of B samples: bps workgroups per sample, grid /
+// bps samples in flight, the wavefronts of a sample's workgroups taking rows
+// k_in*4 + w, stride 4*bps, from (b * skew) % N rows in (wrapping); with one
+// sample and bps = grid = rows / 4 it is the forward's grid of one row per
+// wavefront.  Same two kinds, rows of 1 to 10 KiB.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
