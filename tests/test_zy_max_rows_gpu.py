@@ -56,8 +56,11 @@ def _rows_of(t, rows_t):
 
 
 def test_max_rows(A):
-    assert torch.cuda.get_device_properties(0).total_memory > 160e9, \
-        "needs about 140 GB of device memory"
+    torch.cuda.empty_cache()
+    free, _ = torch.cuda.mem_get_info()
+    if free < 130e9:
+        pytest.skip(f"needs about 130 GB of free device memory, {free / 1e9:.0f} "
+                    "GB free")
     wl = W.custom(1, BASE, D, "bf16", x_kind="normal")
     base = synth.make_inputs(wl, seed=7)
     bx = base.x.reshape(BASE, D)
