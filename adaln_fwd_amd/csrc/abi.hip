@@ -153,11 +153,12 @@ DmodPlan choose_dmod_plan(int64_t B, int64_t N, int64_t nvec) {
 // 1280; the forward takes a pair past 1024 and four past 1536).  V is the
 // smallest instantiated count that holds the row.
 //
-// The forward of one-wavefront rows covers the rows with its grid, one row
-// per wavefront: ceil(B * N / 4) workgroups in all (fwd_rows_kernel, fwd.hip,
-// has the measurements).
+// The forward covers the rows with its grid, one row per row walker (a
+// wavefront, or the W wavefronts sharing a row): ceil(B * N * W / 4)
+// workgroups in all (fwd_rows_kernel and fwd_wide_kernel have the
+// measurements).
 //
-// The other kernels run a persistent grid: the occupancy OCC fixes G = 256 *
+// The backward runs a persistent grid: the occupancy OCC fixes G = 256 *
 // OCC workgroups (OCC per CU on a 256-CU MI355X), spread over the samples:
 // up to G / B workgroups per sample (at least one), `groups` = G / bps
 // samples in flight.  Of the counts that keep the most rows any row walker (a
@@ -168,9 +169,6 @@ DmodPlan choose_dmod_plan(int64_t B, int64_t N, int64_t nvec) {
 // size ([B, bps, D] partial sums of the backward) is a pure function of it;
 // on a part with another CU count the kernels remain correct and only use
 // the GPU less evenly.
-#ifndef ADALN_FWD_MIN_BPS
-#define ADALN_FWD_MIN_BPS 1
-#endif
 #ifndef ADALN_BWD_MIN_BPS
 #define ADALN_BWD_MIN_BPS 1
 #endif
@@ -189,18 +187,13 @@ DmodPlan choose_dmod_plan(int64_t B, int64_t N, int64_t nvec) {
 constexpr int kBwdSkewRows = 97;
 constexpr int64_t kBwdSkewMinSamples = 16;
 
-// Samples of at least this many rows count as long for a persistent plan.
+// Samples of at least this many rows count as long for the backward's plan.
 constexpr int64_t kLongSample = 4096;
 
-// Waves per SIMD (and so workgroups per CU) a persistent plan's kernel runs
-// at.
-int stream_occ(const StreamPlan &p, bool bwd) {
-  if (!bwd) return fwd_wide_occ(p.V);
+// Waves per SIMD (and so workgroups per CU) the backward's kernel runs at.
+int stream_occ(const StreamPlan &p) {
   return p.W > 1 ? bwd_wide_occ(p.V) : bwd_stream_occ(p.V);
 }
-
-// The forward's one-row-per-wavefront kernel: a grid over the rows.
-bool rows_grid(const StreamPlan &p, bool bwd) { return !bwd && p.W == 1; }
 
 bool choose_stream_plan(int64_t B, int64_t N, int64_t nvec, bool bwd,
                         StreamPlan *plan) {
@@ -235,24 +228,25 @@ bool choose_stream_plan(int64_t B, int64_t N, int64_t nvec, bool bwd,
 #undef ADALN_QUAD_PLAN_CASE
   }
   if (p.V == 0) return false;
-  if (rows_grid(p, bwd)) {
-    p.grid = (B * N + 3) / 4;  // one row per wavefront
+  if (!bwd) {
+    const int64_t walkers = 4 / p.W;  // rows a workgroup covers
+    p.grid = (B * N + walkers - 1) / walkers;
   } else if (B > 0 && N > 0) {
-    const int occ = stream_occ(p, bwd);
+    const int occ = stream_occ(p);
     const int64_t G = (int64_t)kCUs * occ;
-    const int64_t min_bps = bwd ? ADALN_BWD_MIN_BPS : ADALN_FWD_MIN_BPS;
+    const int64_t min_bps = ADALN_BWD_MIN_BPS;
     int64_t bps = G / B > 1 ? G / B : 1;
     const int64_t walkers = 4 / p.W;  // row walkers per workgroup
-    if (B > 1 && N >= kLongSample && (!bwd || p.W > 1)) {
+    if (B > 1 && N >= kLongSample && p.W > 1) {
       // Long samples: the fewest samples in flight (g, a divisor of B, so
       // every group slot walks B / g samples) that still give each row
-      // walker 16 rows of a sample (the wide forward and the backward with
-      // pairs or quads of wavefronts per row).  Measured on MI355X, D =
-      // 3072, whole backward with pairs of wavefronts per row, although every
-      // extra workgroup on a sample costs a partial row: 16 x 8190 443 -> 431
-      // us, 8 x 16380 444 -> 424 us, 4 x 32760 424 -> 422 us.  For samples
-      // of 1560 tokens fewer in flight is slower, hence the length threshold;
-      // the one-wavefront backward keeps one sample per slot.
+      // walker 16 rows of a sample (the backward with pairs or quads of
+      // wavefronts per row).  Measured on MI355X, D = 3072, whole backward
+      // with pairs of wavefronts per row, although every extra workgroup on
+      // a sample costs a partial row: 16 x 8190 443 -> 431 us, 8 x 16380
+      // 444 -> 424 us, 4 x 32760 424 -> 422 us.  For samples of 1560 tokens
+      // fewer in flight is slower, hence the length threshold; the
+      // one-wavefront backward keeps one sample per slot.
       for (int64_t g = 1; g < B && g <= G; ++g) {
         if (B % g == 0 && G / g <= N / (16 * walkers)) {
           bps = G / g;
@@ -268,7 +262,7 @@ bool choose_stream_plan(int64_t B, int64_t N, int64_t nvec, bool bwd,
     p.bps = (int)bps;
     p.groups = (int)groups;
     p.grid = (int)(bps * (groups < B ? groups : B));
-    if (bwd && p.W == 1 && B >= kBwdSkewMinSamples) p.skew = kBwdSkewRows;
+    if (p.W == 1 && B >= kBwdSkewMinSamples) p.skew = kBwdSkewRows;
   }
   *plan = p;
   return true;
@@ -321,9 +315,10 @@ bool plan_segments(const int64_t *off, const int32_t *mod, int64_t nseg,
                    int64_t nvec, bool bwd, SegMap *map, StreamPlan *plan) {
   StreamPlan sp;
   if (!choose_stream_plan(1, 1, nvec, bwd, &sp)) return false;
-  // (the forward of one-wavefront rows uses only the table's row and vector
-  // columns: its grid covers the rows)
-  build_segment_map(off, mod, nseg, (int64_t)kCUs * stream_occ(sp, bwd), map);
+  // (the forward uses only the table's row and vector columns: its grid
+  // covers the rows)
+  build_segment_map(off, mod, nseg, (int64_t)kCUs * (bwd ? stream_occ(sp) : 1),
+                    map);
   *plan = sp;
   return true;
 }

@@ -31,30 +31,6 @@
 
 namespace adaln {
 
-// Row -> modulation vector.  BatchRows: B samples of N rows.
-struct BatchRows {
-  int32_t N;
-};
-
-__device__ __forceinline__ int row_mod(const BatchRows &m, int64_t r) {
-  return r < INT32_MAX ? (int)((uint32_t)r / (uint32_t)m.N)
-                       : (int)(r / m.N);
-}
-
-// SegMap: the segment s with row_start[s] <= r < row_start[s + 1] (the last
-// s with row_start[s] <= r skips the empty segments before it).
-__device__ __forceinline__ int row_mod(const SegMap &m, int64_t r) {
-  int lo = 0, hi = m.nseg - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) / 2;
-    if (m.row_start[mid] <= r)
-      lo = mid;
-    else
-      hi = mid - 1;
-  }
-  return m.mod[lo];
-}
-
 template <typename T, int V, bool FULL, class Map>
 __global__ __launch_bounds__(kBlock) void fwd_rows_kernel(
     const T *__restrict__ x, const T *__restrict__ scale,

@@ -44,8 +44,8 @@ struct DmodPlan {
 // persistent grid of `grid` four-wavefront workgroups: the samples are
 // processed `groups` at a time, with `bps` workgroups per sample, and each
 // row walker (one wavefront, or the W of a row) walks its sample's rows with
-// a stride of (4/W)*bps.  The forward of one-wavefront rows instead covers
-// the rows with its grid (bps = groups = 0, `grid` workgroups of four rows).
+// a stride of (4/W)*bps.  The forward instead covers the rows with its grid
+// (bps = groups = 0, `grid` workgroups of 4/W rows).
 struct StreamPlan {
   int V = 0;       // vectors per lane
   int W = 1;       // wavefronts per row (2 or 4: rows too wide for one)
@@ -79,6 +79,29 @@ struct SegMap {
   int64_t row_start[kMaxSegments + 1];
 };
 
+// Token row -> modulation vector, for the forward's grids over the rows.
+// BatchRows: B samples of N rows (row r belongs to sample r / N; B * N <=
+// 2^31 - 1).  SegMap: the segment s with row_start[s] <= r < row_start[s+1]
+// (the last s with row_start[s] <= r skips the empty segments before it).
+struct BatchRows {
+  int32_t N;
+};
+
+__device__ __forceinline__ int row_mod(const BatchRows &m, int64_t r) {
+  return (int)((uint32_t)r / (uint32_t)m.N);
+}
+
+__device__ __forceinline__ int row_mod(const SegMap &m, int64_t r) {
+  int lo = 0, hi = m.nseg - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) / 2;
+    if (m.row_start[mid] <= r)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  return m.mod[lo];
+}
 
 // Calls f(row0, rows, mod, k_in, bps, part_row, rot) for each segment the
 // calling workgroup works on; a kernel visits the segment's rows in the
@@ -193,10 +216,10 @@ constexpr bool bwd_wide_split(int V, int E) {
 #endif
 }
 
-// fwd_rows_kernel widens x again for the variance pass and x, scale and
-// shift again for the output where keeping them widened would leave one
-// wavefront per SIMD: bf16 rows of 16 vectors per lane (256 -> 216-244
-// VGPRs, two wavefronts per SIMD).  Measured on MI355X, bf16, D = 8192: 16 x
+// The forward kernels (fwd_rows_kernel, fwd_wide_kernel) widen x again for
+// the variance pass and x, scale and shift again for the output where keeping
+// them widened would leave one wavefront per SIMD: bf16 rows of 16 vectors
+// per lane (256 -> 216-252 VGPRs, two wavefronts per SIMD).  Measured on MI355X, bf16, D = 8192: 16 x
 // 1560 rows 160.4 -> 143.1 us, 1 x 16384 106.5 -> 96.6 us; at 10 vectors per
 // lane (two -> three wavefronts per SIMD) it costs 5% (1 x 75600 x 5120
 // 256.4 -> 268.1 us), and 6 vectors 3%.
@@ -204,25 +227,9 @@ constexpr bool fwd_rows_rewiden(int V, int E) { return E == 8 && V >= 16; }
 
 // The forward of rows wider than 1024 vectors splits each row between the W
 // wavefronts of a row group (fwd_wide_kernel), V vectors per lane each:
-// pairs up to 1536 vectors, quads up to 4096.  One wavefront per SIMD; the
-// next row in flight where it fits the registers (V <= 12).
+// pairs up to 1536 vectors, quads up to 4096.
 #define ADALN_FWD_PAIR_V(X) X(10) X(12)
 #define ADALN_FWD_QUAD_V(X) X(8) X(10) X(12) X(16)
-constexpr int fwd_wide_occ(int) { return 1; }
-constexpr int fwd_wide_pf(int V) {
-#ifdef ADALN_FWD_WIDE_PF2
-  return 2;
-#else
-  return V <= 12 ? 2 : 1;
-#endif
-}
-constexpr bool fwd_wide_rewiden(int V, int E) {
-#ifdef ADALN_FWD_WIDE_REWIDEN
-  return true;
-#else
-  return E == 8 && V >= 12;
-#endif
-}
 
 constexpr int kCUs = 256;  // compute units of an MI355X
 

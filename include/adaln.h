@@ -76,7 +76,8 @@ typedef enum adaln_dtype { ADALN_F32 = 0, ADALN_BF16 = 1 } adaln_dtype_t;
 
 /*
  * Forward pass: mean, rstd and y for every token row, one kernel launch
- * (for rows of up to 1024 vectors, one per 2^22 rows of the batch).
+ * (one per 2^20 workgroups: per 2^22 rows of up to 1024 vectors, 2^21 of up
+ * to 1536, 2^20 wider).
  * Section 2.B, forward pass: the row statistics stay in registers (and LDS
  * when several wavefronts share a row) and the modulation is applied on the
  * pass that writes y.
@@ -192,10 +193,10 @@ int adaln_bwd_fused_plan(int64_t B, int64_t N, int64_t D, int dtype,
  * bps * walkers positions; position n stands for row (n + b * skew) mod N of
  * the sample (skew is 0 except in the backward of many samples).  A walker
  * is one wavefront (W = 1) or the W wavefronts that share a row.  The
- * forward of rows of up to 1024 vectors (W = 1) has bps = groups = 0 and
- * covers the B * N rows of the batch with its grid instead: wavefront w of
- * workgroup g takes row 4 * g + w, in launches of at most 2^20 workgroups;
- * out[2] counts the workgroups of all of them.  Returns
+ * forward has bps = groups = 0 and covers the B * N rows of the batch with
+ * its grid instead: walker j of workgroup g takes row (4 / W) * g + j, in
+ * launches of at most 2^20 workgroups; out[2] counts the workgroups of all
+ * of them.  Returns
  * ADALN_ERR_UNSUPPORTED where the entry point would take another path (rows
  * too wide for the fused backward).  Host-only; no HIP call.
  *
@@ -246,7 +247,7 @@ int adaln_bwd_dmod(const void *dy, const void *x, const float *mean,
 /*
  * Packed variable-length AdaLN: the token rows of several sequences
  * ("segments") concatenated in one [T, D] tensor and processed in one launch
- * per pass (the forward of rows of up to 1024 vectors: one per 2^22 rows)
+ * per pass (the forward: one per 2^20 workgroups, as in adaln_fwd)
  * -- mixed-length samples of a bucket without padding, or the text
  * and video token segments of MMDiT samples, each with its own modulation.
  *   seg_offsets  host int64 [nseg+1]: segment s is rows [off[s], off[s+1]);

@@ -1,14 +1,14 @@
 """The launch planner, on the host: for seeded random shapes over every
 kernel family, the plans adaln_plan reports, replayed through the work
-mapping the header documents (persistent grids: workgroup g -> samples
-g / bps, + groups, ...; walker w -> rows (g % bps) * walkers + w,
-+ bps * walkers, ...; the forward of one-wavefront rows: wavefront w of
-workgroup g -> row 4g + w of the batch), visit every token row exactly once,
-fit the resident grid, and for the fused backward give each (sample,
-workgroup) pair its own partial row inside the workspace.  The
-shape-dependent choices are pinned too: the wavefront pairs past 320
-vectors, the fewest long samples in flight (wide forward and paired
-backward), and the balanced workgroups per sample.  CPU only."""
+mapping the header documents (the backward's persistent grids: workgroup
+g -> samples g / bps, + groups, ...; walker w -> rows (g % bps) * walkers
++ w, + bps * walkers, ...; the forward: walker w of workgroup g -> row
+(4/W)g + w of the batch), visit every token row exactly once, fit the
+resident grid, and for the fused backward give each (sample, workgroup)
+pair its own partial row inside the workspace.  The shape-dependent choices
+are pinned too: the wavefront pairs past 320 vectors, the fewest long
+samples in flight (paired backward), and the balanced workgroups per
+sample.  CPU only."""
 
 import numpy as np
 import pytest
@@ -65,12 +65,15 @@ def test_every_row_once(B, N, D, dt):
             assert which == "bwd" and e.code == -6
             assert D // (8 if dt is BF16 else 4) > 2560
             continue
-        if which == "fwd" and p["waves_per_row"] == 1:
-            # a grid over the rows: wavefront w of workgroup g -> row 4g + w
-            assert p["bps"] == 0 and p["groups"] == 0 and p["walkers"] == 4
-            assert p["workgroups"] == -(-B * N // 4)
-            rows = (4 * np.arange(p["workgroups"])[:, None]
-                    + np.arange(4)[None, :]).ravel()
+        if which == "fwd":
+            # a grid over the rows: walker j of workgroup g -> row wg + j,
+            # w = 4 / W walkers (one row each) per workgroup
+            w = p["walkers"]
+            assert p["bps"] == 0 and p["groups"] == 0
+            assert w * p["waves_per_row"] == 4
+            assert p["workgroups"] == -(-B * N // w)
+            rows = (w * np.arange(p["workgroups"])[:, None]
+                    + np.arange(w)[None, :]).ravel()
             rows = rows[rows < B * N]
             assert np.all(np.bincount(rows, minlength=B * N) == 1)
             continue
@@ -116,26 +119,20 @@ def test_rows_past_320_vectors_take_pairs():
 
 
 def test_forward_rows_take_a_grid_over_the_rows():
-    # one wavefront per row up to 1024 vectors, every row its own wavefront
-    for B, N, D, dt in ((16, 1560, 1536, BF16), (1, 75600, 5120, BF16),
-                        (84, 1560, 3072, BF16), (5, 7, 8192, BF16),
-                        (3, 5, 4096, F32), (2, 256, 64, F32)):
+    # every row its own row walker: one wavefront up to 1024 vectors, a pair
+    # or a quad of wavefronts beyond (4 / W rows per workgroup)
+    for B, N, D, dt, W in ((16, 1560, 1536, BF16, 1), (1, 75600, 5120, BF16, 1),
+                           (84, 1560, 3072, BF16, 1), (5, 7, 8192, BF16, 1),
+                           (3, 5, 4096, F32, 1), (2, 256, 64, F32, 1),
+                           (16, 8190, 12288, BF16, 2), (3, 7, 6144, F32, 2),
+                           (1, 8192, 32768, BF16, 4), (5, 3, 16384, F32, 4)):
         p = A.plan("fwd", B, N, D, dt)
-        assert p["waves_per_row"] == 1 and p["bps"] == 0, (B, N, D, p)
-        assert p["workgroups"] == -(-B * N // 4)
+        assert p["waves_per_row"] == W and p["bps"] == 0, (B, N, D, p)
+        assert p["workgroups"] == -(-B * N * W // 4)
 
 
 def test_long_samples_fewer_in_flight():
-    # the wide forward (pairs of wavefronts, D = 12288), 16 samples of 8190
-    # rows: two in flight (8 each in turn), 32 rows per pair
-    p = A.plan("fwd", 16, 8190, 12288, BF16)
-    assert p["walkers"] == 2 and p["groups"] == 2
-    assert 8190 / (p["bps"] * p["walkers"]) >= 16
-    # 8 samples of 16380 rows: one in flight
-    p = A.plan("fwd", 8, 16380, 12288, BF16)
-    assert p["groups"] == 1 and 16380 / (p["bps"] * p["walkers"]) >= 16
     # short samples keep one group each
-    assert A.plan("fwd", 84, 1560, 12288, BF16)["groups"] >= 84
     assert A.plan("bwd", 84, 1560, 3072, BF16)["groups"] >= 84
     # the backward with pairs of wavefronts per row (2 walkers per
     # workgroup) follows the same rule: 16 rows per pair
