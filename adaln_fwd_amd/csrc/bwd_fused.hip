@@ -39,7 +39,7 @@ __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void bwd_stream_kernel(
     int32_t D, Map map) {
   constexpr int E = Elems<T>::value;
   constexpr int kWaves = kBlock / kWave;
-  extern __shared__ float stage[];  // one wavefront's accumulators
+  extern __shared__ float stage[];  // the four wavefronts' accumulators
   const int lane = lane_id();
   const int wave = wave_id();
   const int nvec = D / E;
@@ -167,46 +167,92 @@ __attribute__((amdgpu_waves_per_eu(OCC, OCC))) void bwd_stream_kernel(
       }
     }
 
-    // Add the four wavefronts' accumulators in wavefront order: wavefront w
-    // (w = 1, 2, 3) stages its values, wavefront 0 adds them.  Lane-major
-    // layout [value][lane] keeps the LDS accesses conflict-free.
-#pragma unroll 1
-    for (int w = 1; w < kWaves; ++w) {
+    // Add the four wavefronts' accumulators in wavefront order and write
+    // them as one partial row.
+    if constexpr (bwd_stage_all(V, E)) {
+      // All four stage theirs ([wave][value][lane]: conflict-free), one
+      // barrier, then wavefront w adds and writes the float4 groups g = w,
+      // w + 4, ... of the 2*V*E/4 groups (values 4g .. 4g + 3).
+      __syncthreads();  // the previous segment's reads of stage are done
+#pragma unroll
+      for (int k = 0; k < V; ++k)
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const int v = wave * V * E + k * E + e;
+          stage[(v * 2 + 0) * kWave + lane] = acc_s[k][e];
+          stage[(v * 2 + 1) * kWave + lane] = acc_h[k][e];
+        }
       __syncthreads();
-      if (wave == w) {
-#pragma unroll
-        for (int k = 0; k < V; ++k)
-#pragma unroll
-          for (int e = 0; e < E; ++e) {
-            stage[((k * E + e) * 2 + 0) * kWave + lane] = acc_s[k][e];
-            stage[((k * E + e) * 2 + 1) * kWave + lane] = acc_h[k][e];
-          }
-      }
-      __syncthreads();
-      if (wave == 0) {
-#pragma unroll
-        for (int k = 0; k < V; ++k)
-#pragma unroll
-          for (int e = 0; e < E; ++e) {
-            acc_s[k][e] += stage[((k * E + e) * 2 + 0) * kWave + lane];
-            acc_h[k][e] += stage[((k * E + e) * 2 + 1) * kWave + lane];
-          }
-      }
-    }
-    if (wave == 0) {
+      constexpr int kGroups = V * E / 4;  // float4 groups per array
       const int64_t po = (int64_t)part_row * D;
 #pragma unroll
-      for (int k = 0; k < V; ++k) {
-        if (ok[k]) {
-          const int64_t c = po + (int64_t)jv[k] * E;
+      for (int gi = 0; gi < (2 * kGroups + kWaves - 1) / kWaves; ++gi) {
+        const int g = gi * kWaves + wave;
+        if (g < 2 * kGroups) {
+          const int a = g / kGroups;         // 0: dscale, 1: dshift
+          const int kq = g - a * kGroups;    // k * (E / 4) + q
+          const int k = kq / (E / 4);
+          if (ok[k]) {
+            float v4[4];
 #pragma unroll
-          for (int q = 0; q < E / 4; ++q) {
-            *reinterpret_cast<float4 *>(part_scale + c + 4 * q) =
-                make_float4(acc_s[k][4 * q], acc_s[k][4 * q + 1],
-                            acc_s[k][4 * q + 2], acc_s[k][4 * q + 3]);
-            *reinterpret_cast<float4 *>(part_shift + c + 4 * q) =
-                make_float4(acc_h[k][4 * q], acc_h[k][4 * q + 1],
-                            acc_h[k][4 * q + 2], acc_h[k][4 * q + 3]);
+            for (int i = 0; i < 4; ++i) {
+              const int val = kq * 4 + i;    // k * E + e
+              float t = stage[((0 * V * E + val) * 2 + a) * kWave + lane];
+#pragma unroll
+              for (int w = 1; w < kWaves; ++w)
+                t += stage[((w * V * E + val) * 2 + a) * kWave + lane];
+              v4[i] = t;
+            }
+            const int q = kq - k * (E / 4);
+            const int64_t c = po + (int64_t)jv[k] * E + 4 * q;
+            float *dst = a == 0 ? part_scale : part_shift;
+            *reinterpret_cast<float4 *>(dst + c) =
+                make_float4(v4[0], v4[1], v4[2], v4[3]);
+          }
+        }
+      }
+    } else {
+      // Add the four wavefronts' accumulators in wavefront order: wavefront w
+      // (w = 1, 2, 3) stages its values, wavefront 0 adds them.  Lane-major
+      // layout [value][lane] keeps the LDS accesses conflict-free.
+#pragma unroll 1
+      for (int w = 1; w < kWaves; ++w) {
+        __syncthreads();
+        if (wave == w) {
+#pragma unroll
+          for (int k = 0; k < V; ++k)
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+              stage[((k * E + e) * 2 + 0) * kWave + lane] = acc_s[k][e];
+              stage[((k * E + e) * 2 + 1) * kWave + lane] = acc_h[k][e];
+            }
+        }
+        __syncthreads();
+        if (wave == 0) {
+#pragma unroll
+          for (int k = 0; k < V; ++k)
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+              acc_s[k][e] += stage[((k * E + e) * 2 + 0) * kWave + lane];
+              acc_h[k][e] += stage[((k * E + e) * 2 + 1) * kWave + lane];
+            }
+        }
+      }
+      if (wave == 0) {
+        const int64_t po = (int64_t)part_row * D;
+#pragma unroll
+        for (int k = 0; k < V; ++k) {
+          if (ok[k]) {
+            const int64_t c = po + (int64_t)jv[k] * E;
+#pragma unroll
+            for (int q = 0; q < E / 4; ++q) {
+              *reinterpret_cast<float4 *>(part_scale + c + 4 * q) =
+                  make_float4(acc_s[k][4 * q], acc_s[k][4 * q + 1],
+                              acc_s[k][4 * q + 2], acc_s[k][4 * q + 3]);
+              *reinterpret_cast<float4 *>(part_shift + c + 4 * q) =
+                  make_float4(acc_h[k][4 * q], acc_h[k][4 * q + 1],
+                              acc_h[k][4 * q + 2], acc_h[k][4 * q + 3]);
+            }
           }
         }
       }
@@ -222,7 +268,8 @@ hipError_t bwd_stream_v(int64_t grid, const Map &map, const void *dy,
                         const float *rstd, void *dx, float *part_scale,
                         float *part_shift, int32_t D, hipStream_t s) {
   constexpr int E = Elems<T>::value;
-  const size_t lds = (size_t)V * E * 2 * kWave * sizeof(float);
+  const int staged = bwd_stage_all(V, E) ? kBlock / kWave : 1;  // wavefronts
+  const size_t lds = (size_t)staged * V * E * 2 * kWave * sizeof(float);
   return launch_kernel_lds(
       bwd_stream_kernel<T, V, FULL, bwd_stream_pf(V), bwd_stream_occ(V), Map>,
       grid, kBlock, lds, s, (const T *)dy, (const T *)x, (const T *)scale,

@@ -163,6 +163,17 @@ constexpr int kMaxStreamVectors = 16 * 64;
 #ifndef ADALN_BWD_SHORT_V
 #define ADALN_BWD_SHORT_V 3
 #endif
+// End of a sample in bwd_stream_kernel: where the four wavefronts'
+// accumulators fit 48 KiB of LDS together (bf16 rows of up to 3 vectors per
+// lane, f32 up to 5), all four stage them at once and each adds and writes a
+// quarter of the partial row (one barrier); wider rows stage them one
+// wavefront at a time into wavefront 0.  The sums run in wavefront order
+// either way.  Measured on MI355X (fused backward + finish, paired, same
+// buffers): bf16 16 x 1560 x 1536 48.6 -> 47.5 us, 64 x 1024 x 768 63.8 ->
+// 63.0 us, one sample within noise.
+constexpr bool bwd_stage_all(int V, int E) {
+  return 4 * V * E * 2 * 64 * 4 <= 48 * 1024;
+}
 constexpr int bwd_stream_pf(int V) {
   return V <= 6 ? ADALN_BWD_PF_SHORT : ADALN_BWD_PF_LONG;
 }
@@ -219,10 +230,10 @@ constexpr bool bwd_wide_split(int V, int E) {
 // The forward kernels (fwd_rows_kernel, fwd_wide_kernel) widen x again for
 // the variance pass and x, scale and shift again for the output where keeping
 // them widened would leave one wavefront per SIMD: bf16 rows of 16 vectors
-// per lane (256 -> 216-252 VGPRs, two wavefronts per SIMD).  Measured on MI355X, bf16, D = 8192: 16 x
-// 1560 rows 160.4 -> 143.1 us, 1 x 16384 106.5 -> 96.6 us; at 10 vectors per
-// lane (two -> three wavefronts per SIMD) it costs 5% (1 x 75600 x 5120
-// 256.4 -> 268.1 us), and 6 vectors 3%.
+// per lane (256 -> 216-252 VGPRs, two wavefronts per SIMD).  Measured on
+// MI355X, bf16, D = 8192: 16 x 1560 rows 160.4 -> 143.1 us, 1 x 16384 106.5
+// -> 96.6 us; at 10 vectors per lane (two -> three wavefronts per SIMD) it
+// costs 5% (1 x 75600 x 5120 256.4 -> 268.1 us), and 6 vectors 3%.
 constexpr bool fwd_rows_rewiden(int V, int E) { return E == 8 && V >= 16; }
 
 // The forward of rows wider than 1024 vectors splits each row between the W
