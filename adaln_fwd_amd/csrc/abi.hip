@@ -148,10 +148,10 @@ DmodPlan choose_dmod_plan(int64_t B, int64_t N, int64_t nvec) {
   return p;
 }
 
-// Row-stream plans (rows of up to 4096 vectors for the forward, 2560 for the
-// backward, which takes a pair of wavefronts per row past 320 and four past
-// 1280; the forward takes a pair past 1024 and four past 1536).  V is the
-// smallest instantiated count that holds the row.
+// Row-stream plans (rows of up to 4096 vectors; the backward takes a pair of
+// wavefronts per row past 320 vectors, four past 1280 and eight past 2560;
+// the forward a pair past 1024 and four past 1536).  V is the smallest
+// instantiated count that holds the row.
 //
 // The forward covers the rows with its grid, one row per row walker (a
 // wavefront, or the W wavefronts sharing a row): ceil(B * N * W / 4)
@@ -191,9 +191,15 @@ constexpr int64_t kBwdSkewMinSamples = 16;
 constexpr int64_t kLongSample = 4096;
 
 // Waves per SIMD (and so workgroups per CU) the backward's kernel runs at.
+// (Workgroups per CU: the same as waves per SIMD for four-wavefront
+// workgroups, half of it for the eight-wavefront one.)
 int stream_occ(const StreamPlan &p) {
-  return p.W > 1 ? bwd_wide_occ(p.V) : bwd_stream_occ(p.V);
+  return p.W > 1 ? bwd_wide_wgs_per_cu(p.V, p.W) : bwd_stream_occ(p.V);
 }
+
+// Rows a workgroup works on at a time: 4 / W for the four-wavefront
+// workgroups, one for the eight-wavefront backward.
+int64_t rows_per_workgroup(int W) { return W >= 4 ? 1 : 4 / W; }
 
 bool choose_stream_plan(int64_t B, int64_t N, int64_t nvec, bool bwd,
                         StreamPlan *plan) {
@@ -204,7 +210,7 @@ bool choose_stream_plan(int64_t B, int64_t N, int64_t nvec, bool bwd,
 #undef ADALN_STREAM_PLAN_CASE
   if (bwd && (p.V == 0 || p.V > kMaxBwdStreamV)) {
     // too wide for one wavefront's registers: a pair of wavefronts per row,
-    // or a quad past 1280 vectors
+    // a quad past 1280 vectors, eight past 2560
     p.V = 0;
 #define ADALN_PAIR_PLAN_CASE(V_) \
   if (p.V == 0 && (int64_t)2 * 64 * V_ >= nvec) p.V = V_, p.W = 2;
@@ -214,6 +220,10 @@ bool choose_stream_plan(int64_t B, int64_t N, int64_t nvec, bool bwd,
   if (p.V == 0 && (int64_t)4 * 64 * V_ >= nvec) p.V = V_, p.W = 4;
     ADALN_BWD_QUAD_V(ADALN_QUAD_PLAN_CASE)
 #undef ADALN_QUAD_PLAN_CASE
+#define ADALN_OCT_PLAN_CASE(V_) \
+  if (p.V == 0 && (int64_t)8 * 64 * V_ >= nvec) p.V = V_, p.W = 8;
+    ADALN_BWD_OCT_V(ADALN_OCT_PLAN_CASE)
+#undef ADALN_OCT_PLAN_CASE
   }
   if (!bwd && p.V == 0) {
     // the forward of rows past 1024 vectors: a pair of wavefronts per row,
@@ -229,14 +239,14 @@ bool choose_stream_plan(int64_t B, int64_t N, int64_t nvec, bool bwd,
   }
   if (p.V == 0) return false;
   if (!bwd) {
-    const int64_t walkers = 4 / p.W;  // rows a workgroup covers
+    const int64_t walkers = rows_per_workgroup(p.W);
     p.grid = (B * N + walkers - 1) / walkers;
   } else if (B > 0 && N > 0) {
     const int occ = stream_occ(p);
     const int64_t G = (int64_t)kCUs * occ;
     const int64_t min_bps = ADALN_BWD_MIN_BPS;
     int64_t bps = G / B > 1 ? G / B : 1;
-    const int64_t walkers = 4 / p.W;  // row walkers per workgroup
+    const int64_t walkers = rows_per_workgroup(p.W);  // row walkers
     if (B > 1 && N >= kLongSample && p.W > 1) {
       // Long samples: the fewest samples in flight (g, a divisor of B, so
       // every group slot walks B / g samples) that still give each row
@@ -560,7 +570,7 @@ ADALN_API int adaln_plan(int which, int64_t B, int64_t N, int64_t D,
     return ok();
   }
   if (choose_stream_plan(B, N, nvec, which == 1, &sp)) {
-    const int64_t walkers = 4 / sp.W;  // four-wavefront workgroups
+    const int64_t walkers = rows_per_workgroup(sp.W);
     const int64_t v[7] = {sp.V,      sp.W,    sp.grid, sp.bps,
                           sp.groups, walkers, sp.skew};
     std::copy(v, v + 7, out);
@@ -613,17 +623,11 @@ ADALN_API int adaln_bwd(const void *dy, const void *x, const void *scale,
   ADALN_TRY(check_ptr(dshift, B > 0, "dshift"));
   ADALN_TRY(check_workspace(workspace, workspace_bytes_given,
                             workspace_bytes(B, N, D, dtype)));
-  StreamPlan plan;
-  if (choose_stream_plan(B, N, D / elems_per_vec(dtype), true, &plan)) {
-    ADALN_TRY(adaln_bwd_fused(dy, x, scale, mean, rstd, dx, workspace,
-                              workspace_bytes_given, B, N, D, dtype, stream));
-    return adaln_bwd_finish(workspace, workspace_bytes_given, dscale, dshift,
-                            B, N, D, dtype, stream);
-  }
-  // rows too wide for the fused kernel: dx, then the D-tile reduction
-  ADALN_TRY(adaln_bwd_dx(dy, x, scale, mean, rstd, dx, B, N, D, dtype, stream));
-  return adaln_bwd_dmod(dy, x, mean, rstd, dscale, dshift, workspace,
-                        workspace_bytes_given, B, N, D, dtype, stream);
+  // every row width that check_shape admits has a fused plan
+  ADALN_TRY(adaln_bwd_fused(dy, x, scale, mean, rstd, dx, workspace,
+                            workspace_bytes_given, B, N, D, dtype, stream));
+  return adaln_bwd_finish(workspace, workspace_bytes_given, dscale, dshift, B,
+                          N, D, dtype, stream);
 }
 
 // ------------------------------------------------------ packed segments

@@ -1,7 +1,7 @@
-// Fused backward for rows of 321 to 2560 16-byte vectors (bf16 D of 2568 to
-// 20480, f32 D of 1284 to 10240): dx and the D-tile partial sums of
+// Fused backward for rows of 321 to 4096 16-byte vectors (bf16 D of 2568 to
+// 32768, f32 D of 1284 to 16384): dx and the D-tile partial sums of
 // dscale/dshift in one pass over x and dy, like bwd_stream_kernel, with each
-// row split between W = 2 or 4 wavefronts.
+// row split between W = 2, 4 or 8 wavefronts.
 //
 // A row held in one wavefront together with its per-lane accumulators (2
 // floats per element it owns) takes the whole register file from 640
@@ -12,7 +12,9 @@
 // vectors [h*V*64, (h+1)*V*64) of the group's row (lane l: vector
 // (h*V + k)*64 + l), so each keeps the registers of 1/W of the row: pairs
 // take rows of up to 1280 vectors (two wavefronts per SIMD up to 640), quads
-// up to 2560.  The two row sums of dx (of g and of g*xhat) are combined
+// up to 2560.  Past that, a 512-thread workgroup of eight wavefronts (two per
+// SIMD) works on one row at a time, each wavefront an eighth of it, up to
+// 4096 vectors.  The two row sums of dx (of g and of g*xhat) are combined
 // through LDS: each wavefront reduces its part with DPP, lane 0 stores the
 // two values, one barrier, and every wavefront of the group reads the W
 // parts and adds them in part order.  The store area is double-buffered by
@@ -24,10 +26,11 @@
 // 2.B, backward pass), every lane stays pinned to its features for all the
 // rows it visits and accumulates dy*xhat and dy in float32.  At the end of a
 // segment the pairs' accumulators (same features, different rows) are added
-// in pair order through LDS -- a quad owns all of its workgroup's rows and
-// needs no such step -- and written as one partial row per (segment,
-// workgroup): the workspace layout of bwd_stream_kernel, summed by the same
-// finishing kernels.  Fixed-order sums only; no atomics.
+// in pair order through LDS -- a quad or an eight-wavefront group owns all
+// of its workgroup's rows and needs no such step -- and written as one
+// partial row per (segment, workgroup): the workspace layout of
+// bwd_stream_kernel, summed by the same finishing kernels.  Fixed-order
+// sums only; no atomics.
 //
 // Two choices are made per row width, by measurement (launch.hpp): PF, the
 // rows in flight per wavefront (a second one where it fits beside the
@@ -40,22 +43,24 @@
 namespace adaln {
 
 template <typename T, int V, int W, int PF, bool SPLIT, bool FULL, class Map>
-__global__ __launch_bounds__(kBlock)
-__attribute__((amdgpu_waves_per_eu(bwd_wide_occ(V), bwd_wide_occ(V)))) void
+__global__ __launch_bounds__(bwd_wide_block(W))
+__attribute__((amdgpu_waves_per_eu(bwd_wide_occ(V, W),
+                                   bwd_wide_occ(V, W)))) void
 bwd_wide_kernel(
     const T *__restrict__ dy, const T *__restrict__ x,
     const T *__restrict__ scale, const float *__restrict__ mean,
     const float *__restrict__ rstd, T *__restrict__ dx,
     float *__restrict__ part_scale, float *__restrict__ part_shift,
     int32_t D, Map map) {
-  static_assert(W == 2 || W == 4, "a row takes two or four wavefronts");
+  static_assert(W == 2 || W == 4 || W == 8,
+                "a row takes two, four or eight wavefronts");
   constexpr int E = Elems<T>::value;
-  constexpr int kRows = kBlock / kWave / W;  // rows a workgroup works on
+  constexpr int kRows = bwd_wide_block(W) / kWave / W;  // rows at a time
   extern __shared__ float stage[];  // [part][value][lane], one quantity
   __shared__ float sums[2][kRows][W][2];  // [parity][group][part][s1, s2]
   const int lane = lane_id();
   const int wave = wave_id();
-  const int group = wave / W;  // row group (pair or quad) of this wavefront
+  const int group = wave / W;  // row group of this wavefront
   const int part = wave % W;   // its part of the group's row
   const int nvec = D / E;
   const float inv_d = 1.0f / (float)D;
@@ -68,6 +73,37 @@ bwd_wide_kernel(
     ok[k] = FULL || jv[k] < nvec;
     jl[k] = FULL ? jv[k] : clamp_vec(jv[k], nvec);
   }
+  // Where registers are short, the indices are derived again in each row
+  // from a base that an empty asm makes new there, so they are not held
+  // across the row loop.
+  constexpr bool kIdxRegs = bwd_wide_index_regs(V, W, E);
+  int vbase = part * V * kWave + lane;
+  auto JV = [&](int k) -> int {
+    if constexpr (kIdxRegs) return jv[k];
+    else return vbase + k * kWave;
+  };
+  auto OK = [&](int k) -> bool {
+    if constexpr (kIdxRegs) return ok[k];
+    else return FULL || vbase + k * kWave < nvec;
+  };
+  auto JL = [&](int k) -> int {
+    if constexpr (kIdxRegs) return jl[k];
+    else return FULL ? JV(k) : clamp_vec(JV(k), nvec);
+  };
+  auto fresh = [&]() {
+    if constexpr (!kIdxRegs) asm volatile("" : "+v"(vbase));
+  };
+  // zero the vectors past the row's end
+  auto mask_row = [&](Vec (&xv)[V], Vec (&gv)[V]) {
+    if constexpr (!FULL && kIdxRegs) {
+      mask_tail(xv, ok), mask_tail(gv, ok);
+    } else if constexpr (!FULL) {
+      bool okr[V];
+#pragma unroll
+      for (int k = 0; k < V; ++k) okr[k] = OK(k);
+      mask_tail(xv, okr), mask_tail(gv, okr);
+    }
+  };
 
   int parity = 0;
   // One segment: rows [row0, row0 + N) modulated by vector `mod`, walked
@@ -84,11 +120,27 @@ bwd_wide_kernel(
       return row0 + (p >= N ? p - N : p);
     };
     const int stride = bps * kRows;
-    Vec sv[V];
+    // The segment's scale: held in registers for the whole segment, or, where
+    // the accumulators leave no room for it, read again (from L2) at each use.
+    // The empty asm makes the address new at every use, so the compiler
+    // cannot hoist those loads out of the row loop into registers.
+    constexpr bool kScaleRegs = bwd_wide_scale_regs(V, W, E);
+    Vec sv[kScaleRegs ? V : 1];
+    if constexpr (kScaleRegs) {
 #pragma unroll
-    for (int k = 0; k < V; ++k)
-      sv[k] = ok[k] ? load_vec(scale + (int64_t)mod * D + (int64_t)jv[k] * E)
-                    : vzero();
+      for (int k = 0; k < V; ++k)
+        sv[k] = OK(k) ? load_vec(scale + (int64_t)mod * D + (int64_t)JV(k) * E)
+                      : vzero();
+    }
+    auto scale_vec = [&](int k) -> Vec {
+      if constexpr (kScaleRegs) {
+        return sv[k];
+      } else {
+        const T *p = scale + (int64_t)mod * D;
+        asm volatile("" : "+s"(p));
+        return OK(k) ? load_vec(p + (int64_t)JV(k) * E) : vzero();
+      }
+    };
 
     float acc_s[V][E], acc_h[V][E];
 #pragma unroll
@@ -105,10 +157,11 @@ bwd_wide_kernel(
         st[0] = mean[at(n)];
         st[1] = rstd[at(n)];
         const int64_t off = at(n) * D;
+        fresh();
 #pragma unroll
         for (int k = 0; k < V; ++k) {
-          xv[k] = load_stream(x + off + (int64_t)jl[k] * E);
-          gv[k] = load_stream(dy + off + (int64_t)jl[k] * E);
+          xv[k] = load_stream(x + off + (int64_t)JL(k) * E);
+          gv[k] = load_stream(dy + off + (int64_t)JL(k) * E);
         }
       }
     };
@@ -120,15 +173,17 @@ bwd_wide_kernel(
       const float r = st[1];
       float s1 = 0.f, s2 = 0.f;
       if (live) {
-        if constexpr (!FULL) mask_tail(xv, ok), mask_tail(gv, ok);
+        fresh();
+        mask_row(xv, gv);
         // this part's sums of g = dy * (1 + scale) and g * xhat (vectors
         // past the row end hold dy = 0, so g = 0 there)
 #pragma unroll
         for (int k = 0; k < V; ++k) {
+          const Vec sk = scale_vec(k);
 #pragma unroll
           for (int e = 0; e < E; ++e) {
             const float xh = (elem<T>(xv[k], e) - mu) * r;
-            const float g = elem<T>(gv[k], e) * (1.0f + elem<T>(sv[k], e));
+            const float g = elem<T>(gv[k], e) * (1.0f + elem<T>(sk, e));
             s1 += g;
             s2 = fmaf(g, xh, s2);
           }
@@ -152,21 +207,23 @@ bwd_wide_kernel(
         const float c2 = t2 * inv_d;
 #pragma unroll
         for (int k = 0; k < V; ++k) opaque(xv[k]), opaque(gv[k]);
+        fresh();
         const int64_t off = at(n) * D;
 #pragma unroll
         for (int k = 0; k < V; ++k) {
-          if (ok[k]) {
+          if (OK(k)) {
+            const Vec sk = scale_vec(k);
             float o[E];
 #pragma unroll
             for (int e = 0; e < E; ++e) {
               const float xh = (elem<T>(xv[k], e) - mu) * r;
               const float gy = elem<T>(gv[k], e);
-              const float g = gy * (1.0f + elem<T>(sv[k], e));
+              const float g = gy * (1.0f + elem<T>(sk, e));
               o[e] = r * fmaf(-xh, c2, g - c1);
               acc_s[k][e] = fmaf(gy, xh, acc_s[k][e]);
               acc_h[k][e] += gy;
             }
-            store_stream(dx + off + (int64_t)jv[k] * E, pack<T>(o));
+            store_stream(dx + off + (int64_t)JV(k) * E, pack<T>(o));
           }
         }
       }
@@ -199,18 +256,20 @@ bwd_wide_kernel(
         if (live) {
           mu = mean[at(n)];
           r = rstd[at(n)];
+          fresh();
 #pragma unroll
           for (int k = 0; k < V; ++k) {
-            xv[k] = load_stream(x + off + (int64_t)jl[k] * E);
-            gv[k] = load_stream(dy + off + (int64_t)jl[k] * E);
+            xv[k] = load_stream(x + off + (int64_t)JL(k) * E);
+            gv[k] = load_stream(dy + off + (int64_t)JL(k) * E);
           }
-          if constexpr (!FULL) mask_tail(xv, ok), mask_tail(gv, ok);
+          mask_row(xv, gv);
 #pragma unroll
           for (int k = 0; k < V; ++k) {
+            const Vec sk = scale_vec(k);
 #pragma unroll
             for (int e = 0; e < E; ++e) {
               const float xh = (elem<T>(xv[k], e) - mu) * r;
-              const float g = elem<T>(gv[k], e) * (1.0f + elem<T>(sv[k], e));
+              const float g = elem<T>(gv[k], e) * (1.0f + elem<T>(sk, e));
               s1 += g;
               s2 = fmaf(g, xh, s2);
             }
@@ -234,20 +293,22 @@ bwd_wide_kernel(
           const float c2 = t2 * inv_d;
 #pragma unroll
           for (int k = 0; k < V; ++k) opaque(xv[k]), opaque(gv[k]);
+          fresh();
 #pragma unroll
           for (int k = 0; k < V; ++k) {
-            if (ok[k]) {
+            if (OK(k)) {
+              const Vec sk = scale_vec(k);
               float o[E];
 #pragma unroll
               for (int e = 0; e < E; ++e) {
                 const float xh = (elem<T>(xv[k], e) - mu) * r;
                 const float gy = elem<T>(gv[k], e);
-                const float g = gy * (1.0f + elem<T>(sv[k], e));
+                const float g = gy * (1.0f + elem<T>(sk, e));
                 o[e] = r * fmaf(-xh, c2, g - c1);
                 acc_s[k][e] = fmaf(gy, xh, acc_s[k][e]);
                 acc_h[k][e] += gy;
               }
-              store_stream(dx + off + (int64_t)jv[k] * E, pack<T>(o));
+              store_stream(dx + off + (int64_t)JV(k) * E, pack<T>(o));
             }
           }
         }
@@ -278,8 +339,8 @@ bwd_wide_kernel(
     // quantity at a time through LDS ([part][value][lane]), then pair 0
     // writes the partial row, each wavefront its half.  The first barrier
     // keeps the staging area from being overwritten while the previous
-    // segment's values are still being read.  A quad holds the workgroup's
-    // only row group and writes its parts directly.
+    // segment's values are still being read.  A quad or eight-wavefront
+    // group is the workgroup's only row group and writes its parts directly.
     if constexpr (kRows == 2) {
       float *st = stage + (size_t)part * V * E * kWave;
 #pragma unroll
@@ -312,8 +373,8 @@ bwd_wide_kernel(
       const int64_t po = (int64_t)part_row * D;
 #pragma unroll
       for (int k = 0; k < V; ++k) {
-        if (ok[k]) {
-          const int64_t c = po + (int64_t)jv[k] * E;
+        if (OK(k)) {
+          const int64_t c = po + (int64_t)JV(k) * E;
 #pragma unroll
           for (int q = 0; q < E / 4; ++q) {
             *reinterpret_cast<float4 *>(part_scale + c + 4 * q) =
@@ -338,11 +399,13 @@ hipError_t bwd_wide_v(int64_t grid, const Map &map, const void *dy,
                       float *part_shift, int32_t D, hipStream_t s) {
   constexpr int E = Elems<T>::value;
   // staging of the pairs' end-of-segment sum: W parts of V*E floats per lane
+  constexpr int kThreads = bwd_wide_block(W);
   const size_t lds =
-      kBlock / kWave / W == 2 ? (size_t)W * V * E * kWave * sizeof(float) : 0;
-  return launch_kernel_lds(bwd_wide_kernel<T, V, W, bwd_wide_pf(V, E, FULL),
+      kThreads / kWave / W == 2 ? (size_t)W * V * E * kWave * sizeof(float)
+                                : 0;
+  return launch_kernel_lds(bwd_wide_kernel<T, V, W, bwd_wide_pf(V, W, E, FULL),
                                            bwd_wide_split(V, E), FULL, Map>,
-                           grid, kBlock,
+                           grid, kThreads,
                            lds, s, (const T *)dy, (const T *)x,
                            (const T *)scale, mean, rstd, (T *)dx, part_scale,
                            part_shift, D, map);
@@ -376,8 +439,10 @@ hipError_t bwd_wide_dispatch_w(int dtype, int V, int64_t grid, const Map &map,
   }
   if constexpr (W == 2) {
     ADALN_BWD_PAIR_V(ADALN_BWD_WIDE_CASE)
-  } else {
+  } else if constexpr (W == 4) {
     ADALN_BWD_QUAD_V(ADALN_BWD_WIDE_CASE)
+  } else {
+    ADALN_BWD_OCT_V(ADALN_BWD_WIDE_CASE)
   }
 #undef ADALN_BWD_WIDE_CASE
   return hipErrorInvalidValue;
@@ -395,6 +460,9 @@ hipError_t bwd_wide_dispatch(int dtype, int V, int W, int64_t grid,
                                   rstd, dx, part_scale, part_shift, D, stream);
   if (W == 4)
     return bwd_wide_dispatch_w<4>(dtype, V, grid, map, dy, x, scale, mean,
+                                  rstd, dx, part_scale, part_shift, D, stream);
+  if (W == 8)
+    return bwd_wide_dispatch_w<8>(dtype, V, grid, map, dy, x, scale, mean,
                                   rstd, dx, part_scale, part_shift, D, stream);
   return hipErrorInvalidValue;
 }

@@ -48,7 +48,7 @@ struct DmodPlan {
 // (bps = groups = 0, `grid` workgroups of 4/W rows).
 struct StreamPlan {
   int V = 0;       // vectors per lane
-  int W = 1;       // wavefronts per row (2 or 4: rows too wide for one)
+  int W = 1;       // wavefronts per row (2, 4 or 8: rows too wide for one)
   int64_t grid = 0;
   int bps = 0;     // workgroups per sample (partial rows per sample)
   int groups = 0;  // samples in flight
@@ -185,8 +185,9 @@ constexpr int bwd_stream_occ(int V) {
 // vectors.  Wider rows split between the W wavefronts of a row group
 // (bwd_wide_kernel), V vectors per lane each: pairs up to 2 * 640 vectors,
 // quads (W = 4) up to 4 * 640; past 2560 vectors the accumulators outgrow
-// the register file of a four-wavefront workgroup and the separate dx and
-// D-tile kernels take over.  A whole 640-vector row in one wavefront needs
+// the register file of a four-wavefront workgroup, and eight wavefronts (a
+// 512-thread workgroup, two per SIMD) share the row, up to 8 * 512 vectors,
+// the widest row of the library.  A whole 640-vector row in one wavefront needs
 // the full register file at one wavefront per SIMD, so nothing covers its
 // memory latency while it computes; as halves, rows of up to 640 vectors run
 // at two wavefronts per SIMD (measured on MI355X: the D = 5120 bf16 backward
@@ -194,7 +195,18 @@ constexpr int bwd_stream_occ(int V) {
 constexpr int kMaxBwdStreamV = 5;
 #define ADALN_BWD_PAIR_V(X) X(3) X(4) X(5) X(6) X(8) X(10)
 #define ADALN_BWD_QUAD_V(X) X(6) X(8) X(10)
-constexpr int bwd_wide_occ(int V) { return V <= 5 ? 2 : 1; }
+#define ADALN_BWD_OCT_V(X) X(6) X(8)
+// Threads per workgroup of bwd_wide_kernel: four wavefronts, or eight for
+// rows split eight ways.
+constexpr int bwd_wide_block(int W) { return W == 8 ? 512 : 256; }
+// Waves per SIMD of bwd_wide_kernel (an eight-wavefront workgroup puts two on
+// each SIMD), and so workgroups per CU: occ * 4 * 64 / threads.
+constexpr int bwd_wide_occ(int V, int W) {
+  return W == 8 || V <= 5 ? 2 : 1;
+}
+constexpr int bwd_wide_wgs_per_cu(int V, int W) {
+  return bwd_wide_occ(V, W) * 4 * 64 / bwd_wide_block(W);
+}
 // Rows in flight per wavefront of bwd_wide_kernel (E elements per vector):
 // bf16 rows at one wavefront per SIMD take a second row where its 2*V
 // vectors of x and dy fit beside the accumulators without spills (V*E <= 64
@@ -202,12 +214,26 @@ constexpr int bwd_wide_occ(int V) { return V <= 5 ? 2 : 1; }
 // tail needs registers of its own).  Measured on MI355X (fused backward,
 // bf16): D = 6144 288 -> 262 us, D = 8192 471 -> 440 us, D = 12288 555 ->
 // 517 us, D = 16384 586 -> 540 us.  f32 rows gained at most 2% and keep one.
-constexpr int bwd_wide_pf(int V, int E, bool full) {
+constexpr int bwd_wide_pf(int V, int W, int E, bool full) {
 #ifdef ADALN_BWD_WIDE_PF1
   return 1;
 #else
-  return bwd_wide_occ(V) == 1 && E == 8 && V * E <= (full ? 64 : 48) ? 2 : 1;
+  return bwd_wide_occ(V, W) == 1 && E == 8 && V * E <= (full ? 64 : 48) ? 2
+                                                                         : 1;
 #endif
+}
+// Registers of bf16 rows split eight ways: two wavefronts per SIMD leave 256
+// registers each, and at 8 vectors per lane the accumulators (128), the row
+// (64) and the scale (32) spill.  There bwd_wide_kernel reads the scale
+// again (from L2) at each use instead of holding it for the whole segment,
+// and, from 6 vectors per lane, derives its vector indices again in each row
+// instead of holding them (no spills left; bf16 1 x 12000 x 32768: 1768 us
+// with 398 spilled registers, 513 us without).
+constexpr bool bwd_wide_scale_regs(int V, int W, int E) {
+  return !(W == 8 && E == 8 && V >= 8);
+}
+constexpr bool bwd_wide_index_regs(int V, int W, int E) {
+  return !(W == 8 && E == 8);
 }
 // Loop form of bwd_wide_kernel at one row in flight: the loads as one step
 // and the arithmetic as the next, or both in one branch.  The compiler

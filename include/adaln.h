@@ -107,10 +107,10 @@ size_t adaln_bwd_workspace_bytes(int64_t B, int64_t N, int64_t D, int dtype);
  * dimension N, taken over a (d_tile, n_tile) grid with every lane pinned to
  * its features so that each access is contiguous along D, then combined
  * across the n_tiles; dx, on which the pages are silent, is the exact
- * gradient of the forward formula above.  For rows of at most 2560 vectors
- * (D <= 20480 bf16 / 10240 f32) it enqueues adaln_bwd_fused then
- * adaln_bwd_finish (x and dy read once); for wider rows, adaln_bwd_dx then
- * adaln_bwd_dmod.
+ * gradient of the forward formula above.  It enqueues adaln_bwd_fused then
+ * adaln_bwd_finish (x and dy read once) for every row width the library
+ * takes; adaln_bwd_dx and adaln_bwd_dmod below are the same gradients as
+ * two separate passes.
  *   dy        [B,N,D] dtype in   upstream gradient dL/dy
  *   x         [B,N,D] dtype in   the forward input
  *   scale     [B,D]   dtype in
@@ -147,19 +147,19 @@ int adaln_bwd_noalloc(const void *dy, const void *x, const void *scale,
                       int64_t D, int dtype, void *stream);
 
 /*
- * The two launches adaln_bwd makes for rows of at most 2560 vectors
- * (D <= 20480 bf16 / 10240 f32), exposed so callers can schedule or time them
- * separately.  Rows of up to 320 vectors are owned by one wavefront each,
- * wider ones by a pair of wavefronts (up to 1280 vectors) or four of them,
- * which combine their row sums through LDS.  adaln_bwd_fused reads x and dy once: it writes dx and, per
+ * The two launches adaln_bwd makes, exposed so callers can schedule or time
+ * them separately.  Rows of up to 320 vectors are owned by one wavefront
+ * each, wider ones by a pair of wavefronts (up to 1280 vectors), four (up to
+ * 2560) or eight (up to 4096, the widest row; 512-thread workgroups), which
+ * combine their row sums through LDS.  adaln_bwd_fused reads x and dy once:
+ * it writes dx and, per
  * (sample, n_tile), float32 partial sums of dscale and dshift into the
  * workspace -- the D-tile coalesced reduction of section 2.B with dx fused
  * into the same pass over the rows: one partial row per (sample, workgroup).
  * adaln_bwd_finish then sums those partials over the workgroups of each
  * sample in index order into dscale and dshift.  The
  * workspace must be the one adaln_bwd_fused filled for the same B, N, D and
- * dtype, with no other call using it in between.  Both return
- * ADALN_ERR_UNSUPPORTED for wider rows (adaln_bwd handles those).
+ * dtype, with no other call using it in between.
  */
 int adaln_bwd_fused(const void *dy, const void *x, const void *scale,
                     const float *mean, const float *rstd, void *dx,
@@ -173,10 +173,9 @@ int adaln_bwd_finish(const void *workspace, size_t workspace_bytes,
 /*
  * Launch plan of adaln_bwd_fused for this shape, for callers that account
  * for the partial sums it writes: fills out[0..3] with {vectors per lane,
- * wavefronts per row (1, 2 or 4), workgroups launched, partial rows per sample
- * P}.
+ * wavefronts per row (1, 2, 4 or 8), workgroups launched, partial rows per
+ * sample P}.
  * The partials occupy 2*B*P*D floats at the start of the workspace.
- * Returns ADALN_ERR_UNSUPPORTED for rows too wide for the fused kernel.
  * Host-only; no HIP call.
  */
 int adaln_bwd_fused_plan(int64_t B, int64_t N, int64_t D, int dtype,
@@ -192,16 +191,15 @@ int adaln_bwd_fused_plan(int64_t B, int64_t N, int64_t D, int dtype,
  * visits the walk positions (g % bps) * walkers + w, then every
  * bps * walkers positions; position n stands for row (n + b * skew) mod N of
  * the sample (skew is 0 except in the backward of many samples).  A walker
- * is one wavefront (W = 1) or the W wavefronts that share a row.  The
- * forward has bps = groups = 0 and covers the B * N rows of the batch with
- * its grid instead: walker j of workgroup g takes row (4 / W) * g + j, in
- * launches of at most 2^20 workgroups; out[2] counts the workgroups of all
- * of them.  Returns
- * ADALN_ERR_UNSUPPORTED where the entry point would take another path (rows
- * too wide for the fused backward).  Host-only; no HIP call.
+ * is one wavefront (W = 1) or the W wavefronts that share a row (a
+ * workgroup holds 4 / W walkers, or one when W = 8).  The forward has
+ * bps = groups = 0 and covers the B * N rows of the batch with its grid
+ * instead: walker j of workgroup g takes row (4 / W) * g + j, in launches
+ * of at most 2^20 workgroups; out[2] counts the workgroups of all of them.
+ * Host-only; no HIP call.
  *
  * which = 2: the launch that sums the partial rows into dscale and dshift
- * (adaln_bwd_finish, or the last launch of adaln_bwd_dmod for wider rows).
+ * (adaln_bwd_finish).
  * Fills out[0..5] with {features per column block F (16, 32 or 64),
  * wavefronts per block wpc, blocks per workgroup cpb, workgroups launched G,
  * threads per workgroup, partial rows P summed per output}.  Block k covers
@@ -260,8 +258,8 @@ int adaln_bwd_dmod(const void *dy, const void *x, const float *mean,
  *                dscale[m] sums dy*xhat over every row of every segment
  *                with seg_mod[s] == m (zero for an unused m)
  * The per-row math is that of adaln_fwd / adaln_bwd.  The forward takes every
- * row width adaln_fwd takes; the backward rows of up to 2560 vectors (D <=
- * 20480 bf16 / 10240 f32), wider rows return ADALN_ERR_UNSUPPORTED.  The workspace of adaln_bwd_segments is
+ * row width adaln_fwd takes, and so does the backward.  The workspace of
+ * adaln_bwd_segments is
  * adaln_bwd_segments_workspace_bytes(seg_offsets, nseg, D, dtype) bytes; the
  * host arrays are read during the call only.
  */

@@ -175,9 +175,13 @@ def test_segments_validation(lib):
              None) == _lib.ERR_WORKSPACE
     assert g(p, p, p, p, p, p, p, None, p, need, off, mod, 2, 2, 1536, 1,
              None) == _lib.ERR_INVALID
-    # past the packed backward's widest row (2560 vectors)
-    assert g(p, p, p, p, p, p, p, p, p, need, off, mod, 2, 2, 20488, 1,
+    # past the widest row (4096 vectors)
+    assert g(p, p, p, p, p, p, p, p, p, need, off, mod, 2, 2, 32776, 1,
              None) == _lib.ERR_UNSUPPORTED
+    # the packed backward takes every width up to it: with eight wavefronts
+    # per row from 2561 vectors, so only the workspace is short here
+    assert g(p, p, p, p, p, p, p, p, p, need, off, mod, 2, 2, 20488, 1,
+             None) == _lib.ERR_WORKSPACE
     # nothing to do: no segments and no modulation vectors
     assert f(None, None, None, None, None, None, None, None, 0, 0, 64, 1,
              None) == _lib.OK

@@ -69,7 +69,7 @@ def test_video_bucket_full(A):
     (1, 50, 6144, "bf16", "normal"),
     (1, 30, 8192, "bf16", "normal"),
     (1, 20, 12288, "bf16", "normal"),      # two wavefronts per row
-    (1, 9, 32768, "bf16", "normal"),       # four wavefronts per row (max D)
+    (1, 9, 32768, "bf16", "normal"),       # fwd quads, bwd eights (max D)
     (2, 17, 8192, "f32", "normal"),        # two wavefronts per row, f32
     (1, 5, 16384, "f32", "normal"),        # largest f32 row
     (3, 257, 1024, "f32", "offset"),
@@ -101,6 +101,17 @@ def test_video_bucket_full(A):
     (1, 64, 10240, "f32", "offset"),       # widest fused f32 backward
     (5, 333, 6144, "f32", "normal"),       # 6 vectors per lane, exact
     (700, 2, 12288, "bf16", "offset"),     # more samples than workgroups
+    # backward rows split between eight wavefronts (2561..4096 vectors), one
+    # row per 512-thread workgroup; bf16 rows of 8 vectors per lane read the
+    # scale at each use and derive their indices in each row
+    (2, 77, 20488, "bf16", "offset"),      # narrowest, ragged eighth
+    (1, 200, 24576, "bf16", "normal"),     # 6 vectors per lane, exact
+    (3, 50, 28000, "bf16", "outliers"),    # 8 vectors per lane, ragged
+    (1, 120, 32768, "bf16", "offset"),     # widest row
+    (600, 2, 24584, "bf16", "offset"),     # more samples than workgroups
+    (2, 99, 10244, "f32", "normal"),       # f32, ragged
+    (5, 300, 12292, "f32", "normal"),      # f32, 8 vectors per lane, ragged
+    (1, 64, 16384, "f32", "offset"),       # widest f32 row
 ])
 def test_shapes(A, B, N, D, dtype, kind):
     wl = W.custom(B, N, D, dtype, x_kind=kind, dy_std=1e-2 if dtype ==
@@ -164,6 +175,23 @@ def test_quad_rows_all_rows(A):
                   index=211)
     _say(f"quad rows {wl.shape}, every row")
     assert A.bwd_fused_plan(*wl.shape, torch.bfloat16)["waves_per_row"] == 4
+    _run_all_rows(A, wl)
+
+
+@pytest.mark.parametrize("B,N,D,dtype", [
+    (1, 6000, 32768, "bf16"),    # the widest row, 8 vectors per lane
+    (3, 2500, 27992, "bf16"),    # ragged, several samples
+    (1, 9000, 16384, "f32"),     # the widest f32 row
+])
+def test_eight_wave_rows_all_rows(A, B, N, D, dtype):
+    """Rows of 2561 to 4096 vectors (eight wavefronts per backward row) at
+    about a quarter of the large model's activation size: every row, and
+    dscale/dshift."""
+    wl = W.custom(B, N, D, dtype, x_kind="outliers",
+                  dy_std=1e-2 if dtype == "bf16" else 1.0, index=223)
+    _say(f"eight-wave rows {wl.shape} {dtype}, every row")
+    assert A.bwd_fused_plan(*wl.shape, synth.torch_dtype(dtype))[
+        "waves_per_row"] == 8
     _run_all_rows(A, wl)
 
 
@@ -294,7 +322,10 @@ def test_split_entry_points_match_bwd(A):
                                 synth.VIDEO_BUCKET,
                                 W.custom(3, 77, 5120, "bf16", x_kind="outliers",
                                          dy_std=1e-2),
-                                W.custom(2, 50, 520, "bf16")],
+                                W.custom(2, 50, 520, "bf16"),
+                                W.custom(2, 9, 20488, "bf16", dy_std=1e-2),
+                                W.custom(1, 9, 32768, "bf16", dy_std=1e-2),
+                                W.custom(2, 7, 16384, "f32")],
                          ids=lambda w: w.name + f"_{w.D}")
 def test_unfused_entry_points(A, wl):
     """adaln_bwd_dx and adaln_bwd_dmod (the separate dx kernel and the
@@ -310,24 +341,6 @@ def test_unfused_entry_points(A, wl):
                dscale=ds.cpu(), dshift=dh.cpu())
     for r in P.compare_full(inp, out, wl.dtype):
         _say(f"  {r}")
-
-
-@pytest.mark.parametrize("D", [20488, 32768])
-def test_fused_unsupported_for_wide_rows(A, D):
-    """Rows wider than 2560 vectors have no fused plan; adaln_bwd falls back
-    to the unfused kernels and gives the same bits as calling them."""
-    wl = W.custom(1, 9, D, "bf16", dy_std=1e-2)
-    _say("wide rows: bwd falls back to bwd_dx + bwd_dmod")
-    dev = P.to_device(synth.make_inputs(wl))
-    out = P.gpu_fwd_bwd(dev)
-    dx = A.bwd_dx(dev["dy"], dev["x"], dev["scale"], out["mean"], out["rstd"])
-    ds, dh = A.bwd_dmod(dev["dy"], dev["x"], out["mean"], out["rstd"])
-    torch.cuda.synchronize()
-    assert torch.equal(dx, out["dx"])
-    assert torch.equal(ds, out["dscale"]) and torch.equal(dh, out["dshift"])
-    with pytest.raises(A.AdalnError):
-        A.bwd_fused(dev["dy"], dev["x"], dev["scale"], out["mean"],
-                    out["rstd"])
 
 
 def test_empty(A):

@@ -6,7 +6,8 @@ g -> samples g / bps, + groups, ...; walker w -> rows (g % bps) * walkers
 (4/W)g + w of the batch), visit every token row exactly once, fit the
 resident grid, and for the fused backward give each (sample, workgroup)
 pair its own partial row inside the workspace.  The shape-dependent choices
-are pinned too: the wavefront pairs past 320 vectors, the fewest long
+are pinned too: the wavefront pairs past 320 vectors (quads past 1280, eight
+wavefronts past 2560, up to the widest row), the fewest long
 samples in flight (paired backward), and the balanced workgroups per
 sample.  CPU only."""
 
@@ -59,12 +60,8 @@ def _visits(p, B, N):
 @pytest.mark.parametrize("B,N,D,dt", _shapes(7, 300))
 def test_every_row_once(B, N, D, dt):
     for which in ("fwd", "bwd"):
-        try:
-            p = A.plan(which, B, N, D, dt)
-        except A.AdalnError as e:
-            assert which == "bwd" and e.code == -6
-            assert D // (8 if dt is BF16 else 4) > 2560
-            continue
+        # every row width up to the widest has a forward and a fused plan
+        p = A.plan(which, B, N, D, dt)
         if which == "fwd":
             # a grid over the rows: walker j of workgroup g -> row wg + j,
             # w = 4 / W walkers (one row each) per workgroup
@@ -80,9 +77,10 @@ def test_every_row_once(B, N, D, dt):
         assert 1 <= p["bps"] and 1 <= p["groups"]
         assert p["workgroups"] == p["bps"] * min(p["groups"], B)
         assert p["bps"] * p["groups"] <= MAX_GRID
-        # four-wavefront workgroups of row walkers: single wavefronts,
-        # pairs or quads
-        assert p["walkers"] * p["waves_per_row"] == 4
+        # four-wavefront workgroups of row walkers (single wavefronts, pairs
+        # or quads), or eight wavefronts on one row
+        w = p["waves_per_row"]
+        assert p["walkers"] * w == (8 if w == 8 else 4)
         assert np.all(_visits(p, B, N) == 1), (which, p)
         if which == "bwd":
             # partial row b * bps + (g % bps) of [B, bps, D], and room for it
@@ -99,15 +97,20 @@ def test_rows_past_320_vectors_take_pairs():
     assert A.plan("bwd", 1, 75600, 1280, F32)["waves_per_row"] == 1
     assert A.plan("bwd", 1, 75600, 1288, F32)["waves_per_row"] == 2
     # past 1280 vectors four wavefronts share a row, one row per workgroup,
-    # up to 2560 vectors; wider rows have no fused plan
+    # up to 2560 vectors; past that eight (a 512-thread workgroup, one per
+    # CU), up to the widest row, 4096 vectors
     for D, dt in ((10240, BF16), (5120, F32)):
         assert A.plan("bwd", 1, 75600, D, dt)["waves_per_row"] == 2
     for D, dt in ((10248, BF16), (20480, BF16), (5124, F32), (10240, F32)):
         p = A.plan("bwd", 1, 30000, D, dt)
         assert p["waves_per_row"] == 4 and p["walkers"] == 1
-    for D, dt in ((20488, BF16), (10244, F32)):
-        with pytest.raises(A.AdalnError):
-            A.plan("bwd", 1, 30000, D, dt)
+    for D, dt, V in ((20488, BF16, 6), (24576, BF16, 6), (24584, BF16, 8),
+                     (32768, BF16, 8), (10244, F32, 6), (12288, F32, 6),
+                     (12292, F32, 8), (16384, F32, 8)):
+        p = A.plan("bwd", 3, 30000, D, dt)
+        assert (p["waves_per_row"], p["walkers"], p["V"]) == (8, 1, V), (D, p)
+        assert p["workgroups"] <= 256   # at most one per CU
+        assert A.bwd_fused_plan(3, 30000, D, dt)["waves_per_row"] == 8
     # the forward keeps one wavefront per row up to 1024 vectors, then
     # pairs up to 1536 and quads up to 4096
     assert A.plan("fwd", 1, 75600, 8192, BF16)["waves_per_row"] == 1
@@ -184,5 +187,5 @@ def test_plan_validation():
     with pytest.raises(ValueError):
         A.plan("both", 1, 1, 64, BF16)
     with pytest.raises(A.AdalnError) as e:
-        A.plan("bwd", 1, 10, 32768, BF16)      # past 2560 vectors: unfused
+        A.plan("bwd", 1, 10, 32776, BF16)      # past the widest row
     assert e.value.code == -6

@@ -51,8 +51,14 @@ SMALL = [
     # four wavefronts per backward row (1281..2560 vectors), and per
     # forward row past 1536
     (10248, "bf16", [7, 130, 0, 1], [0, 1, 1, 0], 2),  # narrowest, ragged
-    (20480, "bf16", [40, 3], None, 2),                 # widest bwd
+    (20480, "bf16", [40, 3], None, 2),                 # widest quad bwd
     (6144, "f32", [99, 0, 250], [2, 0, 1], 3),
+    # eight wavefronts per backward row (2561..4096 vectors)
+    (20488, "bf16", [10, 0, 21, 1], [1, 0, 0, 1], 2),  # narrowest, ragged
+    (32768, "bf16", [6, 40], None, 2),                 # widest row
+    (28000, "bf16", [3, 17, 9], [0, 2, 0], 3),         # scale read at use
+    (16384, "f32", [25, 2], [0, 0], 1),                # widest f32 row
+    (10244, "f32", [1, 50], None, 2),                  # ragged f32
 ]
 
 
@@ -193,19 +199,17 @@ def test_wide_forward_uniform_matches_batched(A):
 
 
 def test_wide_rows_rejected(A):
-    """Rows past the packed backward's width (2560 vectors) are refused
-    before anything is enqueued; so are rows past the forward's (4096)."""
-    inp = synth.make_packed(_wl(20488, "bf16"), [10, 20], seed=1)
-    dev = P.packed_to_device(inp)
-    mean = torch.zeros(30, device="cuda")
-    with pytest.raises(A.AdalnError) as e:
-        A.bwd_segments(dev["dy"], dev["x"], dev["scale"], mean, mean,
-                       inp.seg_offsets)
-    assert e.value.code == -6
+    """Rows past the widest row (4096 vectors) are refused before anything
+    is enqueued, by the packed forward and backward alike."""
     x = torch.zeros(4, 32776, device="cuda", dtype=torch.bfloat16)
     v = torch.zeros(1, 32776, device="cuda", dtype=torch.bfloat16)
+    m = torch.zeros(4, device="cuda")
+    off = np.array([0, 4], dtype=np.int64)
     with pytest.raises(A.AdalnError) as e:
-        A.fwd_segments(x, v, v, np.array([0, 4], dtype=np.int64))
+        A.fwd_segments(x, v, v, off)
+    assert e.value.code == -6
+    with pytest.raises(A.AdalnError) as e:
+        A.bwd_segments(x, x, v, m, m, off)
     assert e.value.code == -6
 
 
