@@ -29,7 +29,9 @@
 // f32 1 x 30000 x 6148 321.3 -> 295.2 us, 1 x 16384 x 12288 283.6 -> 268.1
 // us, and 0.5-4.9% slower only for f32 rows of 16 vectors per lane (D =
 // 16384).  The same grid written inside the work map's walk loops kept more
-// registers alive and was 3-12% slower than the persistent kernel.
+// registers alive and was 3-12% slower than the persistent kernel.  Ragged
+// f32 rows of 16 vectors per lane load scale and shift late
+// (fwd_wide_late_mod in launch.hpp).
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -78,11 +80,14 @@ __global__ __launch_bounds__(kBlock) void fwd_wide_kernel(
   for (int k = 0; k < V; ++k)
     xv[k] = load_stream(x + off + (int64_t)jl[k] * E);
   const int64_t mod = row_mod(map, rr);
+  constexpr bool kLate = fwd_wide_late_mod(V, E, FULL);
+  if constexpr (!kLate) {
 #pragma unroll
-  for (int k = 0; k < V; ++k) {
-    const int64_t c = mod * D + (int64_t)jl[k] * E;
-    sv[k] = load_vec(scale + c);
-    hv[k] = load_vec(shift + c);
+    for (int k = 0; k < V; ++k) {
+      const int64_t c = mod * D + (int64_t)jl[k] * E;
+      sv[k] = load_vec(scale + c);
+      hv[k] = load_vec(shift + c);
+    }
   }
   if constexpr (!FULL) mask_tail(xv, ok);
 
@@ -137,10 +142,18 @@ __global__ __launch_bounds__(kBlock) void fwd_wide_kernel(
 #pragma unroll
     for (int k = 0; k < V; ++k) opaque(xv[k]), opaque(sv[k]), opaque(hv[k]);
   }
+  // (late loads: the asm gives the row's modulation pointers a new value
+  // here, after the statistics, so the loads below cannot move up)
+  const T *srow = scale + mod * D, *hrow = shift + mod * D;
+  if constexpr (kLate) asm volatile("" : "+s"(srow), "+s"(hrow));
 #pragma unroll
   for (int k = 0; k < V; ++k) {
     if (ok[k]) {
       float o[E];
+      if constexpr (kLate) {
+        sv[k] = load_vec(srow + (int64_t)jl[k] * E);
+        hv[k] = load_vec(hrow + (int64_t)jl[k] * E);
+      }
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         const float xh = (elem<T>(xv[k], e) - mu) * rs;

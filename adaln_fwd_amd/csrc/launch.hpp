@@ -261,6 +261,17 @@ constexpr bool bwd_wide_split(int V, int E) {
 // -> 96.6 us; at 10 vectors per lane (two -> three wavefronts per SIMD) it
 // costs 5% (1 x 75600 x 5120 256.4 -> 268.1 us), and 6 vectors 3%.
 constexpr bool fwd_rows_rewiden(int V, int E) { return E == 8 && V >= 16; }
+// fwd_wide_kernel loads scale and shift after the row's statistics, vector
+// by vector in the output pass (an empty asm statement keeps the loads
+// there), for f32 rows of 16 vectors per lane that end inside a wavefront's
+// vectors: 225-236 -> 129-134 VGPRs, three wavefronts per SIMD instead of
+// two.  Measured on MI355X (forward, HIP events, same buffers): f32
+// 1 x 16384 x 12292 323 -> 303 us, 1 x 30000 x 14000 647 -> 608 us; rows
+// that fill all 16 vectors were 8-12% slower that way and keep the early
+// loads.
+constexpr bool fwd_wide_late_mod(int V, int E, bool full) {
+  return E == 4 && V >= 16 && !full;
+}
 
 // The forward of rows wider than 1024 vectors splits each row between the W
 // wavefronts of a row group (fwd_wide_kernel), V vectors per lane each:

@@ -111,6 +111,7 @@ def test_video_bucket_full(A):
     (600, 2, 24584, "bf16", "offset"),     # more samples than workgroups
     (2, 99, 10244, "f32", "normal"),       # f32, ragged
     (5, 300, 12292, "f32", "normal"),      # f32, 8 vectors per lane, ragged
+    (3, 150, 14000, "f32", "offset"),      # f32 forward: late scale loads
     (1, 64, 16384, "f32", "offset"),       # widest f32 row
 ])
 def test_shapes(A, B, N, D, dtype, kind):

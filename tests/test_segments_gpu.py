@@ -160,6 +160,7 @@ WIDE_FORWARD = [
     (16384, "f32", [4, 9], None, 2),                  # widest f32 row
     (8200, "bf16", [64, 1], None, 2),                 # ragged, just past 1024
     (6148, "f32", [33, 100], [1, 1], 2),              # ragged quad, f32
+    (14000, "f32", [20, 0, 33], [1, 0, 1], 2),        # f32, late scale loads
 ]
 
 
