@@ -232,15 +232,56 @@ bwd_wide_kernel(
 
     // every wavefront of the workgroup runs `iters` row steps
     const int first = k_in * kRows + group;
-    const int iters =
-        k_in * kRows < N ? (N - 1 - k_in * kRows) / stride + 1 : 0;
+    int iters = k_in * kRows < N ? (N - 1 - k_in * kRows) / stride + 1 : 0;
+    // The XCD-weighted walk (kXcdM > 0, launch.hpp): rounds of kXcdM regular
+    // steps of the plain walk (positions j, j + stride, ... for walker
+    // j = k_in * kRows + group), then one extra step for the walkers of
+    // workgroups with an even block index, which take the positions after
+    // the regular ones in walker order.  A round covers kXcdM * stride + Wf
+    // positions, Wf the number of such walkers of the segment; a segment's
+    // workgroups start at block index blockIdx.x - k_in, so those with
+    // k_in of that parity are the even ones.  A row group's position is
+    // its workgroup's first row group's plus `group` in both kinds of step,
+    // so the workgroup's row groups step together.
+    constexpr int kXcdM = bwd_wide_xcd_m(V, W, E, FULL);
+    const int q0 = (int)((blockIdx.x - (unsigned)k_in) & 1u);
+    const bool even_xcd = (blockIdx.x & 1u) == 0u;
+    const int64_t j0 = (int64_t)k_in * kRows;
+    const int64_t rank0 = (int64_t)((k_in - q0) / 2) * kRows;
+    const int64_t round_len =
+        (int64_t)kXcdM * stride +
+        (int64_t)(q0 == 0 ? (bps + 1) / 2 : bps / 2) * kRows;
+    const int steps = kXcdM + (even_xcd ? 1 : 0);  // per round
+    if constexpr (kXcdM > 0) {
+      // steps whose first row group's position lies in the segment
+      const int64_t t = (int64_t)N / round_len;
+      const int64_t rem = (int64_t)N - t * round_len;
+      int64_t cnt = t * steps;
+      if (rem > j0) cnt += min((int64_t)kXcdM, (rem - j0 - 1) / stride + 1);
+      if (even_xcd && (int64_t)kXcdM * stride + rank0 < rem) cnt += 1;
+      iters = (int)cnt;
+    }
+    // the walk position of step `it` for this row group (N past the end)
+    auto pos = [&](int it) -> int {
+      if constexpr (kXcdM == 0) {
+        return first + it * stride;
+      } else {
+        const int t = it / steps, r = it - t * steps;
+        const int64_t p =
+            (int64_t)t * round_len +
+            (r < kXcdM ? (int64_t)r * stride + j0
+                       : (int64_t)kXcdM * stride + rank0) +
+            group;
+        return p < N ? (int)p : N;
+      }
+    };
     if constexpr (PF == 1 && SPLIT) {
 #pragma unroll 1
       for (int it = 0; it < iters; ++it) {
         Vec xv[V], gv[V];
         float st[2] = {0.f, 0.f};
-        load_row(xv, gv, st, first + it * stride);
-        do_row(xv, gv, st, first + it * stride);
+        load_row(xv, gv, st, pos(it));
+        do_row(xv, gv, st, pos(it));
       }
     } else if constexpr (PF == 1) {
       // the same steps with the loads and the first pass in one branch
@@ -248,7 +289,7 @@ bwd_wide_kernel(
       // depends on the row width)
 #pragma unroll 1
       for (int it = 0; it < iters; ++it) {
-        const int n = first + it * stride;
+        const int n = pos(it);
         const bool live = n < N;  // uniform across the wavefront
         const int64_t off = at(n) * D;
         Vec xv[V], gv[V];
@@ -318,20 +359,20 @@ bwd_wide_kernel(
       Vec xa[V], ga[V], xb[V], gb[V];
       float sa[2] = {0.f, 0.f}, sb[2] = {0.f, 0.f};
       int it = 0;
-      load_row(xa, ga, sa, first);
+      load_row(xa, ga, sa, pos(0));
 #pragma unroll 1
       for (; it + 2 < iters; it += 2) {
-        load_row(xb, gb, sb, first + (it + 1) * stride);
-        do_row(xa, ga, sa, first + it * stride);
-        load_row(xa, ga, sa, first + (it + 2) * stride);
-        do_row(xb, gb, sb, first + (it + 1) * stride);
+        load_row(xb, gb, sb, pos(it + 1));
+        do_row(xa, ga, sa, pos(it));
+        load_row(xa, ga, sa, pos(it + 2));
+        do_row(xb, gb, sb, pos(it + 1));
       }
       if (it + 1 < iters) {
-        load_row(xb, gb, sb, first + (it + 1) * stride);
-        do_row(xa, ga, sa, first + it * stride);
-        do_row(xb, gb, sb, first + (it + 1) * stride);
+        load_row(xb, gb, sb, pos(it + 1));
+        do_row(xa, ga, sa, pos(it));
+        do_row(xb, gb, sb, pos(it + 1));
       } else {
-        do_row(xa, ga, sa, first + it * stride);
+        do_row(xa, ga, sa, pos(it));
       }
     }
 

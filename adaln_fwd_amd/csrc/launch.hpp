@@ -235,6 +235,25 @@ constexpr bool bwd_wide_scale_regs(int V, int W, int E) {
 constexpr bool bwd_wide_index_regs(int V, int W, int E) {
   return !(W == 8 && E == 8);
 }
+// XCD-weighted walk of bwd_wide_kernel.  Its workgroups each take a fixed
+// share of a sample's rows, and the kernel ends with its slowest workgroup.
+// A copy of the kernel that records each wavefront's clock showed the
+// workgroups on odd XCDs (odd block index: workgroups go to the eight XCDs
+// in turn) finishing their rows about 4% after those on even XCDs, run after
+// run, for bf16 rows split between a pair of wavefronts at two wavefronts per
+// SIMD.  There, after every m rounds of the walk, the walkers of even-XCD
+// workgroups take one extra row each, so that all XCDs finish together
+// (every row still visited once; the partial sums change grouping, not
+// precision).  Measured on MI355X (backward + finish, HIP events, same
+// buffers, two boxes): 1 x 75600 x 5120 401-404 -> 386-388 us (m = 16),
+// 3 x 20000 x 5120 333.5 -> 321.5 us; D = 3072 (m = 12) 84 x 1560 459-462 ->
+// 443-446 us, 16 x 8190 429-433 -> 421-426 us, 32 x 1560 179.8 -> 177.5 us.
+// Rows of 4 vectors per lane were unchanged, and ragged rows, f32 rows,
+// quads and rows at one wavefront per SIMD 2-5% slower: those keep m = 0,
+// the plain walk.
+constexpr int bwd_wide_xcd_m(int V, int W, int E, bool full) {
+  return E == 8 && W == 2 && full ? (V == 5 ? 16 : V == 3 ? 12 : 0) : 0;
+}
 // Loop form of bwd_wide_kernel at one row in flight: the loads as one step
 // and the arithmetic as the next, or both in one branch.  The compiler
 // schedules the two forms differently, and on MI355X neither wins

@@ -190,7 +190,14 @@ int adaln_bwd_fused_plan(int64_t B, int64_t N, int64_t D, int dtype,
  * g / bps, g / bps + groups, ... in turn; in each sample b, its walker w
  * visits the walk positions (g % bps) * walkers + w, then every
  * bps * walkers positions; position n stands for row (n + b * skew) mod N of
- * the sample (skew is 0 except in the backward of many samples).  A walker
+ * the sample (skew is 0 except in the backward of many samples).  The
+ * backward of bf16 rows of exactly D = 3072 or 5120 (pairs of wavefronts,
+ * 3 or 5 vectors per lane) walks in rounds instead: m regular steps as
+ * above (m = 12 for D = 3072, 16 for D = 5120), then one extra step for the
+ * walkers of workgroups with an even g, which take, in the order of
+ * ((g % bps) * walkers + w), the positions that follow the round's regular
+ * ones; a round covers m * bps * walkers positions plus one per such
+ * walker of the sample.  A walker
  * is one wavefront (W = 1) or the W wavefronts that share a row (a
  * workgroup holds 4 / W walkers, or one when W = 8).  The forward has
  * bps = groups = 0 and covers the B * N rows of the batch with its grid

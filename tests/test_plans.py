@@ -38,7 +38,26 @@ def _shapes(seed, n):
     return out
 
 
-def _visits(p, B, N):
+def _weighted_positions(g, k, w, bps, walkers, N, m):
+    """Walk positions of walker w of workgroup g (number k of its sample's
+    bps) in the rounds the header documents for the weighted backward walk:
+    m regular steps, then one more for the walkers of even workgroups."""
+    S = bps * walkers
+    first = g - k                       # the sample's first workgroup
+    even_k = [kk for kk in range(bps) if (first + kk) % 2 == 0]
+    Wf = len(even_k) * walkers
+    L = m * S + Wf
+    out = []
+    t = 0
+    while t * L < N:
+        out += [t * L + r * S + k * walkers + w for r in range(m)]
+        if g % 2 == 0:
+            out.append(t * L + m * S + even_k.index(k) * walkers + w)
+        t += 1
+    return [q for q in out if q < N]
+
+
+def _visits(p, B, N, m=0):
     """Times each (sample, row) is visited under the documented mapping."""
     pos = np.zeros((B, N), dtype=np.int32)  # by walk position
     bps, groups, walkers = p["bps"], p["groups"], p["walkers"]
@@ -48,7 +67,11 @@ def _visits(p, B, N):
         if slot >= groups:
             continue
         for w in range(walkers):
-            pos[slot::groups, k * walkers + w::stride] += 1
+            if m:
+                pos[slot::groups, _weighted_positions(g, k, w, bps, walkers,
+                                                      N, m)] += 1
+            else:
+                pos[slot::groups, k * walkers + w::stride] += 1
     # position n of sample b is row (n + b * skew) mod N
     count = np.zeros_like(pos)
     n = np.arange(N)
@@ -81,7 +104,8 @@ def test_every_row_once(B, N, D, dt):
         # or quads), or eight wavefronts on one row
         w = p["waves_per_row"]
         assert p["walkers"] * w == (8 if w == 8 else 4)
-        assert np.all(_visits(p, B, N) == 1), (which, p)
+        m = {3072: 12, 5120: 16}.get(D, 0) if dt is BF16 else 0
+        assert np.all(_visits(p, B, N, m) == 1), (which, p)
         if which == "bwd":
             # partial row b * bps + (g % bps) of [B, bps, D], and room for it
             q = A.bwd_fused_plan(B, N, D, dt)
@@ -189,3 +213,19 @@ def test_plan_validation():
     with pytest.raises(A.AdalnError) as e:
         A.plan("bwd", 1, 10, 32776, BF16)      # past the widest row
     assert e.value.code == -6
+
+
+@pytest.mark.parametrize("B,N,D", [(1, 75600, 5120), (84, 1560, 3072),
+                                   (16, 8190, 3072), (3, 7, 3072),
+                                   (600, 3, 5120), (2, 32760, 3072)])
+def test_weighted_walk_visits_every_row(B, N, D):
+    """The backward of bf16 rows of D = 3072 and 5120 walks in rounds where
+    the walkers of even workgroups take one extra row: every row of every
+    sample is still visited exactly once, and those walkers take more rows."""
+    p = A.plan("bwd", B, N, D, BF16)
+    m = {3072: 12, 5120: 16}[D]
+    assert p["waves_per_row"] == 2 and np.all(_visits(p, B, N, m) == 1)
+    if N >= 2 * m * p["bps"] * p["walkers"]:
+        per = [len(_weighted_positions(g, g, 0, p["bps"], p["walkers"], N, m))
+               for g in range(min(p["bps"], 8))]
+        assert min(per[0::2]) > max(per[1::2])
