@@ -243,7 +243,9 @@ bwd_wide_kernel(
     // k_in of that parity are the even ones.  A row group's position is
     // its workgroup's first row group's plus `group` in both kinds of step,
     // so the workgroup's row groups step together.
-    constexpr int kXcdM = bwd_wide_xcd_m(V, W, E, FULL);
+    constexpr int kXcdM = std::is_same<Map, UniformMap>::value
+                              ? bwd_wide_xcd_m(V, W, E, FULL)
+                              : 0;  // packed layouts keep the plain walk
     const int q0 = (int)((blockIdx.x - (unsigned)k_in) & 1u);
     const bool even_xcd = (blockIdx.x & 1u) == 0u;
     const int64_t j0 = (int64_t)k_in * kRows;

@@ -250,7 +250,8 @@ constexpr bool bwd_wide_index_regs(int V, int W, int E) {
 // 443-446 us, 16 x 8190 429-433 -> 421-426 us, 32 x 1560 179.8 -> 177.5 us.
 // Rows of 4 vectors per lane were unchanged, and ragged rows, f32 rows,
 // quads and rows at one wavefront per SIMD 2-5% slower: those keep m = 0,
-// the plain walk.
+// the plain walk, and so do the packed layouts (the two-stream pack 1%
+// slower with it, the mixed pack unchanged).
 constexpr int bwd_wide_xcd_m(int V, int W, int E, bool full) {
   return E == 8 && W == 2 && full ? (V == 5 ? 16 : V == 3 ? 12 : 0) : 0;
 }
