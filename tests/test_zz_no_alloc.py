@@ -83,8 +83,8 @@ def test_two_calls_in_a_row_second_smaller(lib):
 @pytest.mark.parametrize("D", [12288, 32768])
 def test_wide_rows(lib, D):
     # four wavefronts per row in the fused backward (12288), and eight
-    # (32768: 2 samples x 128 workgroups of partial rows fill the 64 MiB
-    # scratch exactly)
+    # (32768: 2 samples x 100 workgroups of partial rows, 50 of the 64 MiB
+    # of scratch)
     wl = W.custom(2, 300, D, "bf16", x_kind="normal", dy_std=1e-2)
     _say(f"wide rows {wl.shape}")
     inp, (ref, got) = _both(lib, wl, seed=5)
